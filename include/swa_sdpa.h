@@ -1,0 +1,214 @@
+/*
+ * swa_sdpa -- sliding-window scaled-dot-product attention for MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels: a window-trimmed forward that
+ * produces O and the row log-sum-exp, and the window-bounded backward that
+ * produces dQ, dK, dV (and dSink) from Q, K, V, O, dO and LSE.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [PR866] cudnn-frontend PR #866 "frost(sdpa): bound the SM80 backward
+ *           q-loop by the sliding window (6-12x on gpt_oss-style SWA) +
+ *           window-aware deterministic relay": commit message, Change.
+ *   [PR557] cudnn-frontend PR #557 "frost(sdpa): GQA/MQA, padding mask,
+ *           right-band widening, and sink-token gradients for the SM120 f16
+ *           backward": Summary, review comments.
+ *   [PR2352] cudnn-frontend PR #2352 "sdpa bwd: lead square A100 backward
+ *           window graphs from a measured study": Measurement, Not measured.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller allocates and frees every device buffer
+ *     (inputs, outputs and the workspace).  The library never allocates
+ *     device memory and never synchronizes the stream.  Plans are host
+ *     objects owned by the caller (destroy them with *_plan_destroy).
+ *   - Pointers named as device pointers must be device memory of the
+ *     current HIP device; host pointers are plain host memory.
+ *   - Errors are returned as sdpa_status; nothing is thrown across the ABI.
+ *     sdpa_last_error() returns a thread-local message naming the field or
+ *     tensor at fault.  A failed call leaves outputs unspecified.
+ *   - Runs are stream-ordered and asynchronous.  A plan is immutable and may
+ *     be used by concurrent runs that use distinct workspaces.
+ */
+#ifndef SWA_SDPA_H
+#define SWA_SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sdpa_status {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID_ARG = 1, /* a descriptor field or a pointer is invalid   */
+  SDPA_ERR_UNSUPPORTED = 2, /* valid, but not provided (e.g. head_dim 96)  */
+  SDPA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned  */
+  SDPA_ERR_HIP = 4          /* a HIP runtime call (e.g. a launch) failed   */
+} sdpa_status;
+
+typedef enum sdpa_dtype { SDPA_BF16 = 0, SDPA_F16 = 1 } sdpa_dtype;
+
+/* BHSD: dense [B, H, S, D] (any batch / head / row strides, D contiguous).
+ * THD : packed [T, H, D]; sequence b owns the row slots
+ *       [cu_seqlens[b], cu_seqlens[b+1]) of which the first seq_lens[b] are
+ *       valid (the rest is padding). */
+typedef enum sdpa_layout { SDPA_LAYOUT_BHSD = 0, SDPA_LAYOUT_THD = 1 } sdpa_layout;
+
+/*
+ * Problem descriptor, shared by the forward and the backward.
+ *
+ * Mask ([PR866] commit message): query row i of a sequence has the anchor
+ * a(i) = i (top-left) or i + s_kv - s_q (bottom-right), in-sequence indices.
+ * Key j is visible when j < s_kv, i < s_q, j <= a(i) if causal, and
+ * a(i) - j <= window_left if window_left >= 0 (an inclusive left window of
+ * window_left + 1 keys).  With a sink ([PR557] Summary) the per-query-head
+ * logit sink[h] (not multiplied by scale) joins each row's softmax
+ * denominator.  GQA / MQA ([PR557] Summary): query head h reads kv head
+ * h / (heads_q / heads_kv).
+ */
+typedef struct sdpa_attn_desc {
+  int32_t dtype;        /* sdpa_dtype of Q, K, V, O, dO, dQ, dK, dV          */
+  int32_t layout;       /* sdpa_layout                                       */
+  int32_t batch;        /* B: batches (BHSD) or packed sequences (THD), >= 1 */
+  int32_t heads_q;      /* query heads, a multiple of heads_kv               */
+  int32_t heads_kv;     /* key / value heads (1 = MQA)                       */
+  int32_t head_dim;     /* 64 or 128                                         */
+  int32_t seq_q;        /* BHSD: S_q.  THD: >= every slot capacity           */
+  int32_t seq_kv;       /* BHSD: S_kv. THD: >= every slot capacity           */
+  int64_t total_q;      /* THD: rows of the packed Q buffer; BHSD: ignored   */
+  int64_t total_kv;     /* THD: rows of the packed K / V buffers             */
+  int32_t causal;       /* 1: mask keys after the anchor                     */
+  int32_t bottom_right; /* 1: anchor i + s_kv - s_q; 0: anchor i             */
+  int32_t window_left;  /* -1: none; >= 0: inclusive left window W           */
+  float scale;          /* softmax scale on Q.K (> 0), e.g. 1/sqrt(D)        */
+  int32_t deterministic; /* backward dQ: 1 ordered relay (bitwise repeatable),
+                            0 unordered fp32 atomics                         */
+  int32_t has_sink;     /* 1: sink logits given (fp32 [heads_q])             */
+  int32_t has_seq_lens; /* 1: seq_lens_q / seq_lens_kv given (THD requires)  */
+  /* Element strides (batch, head, row) of each tensor; the head_dim axis is
+   * contiguous.  THD ignores the batch entry (rows are tokens).  Rows and
+   * base pointers must be 16-byte aligned. */
+  int64_t stride_q[3], stride_k[3], stride_v[3], stride_o[3], stride_do[3];
+  int64_t stride_dq[3], stride_dk[3], stride_dv[3];
+} sdpa_attn_desc;
+
+/* Row statistics (LSE) layout: BHSD [B, heads_q, seq_q]; THD
+ * [heads_q, total_q] (head-major, indexed by packed row).  fp32, natural
+ * log; -inf for a row with no visible key and no sink, and for padding. */
+
+typedef struct sdpa_fwd_tensors {
+  const void* q;                /* device, dtype, Q                           */
+  const void* k;                /* device, dtype, K                           */
+  const void* v;                /* device, dtype, V                           */
+  const float* sink;            /* device fp32 [heads_q] or NULL              */
+  const int32_t* cu_seqlens_q;  /* device int32 [B+1] (THD) or NULL           */
+  const int32_t* cu_seqlens_kv; /* device int32 [B+1] (THD) or NULL           */
+  const int32_t* seq_lens_q;    /* device int32 [B] valid rows, or NULL       */
+  const int32_t* seq_lens_kv;   /* device int32 [B] valid rows, or NULL       */
+  void* o;                      /* device output, dtype, O (padding -> 0)     */
+  float* lse;                   /* device output fp32, layout above           */
+} sdpa_fwd_tensors;
+
+typedef struct sdpa_bwd_tensors {
+  const void* q;                /* device inputs, dtype                       */
+  const void* k;
+  const void* v;
+  const void* o;                /* forward output O                           */
+  const void* dO;               /* gradient of the loss with respect to O     */
+  const float* lse;             /* forward row LSE (layout above)             */
+  const float* sink;            /* device fp32 [heads_q] or NULL              */
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_kv;
+  const int32_t* seq_lens_q;
+  const int32_t* seq_lens_kv;
+  void* dq;                     /* device outputs, dtype; padding rows -> 0   */
+  void* dk;
+  void* dv;
+  float* dsink;                 /* device fp32 [heads_q] output, or NULL      */
+} sdpa_bwd_tensors;
+
+typedef struct sdpa_bwd_plan sdpa_bwd_plan_t;
+typedef struct sdpa_fwd_plan sdpa_fwd_plan_t;
+
+/*
+ * sdpa_bwd_plan -- validate a descriptor and build a backward plan.
+ * Host only: no device call.  *workspace_bytes receives the size of the
+ * device workspace sdpa_bwd_run needs (256-byte aligned).  Rejects, among
+ * others: head_dim other than 64/128, heads_q % heads_kv != 0, a dense
+ * bottom-right mask with seq_q > seq_kv (every early row would see no key;
+ * [PR2352] Not measured), THD without seq lens.
+ */
+sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan,
+                          size_t* workspace_bytes);
+
+/*
+ * sdpa_bwd_run -- enqueue the backward on `stream`:
+ *   1. dot  : delta_i = <dO_i, O_i> per row, per-row dSink terms, and
+ *             clearing of the relay counters / dQ accumulator;
+ *   2. main : per kv-tile, the window-bounded q-tile loop ([PR866] Change):
+ *             recompute P, dS = P (dP - delta), accumulate dK / dV over the
+ *             kv head's query-head group ([PR557] Summary), add dS K into
+ *             dQ through fp32 atomics or the ordered relay whose turns
+ *             count from kv_first ([PR866] commit message); a kv-tile with
+ *             no q-tile stores dK = dV = 0;
+ *   3. cvt  : (atomic mode) fp32 dQ accumulator -> dtype;
+ *   4. dsink: fixed-order reduction dSink[h] = -sum exp(sink_h - LSE) delta
+ *             over valid rows ([PR557] Summary and review).
+ * `workspace` is a device buffer of at least the planned size.
+ */
+sdpa_status sdpa_bwd_run(const sdpa_bwd_plan_t* plan, const sdpa_bwd_tensors* tensors,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* As sdpa_bwd_run, also recording `main_start` / `main_stop` (created by the
+ * caller, may be NULL) on `stream` right around the main kernel, so its
+ * duration can be read with hipEventElapsedTime. */
+sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* plan, const sdpa_bwd_tensors* tensors,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t main_start, hipEvent_t main_stop);
+
+void sdpa_bwd_plan_destroy(sdpa_bwd_plan_t* plan);
+
+/*
+ * sdpa_fwd_plan / sdpa_fwd_run -- the window-trimmed forward
+ * ([PR866] Problem: the forward already trims its kv range by the window):
+ * each q-tile walks only the kv-tiles [kv_first, kv_last] its rows can see
+ * and writes O (dtype) and LSE (fp32).  Workspace is 0 bytes today; pass
+ * the planned size anyway.
+ */
+sdpa_status sdpa_fwd_plan(const sdpa_attn_desc* desc, sdpa_fwd_plan_t** plan,
+                          size_t* workspace_bytes);
+sdpa_status sdpa_fwd_run(const sdpa_fwd_plan_t* plan, const sdpa_fwd_tensors* tensors,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+void sdpa_fwd_plan_destroy(sdpa_fwd_plan_t* plan);
+
+/*
+ * sdpa_bwd_schedule -- host-side view of a plan's tile schedule for one
+ * sequence of valid lengths (len_q, len_kv).  Writes the tile sizes, then
+ * for each kv-tile j < n_kv (n_kv <= kv_cap) q_lo[j], q_hi[j] (q_hi <= q_lo
+ * means the tile stores zeros), and for each q-tile i < n_q (<= q_cap)
+ * kv_first[i], kv_last[i] (the relay visitor range).  Any array may be
+ * NULL.  Host only.
+ */
+sdpa_status sdpa_bwd_schedule(const sdpa_bwd_plan_t* plan, int32_t len_q, int32_t len_kv,
+                              int32_t* tile_q, int32_t* tile_kv, int32_t* n_q, int32_t* n_kv,
+                              int32_t kv_cap, int32_t* q_lo, int32_t* q_hi, int32_t q_cap,
+                              int32_t* kv_first, int32_t* kv_last);
+
+/*
+ * sdpa_bwd_relay_expiries -- debug / test aid: copies to *count (host) the
+ * number of ordered-relay waits of the last run on `workspace` that gave up
+ * after the watchdog's spin limit (0 when every turn arrived in order).
+ * Synchronizes `stream`.
+ */
+sdpa_status sdpa_bwd_relay_expiries(const sdpa_bwd_plan_t* plan, const void* workspace,
+                                    hipStream_t stream, int32_t* count);
+
+const char* sdpa_status_string(sdpa_status status);
+const char* sdpa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWA_SDPA_H */

@@ -193,7 +193,9 @@ def _sink(p: Problem, sink):
         return None
     if sink is None:
         raise ValueError("problem has a sink but no sink tensor given")
-    return _prep(sink).to(torch.float64).contiguous()
+    if sink.device.type != "cpu":
+        raise ValueError("oracle inputs must be CPU tensors")
+    return sink.to(torch.float64).contiguous()
 
 
 def forward(p: Problem, q, k, v, sink=None, lib=None):

@@ -1,0 +1,396 @@
+// C ABI of swa_sdpa: descriptor validation, plans, workspace layout and the
+// launch sequence of the forward and the backward.  Host code only.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "kernels.h"
+#include "swa_sdpa.h"
+
+using swa::kTile;
+
+struct sdpa_bwd_plan {
+  sdpa_attn_desc desc;
+  swa::Problem prob;
+  int64_t stat_rows;  // rows of the delta / dQ-accumulator workspace
+  size_t off_delta, off_acc, off_sem, off_ctl, off_sink, ws_bytes;
+  int spin_limit;
+};
+
+struct sdpa_fwd_plan {
+  sdpa_attn_desc desc;
+  swa::Problem prob;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sdpa_status fail(sdpa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+sdpa_status check_strides(const char* name, const int64_t* st, const sdpa_attn_desc* d) {
+  const int first = d->layout == SDPA_LAYOUT_THD ? 1 : 0;
+  for (int k = first; k < 3; ++k) {
+    if (st[k] < 0) return fail(SDPA_ERR_INVALID_ARG, "stride_%s[%d] = %lld is negative", name, k, (long long)st[k]);
+    if (st[k] % 8)
+      return fail(SDPA_ERR_INVALID_ARG, "stride_%s[%d] = %lld is not a multiple of 8 elements (16-byte rows)",
+                  name, k, (long long)st[k]);
+  }
+  if (st[2] < d->head_dim)
+    return fail(SDPA_ERR_INVALID_ARG, "stride_%s row stride %lld is smaller than head_dim %d", name,
+                (long long)st[2], d->head_dim);
+  return SDPA_OK;
+}
+
+sdpa_status check_desc(const sdpa_attn_desc* d, bool backward) {
+  if (!d) return fail(SDPA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->dtype != SDPA_BF16 && d->dtype != SDPA_F16)
+    return fail(SDPA_ERR_INVALID_ARG, "dtype %d is not SDPA_BF16 or SDPA_F16", d->dtype);
+  if (d->layout != SDPA_LAYOUT_BHSD && d->layout != SDPA_LAYOUT_THD)
+    return fail(SDPA_ERR_INVALID_ARG, "layout %d is not BHSD or THD", d->layout);
+  if (d->batch < 1) return fail(SDPA_ERR_INVALID_ARG, "batch %d < 1", d->batch);
+  if (d->heads_q < 1 || d->heads_kv < 1)
+    return fail(SDPA_ERR_INVALID_ARG, "heads_q %d / heads_kv %d must be >= 1", d->heads_q, d->heads_kv);
+  if (d->heads_q % d->heads_kv)
+    return fail(SDPA_ERR_INVALID_ARG, "heads_q %d is not a multiple of heads_kv %d", d->heads_q, d->heads_kv);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are provided", d->head_dim);
+  if (d->seq_q < 0 || d->seq_kv < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "seq_q %d / seq_kv %d must be >= 0", d->seq_q, d->seq_kv);
+  if (d->causal != 0 && d->causal != 1) return fail(SDPA_ERR_INVALID_ARG, "causal %d is not 0/1", d->causal);
+  if (d->bottom_right != 0 && d->bottom_right != 1)
+    return fail(SDPA_ERR_INVALID_ARG, "bottom_right %d is not 0/1", d->bottom_right);
+  if (d->window_left < -1) return fail(SDPA_ERR_INVALID_ARG, "window_left %d < -1", d->window_left);
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale))
+    return fail(SDPA_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)d->scale);
+  if (d->deterministic != 0 && d->deterministic != 1)
+    return fail(SDPA_ERR_INVALID_ARG, "deterministic %d is not 0/1", d->deterministic);
+  if (d->has_sink != 0 && d->has_sink != 1) return fail(SDPA_ERR_INVALID_ARG, "has_sink %d is not 0/1", d->has_sink);
+  if (d->has_seq_lens != 0 && d->has_seq_lens != 1)
+    return fail(SDPA_ERR_INVALID_ARG, "has_seq_lens %d is not 0/1", d->has_seq_lens);
+  if (d->layout == SDPA_LAYOUT_THD) {
+    if (!d->has_seq_lens) return fail(SDPA_ERR_INVALID_ARG, "THD layout needs seq_lens_q / seq_lens_kv (has_seq_lens = 1)");
+    if (d->total_q < 0 || d->total_kv < 0)
+      return fail(SDPA_ERR_INVALID_ARG, "total_q %lld / total_kv %lld must be >= 0", (long long)d->total_q,
+                  (long long)d->total_kv);
+  } else if (d->bottom_right && d->seq_q > d->seq_kv && !d->has_seq_lens) {
+    // Early rows would have a negative anchor and see no key at all.
+    return fail(SDPA_ERR_UNSUPPORTED, "bottom-right mask with seq_q %d > seq_kv %d is not supported",
+                d->seq_q, d->seq_kv);
+  }
+  sdpa_status st;
+  if ((st = check_strides("q", d->stride_q, d))) return st;
+  if ((st = check_strides("k", d->stride_k, d))) return st;
+  if ((st = check_strides("v", d->stride_v, d))) return st;
+  if ((st = check_strides("o", d->stride_o, d))) return st;
+  if (backward) {
+    if ((st = check_strides("do", d->stride_do, d))) return st;
+    if ((st = check_strides("dq", d->stride_dq, d))) return st;
+    if ((st = check_strides("dk", d->stride_dk, d))) return st;
+    if ((st = check_strides("dv", d->stride_dv, d))) return st;
+  }
+  return SDPA_OK;
+}
+
+swa::Problem make_problem(const sdpa_attn_desc* d) {
+  swa::Problem p{};
+  p.B = d->batch;
+  p.Hq = d->heads_q;
+  p.Hkv = d->heads_kv;
+  p.G = d->heads_q / d->heads_kv;
+  p.D = d->head_dim;
+  p.seq_q = d->seq_q;
+  p.seq_kv = d->seq_kv;
+  p.layout = d->layout;
+  p.total_q = d->layout == SDPA_LAYOUT_THD ? d->total_q : (int64_t)d->batch * d->seq_q;
+  p.total_kv = d->layout == SDPA_LAYOUT_THD ? d->total_kv : (int64_t)d->batch * d->seq_kv;
+  p.causal = d->causal;
+  p.bottom_right = d->bottom_right;
+  p.window = d->window_left;
+  p.scale = d->scale;
+  p.scale_log2 = d->scale * swa::kLog2e;
+  p.has_sink = d->has_sink;
+  for (int k = 0; k < 3; ++k) {
+    p.sq[k] = d->stride_q[k];
+    p.sk[k] = d->stride_k[k];
+    p.sv[k] = d->stride_v[k];
+    p.so[k] = d->stride_o[k];
+    p.sdo[k] = d->stride_do[k];
+    p.sdq[k] = d->stride_dq[k];
+    p.sdk[k] = d->stride_dk[k];
+    p.sdv[k] = d->stride_dv[k];
+  }
+  p.n_q_tiles = (d->seq_q + kTile - 1) / kTile;
+  p.n_kv_tiles = (d->seq_kv + kTile - 1) / kTile;
+  return p;
+}
+
+// Pointer must be device (or managed) memory of the current device.
+sdpa_status check_dev_ptr(const void* ptr, const char* name, bool may_be_null, size_t align) {
+  if (!ptr) return may_be_null ? SDPA_OK : fail(SDPA_ERR_INVALID_ARG, "tensor %s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(ptr) % align)
+    return fail(SDPA_ERR_INVALID_ARG, "tensor %s at %p is not %zu-byte aligned", name, ptr, align);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SDPA_ERR_HIP, "hipGetDevice failed");
+  hipPointerAttribute_t at;
+  std::memset(&at, 0, sizeof at);
+  hipError_t e = hipPointerGetAttributes(&at, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SDPA_ERR_INVALID_ARG, "tensor %s at %p is not device memory (expected device %d)", name, ptr, dev);
+  }
+  if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged)
+    return fail(SDPA_ERR_INVALID_ARG, "tensor %s at %p is host memory, expected device %d", name, ptr, dev);
+  if (at.device != dev)
+    return fail(SDPA_ERR_INVALID_ARG, "tensor %s is on device %d, expected device %d", name, at.device, dev);
+  return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdpa_status_string(sdpa_status s) {
+  switch (s) {
+    case SDPA_OK: return "SDPA_OK";
+    case SDPA_ERR_INVALID_ARG: return "SDPA_ERR_INVALID_ARG";
+    case SDPA_ERR_UNSUPPORTED: return "SDPA_ERR_UNSUPPORTED";
+    case SDPA_ERR_WORKSPACE: return "SDPA_ERR_WORKSPACE";
+    case SDPA_ERR_HIP: return "SDPA_ERR_HIP";
+  }
+  return "SDPA_ERR_UNKNOWN";
+}
+
+const char* sdpa_last_error(void) { return g_err; }
+
+sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, size_t* workspace_bytes) {
+  if (!plan || !workspace_bytes) return fail(SDPA_ERR_INVALID_ARG, "plan / workspace_bytes out-pointer is NULL");
+  *plan = nullptr;
+  sdpa_status st = check_desc(desc, true);
+  if (st) return st;
+  auto* pl = new (std::nothrow) struct sdpa_bwd_plan();
+  if (!pl) return fail(SDPA_ERR_INVALID_ARG, "out of host memory");
+  pl->desc = *desc;
+  pl->prob = make_problem(desc);
+  const swa::Problem& p = pl->prob;
+  pl->stat_rows = (int64_t)p.Hq * p.total_q;
+  size_t off = 0;
+  pl->off_delta = off;
+  off = align256(off + sizeof(float) * (size_t)pl->stat_rows);
+  pl->off_acc = off;
+  off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
+  pl->off_sem = off;
+  off = align256(off + sizeof(int) * (size_t)p.B * p.Hq * p.n_q_tiles);
+  pl->off_ctl = off;
+  off = align256(off + sizeof(int) * 4);
+  pl->off_sink = off;
+  off = align256(off + sizeof(float) * (size_t)p.Hq * p.B * p.n_q_tiles);
+  pl->ws_bytes = off;
+  pl->spin_limit = 1 << 20;  // ~55 ms of s_sleep per wait; legitimate waits take microseconds
+  *plan = pl;
+  *workspace_bytes = off;
+  g_err[0] = 0;
+  return SDPA_OK;
+}
+
+void sdpa_bwd_plan_destroy(sdpa_bwd_plan_t* plan) { delete plan; }
+
+sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensors* t, void* ws,
+                                size_t ws_bytes, hipStream_t stream, hipEvent_t main_start,
+                                hipEvent_t main_stop) {
+  if (!pl) return fail(SDPA_ERR_INVALID_ARG, "plan is NULL");
+  if (!t) return fail(SDPA_ERR_INVALID_ARG, "tensors is NULL");
+  const sdpa_attn_desc& d = pl->desc;
+  if (ws_bytes < pl->ws_bytes)
+    return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the planned %zu", ws_bytes, pl->ws_bytes);
+  if (!ws && pl->ws_bytes) return fail(SDPA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(SDPA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  sdpa_status st;
+  if ((st = check_dev_ptr(ws, "workspace", false, 256))) return st == SDPA_ERR_INVALID_ARG ? SDPA_ERR_WORKSPACE : st;
+  if ((st = check_dev_ptr(t->q, "q", false, 16))) return st;
+  if ((st = check_dev_ptr(t->k, "k", false, 16))) return st;
+  if ((st = check_dev_ptr(t->v, "v", false, 16))) return st;
+  if ((st = check_dev_ptr(t->o, "o", false, 16))) return st;
+  if ((st = check_dev_ptr(t->dO, "dO", false, 16))) return st;
+  if ((st = check_dev_ptr(t->lse, "lse", false, 4))) return st;
+  if ((st = check_dev_ptr(t->dq, "dq", false, 16))) return st;
+  if ((st = check_dev_ptr(t->dk, "dk", false, 16))) return st;
+  if ((st = check_dev_ptr(t->dv, "dv", false, 16))) return st;
+  if (d.has_sink) {
+    if ((st = check_dev_ptr(t->sink, "sink", false, 4))) return st;
+    if ((st = check_dev_ptr(t->dsink, "dsink", false, 4))) return st;
+  } else if (t->sink || t->dsink) {
+    return fail(SDPA_ERR_INVALID_ARG, "sink / dsink given but the plan has has_sink = 0");
+  }
+  if (d.layout == SDPA_LAYOUT_THD) {
+    if ((st = check_dev_ptr(t->cu_seqlens_q, "cu_seqlens_q", false, 4))) return st;
+    if ((st = check_dev_ptr(t->cu_seqlens_kv, "cu_seqlens_kv", false, 4))) return st;
+  }
+  if (d.has_seq_lens) {
+    if ((st = check_dev_ptr(t->seq_lens_q, "seq_lens_q", false, 4))) return st;
+    if ((st = check_dev_ptr(t->seq_lens_kv, "seq_lens_kv", false, 4))) return st;
+  }
+
+  swa::BwdArgs a{};
+  a.p = pl->prob;
+  a.p.cu_q = d.layout == SDPA_LAYOUT_THD ? t->cu_seqlens_q : nullptr;
+  a.p.cu_kv = d.layout == SDPA_LAYOUT_THD ? t->cu_seqlens_kv : nullptr;
+  a.p.len_q = d.has_seq_lens ? t->seq_lens_q : nullptr;
+  a.p.len_kv = d.has_seq_lens ? t->seq_lens_kv : nullptr;
+  a.dtype = d.dtype;
+  a.q = t->q;
+  a.k = t->k;
+  a.v = t->v;
+  a.o = t->o;
+  a.dO = t->dO;
+  a.lse = t->lse;
+  a.sink = t->sink;
+  a.dq = t->dq;
+  a.dk = t->dk;
+  a.dv = t->dv;
+  a.dsink = t->dsink;
+  char* base = static_cast<char*>(ws);
+  a.delta = reinterpret_cast<float*>(base + pl->off_delta);
+  a.dq_acc = reinterpret_cast<float*>(base + pl->off_acc);
+  a.sem = reinterpret_cast<int*>(base + pl->off_sem);
+  a.ctl = reinterpret_cast<int*>(base + pl->off_ctl);
+  a.sink_part = reinterpret_cast<float*>(base + pl->off_sink);
+  a.deterministic = d.deterministic;
+  a.spin_limit = pl->spin_limit;
+
+  hipError_t e;
+  if ((e = swa::launch_bwd_dot(a, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "bwd_dot launch: %s", hipGetErrorString(e));
+  if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if ((e = swa::launch_bwd_main(a, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "bwd_main launch: %s", hipGetErrorString(e));
+  if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if (!d.deterministic && (e = swa::launch_bwd_cvt(a, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "bwd_cvt launch: %s", hipGetErrorString(e));
+  if (d.has_sink && (e = swa::launch_bwd_dsink(a, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "bwd_dsink launch: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return SDPA_OK;
+}
+
+sdpa_status sdpa_bwd_run(const sdpa_bwd_plan_t* plan, const sdpa_bwd_tensors* tensors, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return sdpa_bwd_run_events(plan, tensors, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+sdpa_status sdpa_bwd_schedule(const sdpa_bwd_plan_t* pl, int32_t len_q, int32_t len_kv, int32_t* tile_q,
+                              int32_t* tile_kv, int32_t* n_q, int32_t* n_kv, int32_t kv_cap, int32_t* q_lo,
+                              int32_t* q_hi, int32_t q_cap, int32_t* kv_first, int32_t* kv_last) {
+  if (!pl) return fail(SDPA_ERR_INVALID_ARG, "plan is NULL");
+  if (len_q < 0 || len_kv < 0) return fail(SDPA_ERR_INVALID_ARG, "len_q %d / len_kv %d must be >= 0", len_q, len_kv);
+  swa::SeqSched g;
+  g.init(len_q, len_kv, pl->desc.bottom_right, pl->desc.causal, pl->desc.window_left, kTile, kTile);
+  if (tile_q) *tile_q = kTile;
+  if (tile_kv) *tile_kv = kTile;
+  if (n_q) *n_q = g.n_q_tiles;
+  if (n_kv) *n_kv = g.n_kv_tiles;
+  if ((q_lo || q_hi) && kv_cap < g.n_kv_tiles)
+    return fail(SDPA_ERR_INVALID_ARG, "kv_cap %d < %d kv-tiles", kv_cap, g.n_kv_tiles);
+  if ((kv_first || kv_last) && q_cap < g.n_q_tiles)
+    return fail(SDPA_ERR_INVALID_ARG, "q_cap %d < %d q-tiles", q_cap, g.n_q_tiles);
+  for (int j = 0; j < g.n_kv_tiles; ++j) {
+    if (q_lo) q_lo[j] = g.q_lo(j);
+    if (q_hi) q_hi[j] = g.q_hi(j);
+  }
+  for (int i = 0; i < g.n_q_tiles; ++i) {
+    if (kv_first) kv_first[i] = g.kv_first(i);
+    if (kv_last) kv_last[i] = g.kv_last(i);
+  }
+  g_err[0] = 0;
+  return SDPA_OK;
+}
+
+sdpa_status sdpa_bwd_relay_expiries(const sdpa_bwd_plan_t* pl, const void* ws, hipStream_t stream,
+                                    int32_t* count) {
+  if (!pl || !ws || !count) return fail(SDPA_ERR_INVALID_ARG, "plan / workspace / count is NULL");
+  const char* base = static_cast<const char*>(ws);
+  hipError_t e = hipMemcpyAsync(count, base + pl->off_ctl + sizeof(int), sizeof(int32_t),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "reading the relay watchdog counter: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return SDPA_OK;
+}
+
+sdpa_status sdpa_fwd_plan(const sdpa_attn_desc* desc, sdpa_fwd_plan_t** plan, size_t* workspace_bytes) {
+  if (!plan || !workspace_bytes) return fail(SDPA_ERR_INVALID_ARG, "plan / workspace_bytes out-pointer is NULL");
+  *plan = nullptr;
+  sdpa_status st = check_desc(desc, false);
+  if (st) return st;
+  auto* pl = new (std::nothrow) struct sdpa_fwd_plan();
+  if (!pl) return fail(SDPA_ERR_INVALID_ARG, "out of host memory");
+  pl->desc = *desc;
+  pl->prob = make_problem(desc);
+  *plan = pl;
+  *workspace_bytes = 0;
+  g_err[0] = 0;
+  return SDPA_OK;
+}
+
+void sdpa_fwd_plan_destroy(sdpa_fwd_plan_t* plan) { delete plan; }
+
+sdpa_status sdpa_fwd_run(const sdpa_fwd_plan_t* pl, const sdpa_fwd_tensors* t, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!pl) return fail(SDPA_ERR_INVALID_ARG, "plan is NULL");
+  if (!t) return fail(SDPA_ERR_INVALID_ARG, "tensors is NULL");
+  const sdpa_attn_desc& d = pl->desc;
+  sdpa_status st;
+  if ((st = check_dev_ptr(t->q, "q", false, 16))) return st;
+  if ((st = check_dev_ptr(t->k, "k", false, 16))) return st;
+  if ((st = check_dev_ptr(t->v, "v", false, 16))) return st;
+  if ((st = check_dev_ptr(t->o, "o", false, 16))) return st;
+  if ((st = check_dev_ptr(t->lse, "lse", false, 4))) return st;
+  if (d.has_sink) {
+    if ((st = check_dev_ptr(t->sink, "sink", false, 4))) return st;
+  } else if (t->sink) {
+    return fail(SDPA_ERR_INVALID_ARG, "sink given but the plan has has_sink = 0");
+  }
+  if (d.layout == SDPA_LAYOUT_THD) {
+    if ((st = check_dev_ptr(t->cu_seqlens_q, "cu_seqlens_q", false, 4))) return st;
+    if ((st = check_dev_ptr(t->cu_seqlens_kv, "cu_seqlens_kv", false, 4))) return st;
+  }
+  if (d.has_seq_lens) {
+    if ((st = check_dev_ptr(t->seq_lens_q, "seq_lens_q", false, 4))) return st;
+    if ((st = check_dev_ptr(t->seq_lens_kv, "seq_lens_kv", false, 4))) return st;
+  }
+  swa::FwdArgs a{};
+  a.p = pl->prob;
+  a.p.cu_q = d.layout == SDPA_LAYOUT_THD ? t->cu_seqlens_q : nullptr;
+  a.p.cu_kv = d.layout == SDPA_LAYOUT_THD ? t->cu_seqlens_kv : nullptr;
+  a.p.len_q = d.has_seq_lens ? t->seq_lens_q : nullptr;
+  a.p.len_kv = d.has_seq_lens ? t->seq_lens_kv : nullptr;
+  a.dtype = d.dtype;
+  a.q = t->q;
+  a.k = t->k;
+  a.v = t->v;
+  a.sink = t->sink;
+  a.o = t->o;
+  a.lse = t->lse;
+  hipError_t e = swa::launch_fwd(a, stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "fwd launch: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return SDPA_OK;
+}
+
+}  // extern "C"

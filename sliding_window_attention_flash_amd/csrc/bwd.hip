@@ -1,0 +1,520 @@
+// Backward kernels of the sliding-window attention (gfx950).
+//
+//   bwd_dot   delta_i = <dO_i, O_i>, per-q-tile dSink partials, clearing of
+//             the relay counters and of the dQ accumulator
+//   bwd_main  kv-tile-stationary backward with the window-bounded q-loop
+//   bwd_cvt   fp32 dQ accumulator -> 16-bit dQ (atomic mode)
+//   bwd_dsink fixed-order dSink reduction
+//
+// Method sources (web pages): cudnn-frontend PR #866 "frost(sdpa): bound the
+// SM80 backward q-loop by the sliding window ... + window-aware deterministic
+// relay" (commit message, Change) for the q-loop bounds, the zero store and
+// the relay turn; cudnn-frontend PR #557 "frost(sdpa): GQA/MQA, padding mask,
+// right-band widening, and sink-token gradients for the SM120 f16 backward"
+// (Summary, review comments) for the dot / main / reduce / cvt split, GQA,
+// per-sequence lengths and dSink.  The kernel design itself is written for
+// CDNA4 and is not taken from those pages.
+#include "kernels.h"
+
+namespace swa {
+
+// ---------------------------------------------------------------------------
+// helpers
+
+// Loads 8 contiguous 16-bit elements (16 bytes) from global memory.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::vec8 ld8(const T* p) {
+  return *reinterpret_cast<const typename Elem<T>::vec8*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void st8(T* p, const typename Elem<T>::vec8& v) {
+  *reinterpret_cast<typename Elem<T>::vec8*>(p) = v;
+}
+
+// Two 4-element runs (8 bytes each) from LDS at p and p + 16 elements,
+// as one 8-element MFMA operand.  This is the operand layout that pairs with
+// an accumulator tile used as the other operand (rows 4g..4g+3 of two
+// stacked 16-row blocks).
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::vec8 lds_pair4(const T* p) {
+  typedef typename Elem<T>::vec8 V8;
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
+  u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(V8, r);
+}
+
+// Blocks are dealt to the 8 XCDs round-robin; renumber them so that each XCD
+// runs one contiguous range of logical tiles (neighbouring kv-tiles of one
+// head then share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int base = n >> 3, extra = n & 7;
+  return xcd * base + (xcd < extra ? xcd : extra) + slot;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dot: one block per (q-tile, query head, sequence).
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
+  const Problem& p = a.p;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const Seq s = load_seq(p, b);
+  if (tile == 0 && h == 0 && b == 0 && tid < 2) a.ctl[tid] = 0;
+  if (a.deterministic && tid == 0) a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile] = 0;
+
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int RPP = kThreads / CH;  // rows per pass
+  __shared__ float s_term[kTile];
+  const int c = tid % CH, rl = tid / CH;
+  const int row_base = tile * kTile;
+  const T* op = static_cast<const T*>(a.o);
+  const T* dop = static_cast<const T*>(a.dO);
+  for (int r0 = 0; r0 < kTile; r0 += RPP) {
+    const int row = row_base + r0 + rl;
+    float acc = 0.f;
+    if (row < s.len_q) {
+      const auto ov = ld8(op + elem_off(p, p.so, b, s.row0_q, h, row) + 8 * c);
+      const auto gv = ld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, row) + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gv[e];
+    }
+#pragma unroll
+    for (int off = CH / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (c == 0) {
+      float t = 0.f;
+      if (row < s.cap_q) {
+        const int64_t si = s.stat0 + h * s.stat_hs + row;
+        a.delta[si] = acc;
+        if (p.has_sink && row < s.len_q) {
+          const float l = a.lse[si];
+          t = (l == -INFINITY) ? 0.f : expf(a.sink[h] - l) * acc;
+        }
+      }
+      s_term[r0 + rl] = t;
+    }
+  }
+  if (p.has_sink) {
+    __syncthreads();
+    if (tid == 0) {
+      float sum = 0.f;
+      for (int r = 0; r < kTile; ++r) sum += s_term[r];
+      a.sink_part[((int64_t)h * p.B + b) * p.n_q_tiles + tile] = sum;
+    }
+  }
+
+  // Clearing for the main kernel.  Atomic mode: the fp32 accumulator rows of
+  // this tile.  Relay mode: dQ rows of a q-tile that no kv-tile visits (the
+  // relay's last visitor writes every other q-tile).
+  const int rows = min(kTile, s.cap_q - row_base);
+  if (rows <= 0) return;
+  if (!a.deterministic) {
+    float4* acc = reinterpret_cast<float4*>(a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D);
+    const float4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int e = tid; e < rows * (D / 4); e += kThreads) acc[e] = z;
+  } else {
+    SeqSched g;
+    g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, kTile);
+    if (g.n_visitors(tile) == 0) {
+      T* dqp = static_cast<T*>(a.dq);
+      typename Elem<T>::vec8 z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
+      for (int e = tid; e < rows * CH; e += kThreads)
+        st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_main: one block (4 waves) per (kv-tile of 64 keys, kv head, sequence).
+//
+// Each wave owns 16 keys of the tile.  For every query head of the kv
+// head's group and every q-tile i in [q_lo, q_hi) (descending i):
+//   S  = Q_i K^T,  dP = dO_i V^T            (A: Q / dO rows from LDS,
+//                                             B: the wave's K / V rows, regs)
+//   P  = exp2(S * scale * log2e - LSE_i * log2e),  dS = P (dP - delta_i)
+//   dV^T += dO_i^T P,  dK^T += Q_i^T dS      (B: P / dS straight from the
+//                                             accumulator, A: transposed tile)
+//   dQ_i += dS K                              (dS through LDS, K^T in regs)
+// dQ_i is added into the fp32 accumulator with atomics, or through the
+// ordered relay.  All products are 16x16x32 MFMAs, fp32 accumulation.
+
+template <typename T, int D, bool RELAY>
+__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
+  typedef typename Elem<T>::vec8 V8;
+  constexpr int NS = D / 32;       // k-steps over the head dim
+  constexpr int NDB = D / 16;      // 16-column blocks of the head dim
+  constexpr int LDR = D + 8;       // pitch of row-major tiles (elements)
+  constexpr int LDT = kTile + 8;   // pitch of transposed tiles
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int RPP = kThreads / CH;
+  constexpr int NPASS = kTile / RPP;
+
+  __shared__ __align__(16) T sQ[kTile * LDR];
+  __shared__ __align__(16) T sdO[kTile * LDR];
+  __shared__ __align__(16) T sQt[D * LDT];
+  __shared__ __align__(16) T sdOt[D * LDT];
+  __shared__ __align__(16) T sdS[kTile * LDT];
+  __shared__ __align__(16) T sKt[D * LDT];
+  __shared__ float sLse[kTile], sDelta[kTile];
+  __shared__ int sTicket;
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
+
+  int L;
+  if (RELAY) {
+    // Tickets hand out tiles in start order, kv-tile-major, so a tile's relay
+    // predecessor (same head, kv-tile - 1) always started earlier: every
+    // wait is on a block that is running or done.
+    if (tid == 0) sTicket = atomicAdd(&a.ctl[0], 1);
+    __syncthreads();
+    L = sTicket;
+  } else {
+    L = xcd_remap(blockIdx.x, gridDim.x);
+  }
+  const int nbh = p.B * p.Hkv;
+  int bh, jt;
+  if (RELAY) {
+    jt = L / nbh;
+    bh = L % nbh;
+  } else {
+    bh = L / p.n_kv_tiles;
+    jt = L % p.n_kv_tiles;
+  }
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const Seq s = load_seq(p, b);
+  const int kv0 = jt * kTile;
+  if (kv0 >= s.cap_kv) return;
+  SeqSched g;
+  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, kTile);
+  const int qlo = g.q_lo(jt), nit = g.n_iters(jt);
+  const int nvisit = nit * p.G;
+
+  const T* qp = static_cast<const T*>(a.q);
+  const T* kp = static_cast<const T*>(a.k);
+  const T* vp = static_cast<const T*>(a.v);
+  const T* dop = static_cast<const T*>(a.dO);
+
+  V8 zero8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zero8[e] = Elem<T>::from_float(0.f);
+
+  // K / V rows of this wave's 16 keys: B operands of S = Q K^T, dP = dO V^T.
+  const int key = kv0 + 16 * w + c;
+  V8 kB[NS], vB[NS];
+  {
+    const bool ok = key < s.len_kv;
+    const int64_t ko = elem_off(p, p.sk, b, s.row0_kv, hk, ok ? key : 0);
+    const int64_t vo = elem_off(p, p.sv, b, s.row0_kv, hk, ok ? key : 0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      kB[st] = ok ? ld8(kp + ko + 32 * st + 8 * gq) : zero8;
+      vB[st] = ok ? ld8(vp + vo + 32 * st + 8 * gq) : zero8;
+    }
+  }
+  // K^T of the whole tile through LDS: B operands of dQ = dS K.
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int r = tid / CH + ps * RPP, ch = tid % CH, kk = kv0 + r;
+    V8 x = zero8;
+    if (kk < s.len_kv) x = ld8(kp + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sKt[(8 * ch + e) * LDT + r] = x[e];
+  }
+  __syncthreads();
+  V8 kdq[2][NDB];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) kdq[s2][db] = lds_pair4(&sKt[(16 * db + c) * LDT + 32 * s2 + 4 * gq]);
+
+  f32x4 dV[NDB], dK[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dV[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dK[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Staging of one visit's Q / dO tile (registers first, then LDS).
+  V8 rq[NPASS], rdo[NPASS];
+  float rlse = 0.f, rdelta = 0.f;
+  auto visit_hi = [&](int v, int& h, int& i) {
+    h = hk * p.G + v / nit;
+    i = qlo + (nit - 1 - v % nit);  // descending q-tiles within a head
+  };
+  auto stage_load = [&](int v) {
+    int h, i;
+    visit_hi(v, h, i);
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int r = tid / CH + ps * RPP, ch = tid % CH, qi = i * kTile + r;
+      if (qi < s.len_q) {
+        rq[ps] = ld8(qp + elem_off(p, p.sq, b, s.row0_q, h, qi) + 8 * ch);
+        rdo[ps] = ld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, qi) + 8 * ch);
+      } else {
+        rq[ps] = zero8;
+        rdo[ps] = zero8;
+      }
+    }
+    if (tid < kTile) {
+      const int qi = i * kTile + tid;
+      if (qi < s.len_q) {
+        const int64_t si = s.stat0 + h * s.stat_hs + qi;
+        rlse = a.lse[si] * kLog2e;
+        rdelta = a.delta[si];
+      } else {
+        rlse = INFINITY;  // exp2(x - inf) = 0: padding rows carry no weight
+        rdelta = 0.f;
+      }
+    }
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int r = tid / CH + ps * RPP, ch = tid % CH;
+      st8(&sQ[r * LDR + 8 * ch], rq[ps]);
+      st8(&sdO[r * LDR + 8 * ch], rdo[ps]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sQt[(8 * ch + e) * LDT + r] = rq[ps][e];
+        sdOt[(8 * ch + e) * LDT + r] = rdo[ps][e];
+      }
+    }
+    if (tid < kTile) {
+      sLse[tid] = rlse;
+      sDelta[tid] = rdelta;
+    }
+  };
+
+  if (nvisit > 0) {
+    stage_load(0);
+    stage_store();
+  }
+  __syncthreads();
+
+  T* dqp = static_cast<T*>(a.dq);
+  for (int v = 0; v < nvisit; ++v) {
+    int h, i;
+    visit_hi(v, h, i);
+    if (v + 1 < nvisit) stage_load(v + 1);
+
+    f32x4 S[4], dP[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      S[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dP[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const V8 aq = *reinterpret_cast<const V8*>(&sQ[(16 * mb + c) * LDR + 32 * st + 8 * gq]);
+        const V8 ado = *reinterpret_cast<const V8*>(&sdO[(16 * mb + c) * LDR + 32 * st + 8 * gq]);
+        S[mb] = mfma16(aq, kB[st], S[mb]);
+        dP[mb] = mfma16(ado, vB[st], dP[mb]);
+      }
+    }
+    V8 pP[2], pS[2];
+    const int q0 = i * kTile;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = 16 * mb + 4 * gq + r;
+        const bool vis = visible(g, q0 + lr, key);
+        const float pv = vis ? fast_exp2(S[mb][r] * p.scale_log2 - sLse[lr]) : 0.f;
+        const float dsv = vis ? pv * (dP[mb][r] - sDelta[lr]) : 0.f;
+        pP[mb >> 1][(mb & 1) * 4 + r] = Elem<T>::from_float(pv);
+        pS[mb >> 1][(mb & 1) * 4 + r] = Elem<T>::from_float(dsv);
+        sdS[lr * LDT + 16 * w + c] = Elem<T>::from_float(dsv);
+      }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        dV[db] = mfma16(lds_pair4(&sdOt[(16 * db + c) * LDT + 32 * s2 + 4 * gq]), pP[s2], dV[db]);
+        dK[db] = mfma16(lds_pair4(&sQt[(16 * db + c) * LDT + 32 * s2 + 4 * gq]), pS[s2], dK[db]);
+      }
+    __syncthreads();  // dS complete; the Q / dO tiles are free
+    if (v + 1 < nvisit) stage_store();
+
+    f32x4 dQ[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dQ[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        dQ[db] = mfma16(lds_pair4(&sdS[(16 * w + c) * LDT + 32 * s2 + 4 * gq]), kdq[s2][db], dQ[db]);
+    }
+
+    const int64_t acc_row0 = s.stat0 + h * s.stat_hs + q0;
+    if (RELAY) {
+      // Ordered relay: visitors of q-tile i add in kv-tile order.  The turn
+      // counts from i's first visitor kv_first(i).  Data moves through
+      // agent-scope atomics, so a turn only has to be ordered after the
+      // previous visitor's release.
+      const int turn = g.relay_turn(i, jt), nv = g.n_visitors(i);
+      int* semp = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
+      if (tid == 0 && turn > 0) {
+        int spins = 0;
+        while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != turn) {
+          if (++spins > a.spin_limit) {
+            atomicAdd(&a.ctl[1], 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = 16 * w + 4 * gq + r, qi = q0 + lr;
+          if (qi >= s.cap_q) continue;
+          const float val = dQ[db][r];
+          float* ap = a.dq_acc + (acc_row0 + lr) * D + 16 * db + c;
+          if (nv == 1) {
+            dqp[elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * db + c] = Elem<T>::from_float(p.scale * val);
+          } else if (turn == 0) {
+            __hip_atomic_store(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else if (turn < nv - 1) {
+            __hip_atomic_fetch_add(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            const float old = __hip_atomic_fetch_add(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            dqp[elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * db + c] = Elem<T>::from_float(p.scale * (old + val));
+          }
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (tid == 0 && nv > 1) __hip_atomic_store(semp, turn + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = 16 * w + 4 * gq + r;
+          if (q0 + lr < s.len_q) unsafeAtomicAdd(a.dq_acc + (acc_row0 + lr) * D + 16 * db + c, dQ[db][r]);
+        }
+    }
+    __syncthreads();  // next tile staged; dS reads done
+  }
+
+  // Epilogue: dK = scale * sum dS^T Q, dV = sum P^T dO; a tile that visited
+  // nothing stores zeros.  Lane holds d = 16 db + 4 gq + r of key `key`.
+  if (key < s.cap_kv) {
+    T* dkp = static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, hk, key);
+    T* dvp = static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, hk, key);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      T kx[4], vx[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kx[r] = Elem<T>::from_float(p.scale * dK[db][r]);
+        vx[r] = Elem<T>::from_float(dV[db][r]);
+      }
+      *reinterpret_cast<u32x2*>(dkp + 16 * db + 4 * gq) = __builtin_bit_cast(u32x2, kx);
+      *reinterpret_cast<u32x2*>(dvp + 16 * db + 4 * gq) = __builtin_bit_cast(u32x2, vx);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_cvt: dQ = scale * accumulator, one block per (q-tile, head, sequence).
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_cvt_kernel(BwdArgs a) {
+  const Problem& p = a.p;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const Seq s = load_seq(p, b);
+  const int row_base = tile * kTile;
+  const int rows = min(kTile, s.cap_q - row_base);
+  constexpr int CH = D / 8;
+  T* dqp = static_cast<T*>(a.dq);
+  const float* acc = a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D;
+  for (int e = tid; e < rows * CH; e += kThreads) {
+    const int r = e / CH, ch = e % CH;
+    const float4 x0 = *reinterpret_cast<const float4*>(acc + r * D + 8 * ch);
+    const float4 x1 = *reinterpret_cast<const float4*>(acc + r * D + 8 * ch + 4);
+    typename Elem<T>::vec8 y;
+    y[0] = Elem<T>::from_float(p.scale * x0.x);
+    y[1] = Elem<T>::from_float(p.scale * x0.y);
+    y[2] = Elem<T>::from_float(p.scale * x0.z);
+    y[3] = Elem<T>::from_float(p.scale * x0.w);
+    y[4] = Elem<T>::from_float(p.scale * x1.x);
+    y[5] = Elem<T>::from_float(p.scale * x1.y);
+    y[6] = Elem<T>::from_float(p.scale * x1.z);
+    y[7] = Elem<T>::from_float(p.scale * x1.w);
+    st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + r) + 8 * ch, y);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dsink: dSink[h] = -sum of the per-q-tile partials, in a fixed order.
+
+__global__ __launch_bounds__(64) void bwd_dsink_kernel(BwdArgs a) {
+  const int h = blockIdx.x, l = threadIdx.x;
+  const int n = a.p.B * a.p.n_q_tiles;
+  const float* part = a.sink_part + (int64_t)h * n;
+  float acc = 0.f;
+  for (int e = l; e < n; e += 64) acc += part[e];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (l == 0) a.dsink[h] = -acc;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+template <typename T>
+static hipError_t dot_t(const BwdArgs& a, hipStream_t st) {
+  dim3 grid(a.p.n_q_tiles, a.p.Hq, a.p.B);
+  if (a.p.D == 64)
+    hipLaunchKernelGGL((bwd_dot_kernel<T, 64>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_dot_kernel<T, 128>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t st) {
+  if (a.p.n_q_tiles == 0) return hipSuccess;
+  return a.dtype == 0 ? dot_t<__bf16>(a, st) : dot_t<_Float16>(a, st);
+}
+
+template <typename T, int D>
+static hipError_t main_td(const BwdArgs& a, hipStream_t st) {
+  const int n = a.p.B * a.p.Hkv * a.p.n_kv_tiles;
+  if (a.deterministic)
+    hipLaunchKernelGGL((bwd_main_kernel<T, D, true>), dim3(n), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_main_kernel<T, D, false>), dim3(n), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t st) {
+  if (a.p.n_kv_tiles == 0) return hipSuccess;
+  if (a.dtype == 0) return a.p.D == 64 ? main_td<__bf16, 64>(a, st) : main_td<__bf16, 128>(a, st);
+  return a.p.D == 64 ? main_td<_Float16, 64>(a, st) : main_td<_Float16, 128>(a, st);
+}
+
+template <typename T>
+static hipError_t cvt_t(const BwdArgs& a, hipStream_t st) {
+  dim3 grid(a.p.n_q_tiles, a.p.Hq, a.p.B);
+  if (a.p.D == 64)
+    hipLaunchKernelGGL((bwd_cvt_kernel<T, 64>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_cvt_kernel<T, 128>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_cvt(const BwdArgs& a, hipStream_t st) {
+  if (a.p.n_q_tiles == 0) return hipSuccess;
+  return a.dtype == 0 ? cvt_t<__bf16>(a, st) : cvt_t<_Float16>(a, st);
+}
+
+hipError_t launch_bwd_dsink(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.p.Hq), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace swa

@@ -1,0 +1,129 @@
+// Shared device-side definitions of the swa_sdpa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "swa_sched.h"
+
+namespace swa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kTile = 64;      // rows of a q-tile and of a kv-tile
+constexpr int kThreads = 256;  // 4 waves of 64 lanes
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum { LAYOUT_BHSD = 0, LAYOUT_THD = 1 };
+
+// Everything a kernel needs to address one problem.  Strides are in
+// elements, (batch, head, row); the head_dim axis is contiguous.
+struct Problem {
+  int B, Hq, Hkv, G, D;
+  int seq_q, seq_kv;          // dense lengths, or max slot capacity (THD)
+  int layout;
+  int64_t total_q, total_kv;  // packed rows (THD)
+  int causal, bottom_right, window;
+  float scale;                // softmax scale
+  float scale_log2;           // scale * log2(e)
+  int has_sink;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  const int32_t* len_q;
+  const int32_t* len_kv;
+  int64_t sq[3], sk[3], sv[3], so[3], sdo[3], sdq[3], sdk[3], sdv[3];
+  int n_q_tiles;              // ceil(seq_q / kTile)
+  int n_kv_tiles;             // ceil(seq_kv / kTile)
+};
+
+// One sequence (or dense batch entry): valid lengths, slot capacities,
+// first packed row and where its row statistics start.
+struct Seq {
+  int len_q, len_kv, cap_q, cap_kv;
+  int64_t row0_q, row0_kv;  // first packed row (THD), 0 for BHSD
+  int64_t stat0;            // stat index of (head 0, row 0)
+  int64_t stat_hs;          // stat index stride between heads
+};
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+// Reads sequence b's geometry.  Device metadata is clamped so that a bad
+// cu_seqlens / seq_lens entry can never address outside the buffers.
+__device__ __forceinline__ Seq load_seq(const Problem& p, int b) {
+  Seq s;
+  if (p.layout == LAYOUT_THD) {
+    int64_t q0 = p.cu_q[b], q1 = p.cu_q[b + 1];
+    int64_t k0 = p.cu_kv[b], k1 = p.cu_kv[b + 1];
+    q0 = q0 < 0 ? 0 : (q0 > p.total_q ? p.total_q : q0);
+    q1 = q1 < q0 ? q0 : (q1 > p.total_q ? p.total_q : q1);
+    k0 = k0 < 0 ? 0 : (k0 > p.total_kv ? p.total_kv : k0);
+    k1 = k1 < k0 ? k0 : (k1 > p.total_kv ? p.total_kv : k1);
+    s.row0_q = q0;
+    s.row0_kv = k0;
+    s.cap_q = (int)(q1 - q0 < p.seq_q ? q1 - q0 : p.seq_q);
+    s.cap_kv = (int)(k1 - k0 < p.seq_kv ? k1 - k0 : p.seq_kv);
+    s.stat0 = q0;
+    s.stat_hs = p.total_q;
+  } else {
+    s.row0_q = s.row0_kv = 0;
+    s.cap_q = p.seq_q;
+    s.cap_kv = p.seq_kv;
+    s.stat0 = (int64_t)b * p.Hq * p.seq_q;
+    s.stat_hs = p.seq_q;
+  }
+  s.len_q = p.len_q ? clampi(p.len_q[b], 0, s.cap_q) : s.cap_q;
+  s.len_kv = p.len_kv ? clampi(p.len_kv[b], 0, s.cap_kv) : s.cap_kv;
+  return s;
+}
+
+// Element offset of (b, h, row) in a tensor with strides st.
+__device__ __forceinline__ int64_t elem_off(const Problem& p, const int64_t* st, int b,
+                                            int64_t row0, int h, int row) {
+  if (p.layout == LAYOUT_THD) return (row0 + row) * st[2] + (int64_t)h * st[1];
+  return (int64_t)b * st[0] + (int64_t)h * st[1] + (int64_t)row * st[2];
+}
+
+// Mask of the pages: anchor a = row (+ diag for bottom-right); key visible
+// when inside both valid lengths, key <= a if causal, a - key <= W if W >= 0.
+__device__ __forceinline__ bool visible(const SeqSched& g, int row, int key) {
+  const int a = row + g.diag;
+  bool v = (row < g.len_q) & (key < g.len_kv);
+  if (g.causal) v &= key <= a;
+  if (g.window >= 0) v &= (a - key) <= g.window;
+  return v;
+}
+
+// Storage type traits: 16-bit element <-> float.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ __bf16 from_float(float x) { return (__bf16)x; }
+  static __device__ __forceinline__ float to_float(__bf16 x) { return (float)x; }
+};
+template <>
+struct Elem<_Float16> {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ _Float16 from_float(float x) { return (_Float16)x; }
+  static __device__ __forceinline__ float to_float(_Float16 x) { return (float)x; }
+};
+
+// MFMA 16x16x32 (fp32 accumulate) on 8-element 16-bit operands.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace swa

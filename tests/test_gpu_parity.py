@@ -1,0 +1,169 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Small problems (several tiles, ragged tails, every mask variant) are compared
+element by element with the full oracle; the full-size workloads are
+compared on sampled gradient rows computed one at a time by the oracle, plus
+properties over the whole output.  Outputs start as NaN so an element the
+kernels never write fails the test.
+"""
+import pytest
+import torch
+
+from gpu_harness import (assert_close, compare_full, compare_sampled, run_gpu, say)
+from sliding_window_attention_flash_amd.synth import CONFIGS, Workload, packed_lengths
+
+pytestmark = pytest.mark.gpu
+
+BF16, F16 = torch.bfloat16, torch.float16
+
+
+def _wl(name, dtype, B, Hq, Hkv, D, Sq, Skv, **kw):
+    return Workload(name, dtype, B, Hq, Hkv, D, Sq, Skv, **kw)
+
+
+SMALL = [
+    _wl("mha_tl_w17_s300_d64", BF16, 2, 4, 4, 64, 300, 300, window_left=17),
+    _wl("gqa_br_w100_d128_f16", F16, 2, 8, 2, 128, 200, 333, bottom_right=True, window_left=100),
+    _wl("mqa_tl_causal_d64", BF16, 1, 4, 1, 64, 190, 190),
+    _wl("w0_tl_d64", BF16, 1, 2, 2, 64, 130, 130, window_left=0),
+    _wl("tl_sq_gt_skv_w40", BF16, 1, 2, 2, 64, 260, 130, window_left=40),
+    _wl("swa_only_br_w50", F16, 1, 2, 1, 64, 100, 250, causal=False, bottom_right=True, window_left=50),
+    _wl("noncausal_full_d128", BF16, 1, 2, 2, 128, 150, 170, causal=False),
+    _wl("sink_gqa_tl_w64_d128", BF16, 2, 6, 3, 128, 257, 257, window_left=64, sink=True),
+    _wl("padded_bhsd_w33", F16, 2, 4, 2, 64, 200, 230, bottom_right=True, window_left=33,
+        pad_len_q=(200, 77), pad_len_kv=(230, 140)),
+]
+
+
+@pytest.mark.parametrize("det", [False, True], ids=["atomic", "relay"])
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_full_oracle(w, det):
+    say(f"case {w.name} det={det}")
+    inp, out, _ = run_gpu(w, seed=3, deterministic=det)
+    assert out["expiries"] == 0
+    compare_full(w, inp, out)
+
+
+def _thd_small(sink=True, dtype=F16, D=64):
+    # one sequence with no query rows and one with no keys, slots padded
+    lq = (70, 0, 130, 5, 64)
+    lk = (300, 40, 130, 0, 200)
+    cq = (128, 64, 192, 64, 64)
+    ck = (300, 64, 150, 16, 200)
+    return Workload(f"thd_small_sink{int(sink)}_d{D}", dtype, 5, 8, 2, D, max(cq), max(ck),
+                    bottom_right=True, window_left=90, sink=sink, layout="thd",
+                    len_q=lq, len_kv=lk, cap_q=cq, cap_kv=ck)
+
+
+@pytest.mark.parametrize("det", [False, True], ids=["atomic", "relay"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_thd_padded_with_sinks(det, D):
+    w = _thd_small(D=D)
+    say(f"case {w.name} det={det}")
+    inp, out, _ = run_gpu(w, seed=5, deterministic=det)
+    compare_full(w, inp, out)
+
+
+def test_c1_tiny_full_oracle():
+    w = CONFIGS["c1"]
+    for det in (False, True):
+        say(f"case {w.name} det={det}")
+        inp, out, _ = run_gpu(w, seed=1, deterministic=det)
+        compare_full(w, inp, out)
+
+
+def test_relay_bitwise_repeatable_and_matches_atomic():
+    w = _wl("det_b2_h4_s2048_w128", BF16, 2, 4, 4, 64, 2048, 2048, window_left=128, scale=0.125,
+            deterministic=True)
+    say(f"case {w.name}: 3 relay runs + 1 atomic run")
+    inp, outs, _ = run_gpu(w, seed=9, runs=3)
+    for o in outs:
+        assert o["expiries"] == 0
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(outs[0][key], outs[1][key]) and torch.equal(outs[0][key], outs[2][key]), key
+    _, at, _ = run_gpu(w, seed=9, deterministic=False)
+    for key in ("dq", "dk", "dv"):
+        assert_close(f"{key} det/at", outs[0][key].cpu(), at[key].cpu().double())
+    compare_full(w, inp, outs[0], check_fwd=False)
+
+
+def test_gqa_equals_group_sum_of_expanded_mha():
+    w = _wl("gqa_8x2_br_w70", BF16, 2, 8, 2, 64, 190, 230, bottom_right=True, window_left=70, sink=True)
+    say(f"case {w.name}: GQA vs head-expanded MHA on the GPU")
+    inp, out, ginp = run_gpu(w, seed=11)
+    from gpu_harness import gpu_backward, gpu_forward
+    we = w.with_(name=w.name + "_expanded", heads_kv=8)
+    einp = dict(ginp)
+    einp["k"] = ginp["k"].repeat_interleave(4, dim=1).contiguous()
+    einp["v"] = ginp["v"].repeat_interleave(4, dim=1).contiguous()
+    o, lse = gpu_forward(we, einp)
+    dq, dk, dv, dsink = gpu_backward(we, einp, o, lse).run()
+    torch.cuda.synchronize()
+    assert_close("dQ", out["dq"].cpu(), dq.cpu().double())
+    assert_close("dK", out["dk"].cpu(), dk.view(2, 2, 4, 230, 64).double().sum(2).cpu())
+    assert_close("dV", out["dv"].cpu(), dv.view(2, 2, 4, 230, 64).double().sum(2).cpu())
+    assert_close("dSink", out["dsink"].cpu(), dsink.cpu().double())
+
+
+def test_keys_outside_every_window_are_exact_zero():
+    # bottom-right, s_q much shorter than s_kv: keys below s_kv - s_q - W are
+    # seen by no query; their kv-tiles run zero iterations and store zeros.
+    w = _wl("br_far_keys", BF16, 1, 4, 2, 64, 100, 1000, bottom_right=True, window_left=50)
+    say(f"case {w.name}")
+    inp, out, _ = run_gpu(w, seed=13)
+    first = 1000 - 100 - 50
+    assert torch.count_nonzero(out["dk"][:, :, :first]) == 0
+    assert torch.count_nonzero(out["dv"][:, :, :first]) == 0
+    compare_full(w, inp, out, check_fwd=False)
+
+
+# ---- full-size workloads -----------------------------------------------------
+
+
+def test_c2_s4096_full_oracle():
+    w = CONFIGS["c2_4k"]
+    say(f"case {w.name} (full oracle)")
+    inp, out, _ = run_gpu(w, seed=21)
+    compare_full(w, inp, out)
+
+
+def test_c2_s8192_sampled():
+    w = CONFIGS["c2_8k"]
+    say(f"case {w.name} (sampled)")
+    inp, out, _ = run_gpu(w, seed=22)
+    compare_sampled(w, inp, out)
+
+
+def test_c3_s32768_relay_bitwise_and_sampled():
+    w = CONFIGS["c3"]
+    say(f"case {w.name}: 3 relay runs, sampled oracle, atomic comparison")
+    inp, outs, _ = run_gpu(w, seed=23, runs=3)
+    for o in outs:
+        assert o["expiries"] == 0
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(outs[0][key], outs[1][key]) and torch.equal(outs[0][key], outs[2][key]), key
+    compare_sampled(w, inp, outs[0])
+    _, at, _ = run_gpu(w, seed=23, deterministic=False)
+    for key in ("dq", "dk", "dv"):
+        assert_close(f"{key} det/at", outs[0][key].float(), at[key].float())
+
+
+def test_c4_gqa_s16484_sampled():
+    w = CONFIGS["c4"]
+    say(f"case {w.name} (sampled)")
+    inp, out, _ = run_gpu(w, seed=24)
+    compare_sampled(w, inp, out, n_q=192, n_kv=96)
+
+
+def test_c4_f16_variant_full_oracle():
+    w = CONFIGS["c4_f16"]
+    say(f"case {w.name} (full oracle)")
+    inp, out, _ = run_gpu(w, seed=25)
+    compare_full(w, inp, out)
+
+
+def test_c5_thd_sinks_full_oracle():
+    w = CONFIGS["c5"]
+    say(f"case {w.name} (full oracle, dSink)")
+    inp, out, _ = run_gpu(w, seed=26)
+    compare_full(w, inp, out)

@@ -1,0 +1,223 @@
+"""Host-side checks of the HIP library (no GPU needed): exported symbols,
+descriptor validation, the window-bounded tile schedule against brute force,
+and a host simulation of the ordered dQ relay."""
+import ctypes
+import os
+import re
+import threading
+import time
+
+import pytest
+import torch
+
+import oracle_checks as oc
+from sliding_window_attention_flash_amd import _lib, api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "swa_sdpa.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(sdpa_\w+)\s*\(", header, re.M))
+    assert {"sdpa_bwd_plan", "sdpa_bwd_run", "sdpa_fwd_plan", "sdpa_fwd_run"} <= declared
+    missing = [s for s in sorted(declared) if not hasattr(lib, s)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert set(_lib.EXPORTS) == declared
+
+
+def _desc(**kw):
+    g = api.Geometry(kw.pop("layout", 0), kw.pop("B", 2), kw.pop("Hq", 4), kw.pop("Hkv", 2),
+                     kw.pop("D", 64), kw.pop("Sq", 300), kw.pop("Skv", 300), 600, 600)
+    q = torch.empty(g.batch, g.heads_q, g.seq_q, g.head_dim, dtype=torch.bfloat16)
+    k = torch.empty(g.batch, g.heads_kv, g.seq_kv, g.head_dim, dtype=torch.bfloat16)
+    d = api.make_desc(g, torch.bfloat16, q=q, k=k, v=k, o=q, dO=q, dq=q, dk=k, dv=k,
+                      window_left=kw.pop("window_left", 64), bottom_right=kw.pop("bottom_right", False))
+    for key, val in kw.items():
+        setattr(d, key, val)
+    return d
+
+
+@pytest.mark.parametrize("field,value,status,needle", [
+    ("head_dim", 96, _lib.SDPA_ERR_UNSUPPORTED, "head_dim"),
+    ("heads_q", 5, _lib.SDPA_ERR_INVALID_ARG, "multiple"),
+    ("dtype", 7, _lib.SDPA_ERR_INVALID_ARG, "dtype"),
+    ("window_left", -2, _lib.SDPA_ERR_INVALID_ARG, "window_left"),
+    ("scale", 0.0, _lib.SDPA_ERR_INVALID_ARG, "scale"),
+    ("batch", 0, _lib.SDPA_ERR_INVALID_ARG, "batch"),
+    ("deterministic", 2, _lib.SDPA_ERR_INVALID_ARG, "deterministic"),
+])
+def test_plan_rejects_bad_descriptors(lib, field, value, status, needle):
+    d = _desc(**{field: value})
+    with pytest.raises(_lib.SdpaError) as e:
+        api.sdpa_bwd_plan(d)
+    assert e.value.status == status and needle in str(e.value)
+
+
+def test_plan_rejects_bottom_right_with_more_queries_than_keys(lib):
+    d = _desc(Sq=400, Skv=300, bottom_right=True)
+    with pytest.raises(_lib.SdpaError) as e:
+        api.sdpa_bwd_plan(d)
+    assert e.value.status == _lib.SDPA_ERR_UNSUPPORTED
+
+
+def test_plan_rejects_unaligned_strides_and_thd_without_lengths(lib):
+    d = _desc()
+    d.stride_q[2] = 60
+    with pytest.raises(_lib.SdpaError, match="stride_q"):
+        api.sdpa_bwd_plan(d)
+    d = _desc(layout=1)
+    d.stride_q[:] = (0, 64, 256)
+    with pytest.raises(_lib.SdpaError, match="seq_lens"):
+        api.sdpa_bwd_plan(d)
+
+
+def test_run_validates_workspace_and_tensors_before_touching_a_device(lib):
+    plan = api.sdpa_bwd_plan(_desc())
+    t = _lib.BwdTensors()
+    rc = lib.sdpa_bwd_run(plan.handle, ctypes.byref(t), None, plan.workspace_bytes - 1, None)
+    assert rc == _lib.SDPA_ERR_WORKSPACE
+    assert b"smaller than the planned" in lib.sdpa_last_error()
+    rc = lib.sdpa_bwd_run(plan.handle, ctypes.byref(t), ctypes.c_void_p(1000), plan.workspace_bytes, None)
+    assert rc == _lib.SDPA_ERR_WORKSPACE  # misaligned workspace
+    assert b"256-byte" in lib.sdpa_last_error()
+
+
+def test_workspace_size_formula(lib):
+    plan = api.sdpa_bwd_plan(_desc(B=2, Hq=4, Hkv=2, D=64, Sq=300, Skv=300))
+    rows = 2 * 4 * 300
+    ntq = 5
+    expect = 0
+    for nbytes in (4 * rows, 4 * rows * 64, 4 * 2 * 4 * ntq, 16, 4 * 4 * 2 * ntq):
+        expect = (expect + nbytes + 255) // 256 * 256
+    assert plan.workspace_bytes == expect
+
+
+# ---- the window-bounded schedule, brute force ------------------------------------
+
+
+def _schedule_cases():
+    g = torch.Generator().manual_seed(17)
+    cases = [(256, 256, 64, False, True), (32768 // 64, 32768 // 64, 128, False, True),
+             (100, 1000, 50, True, True), (260, 130, 40, False, True), (190, 190, -1, False, True),
+             (100, 250, 50, True, False), (150, 170, -1, False, False), (16484 % 997, 16484 % 997, 96, True, True),
+             (1, 1, 0, False, True), (0, 5, 3, False, True), (5, 0, 3, True, True)]
+    for _ in range(60):
+        lq, lk = (int(x) for x in torch.randint(0, 400, (2,), generator=g))
+        w = int(torch.randint(-1, 300, (1,), generator=g))
+        br = bool(torch.randint(0, 2, (1,), generator=g))
+        causal = bool(torch.randint(0, 3, (1,), generator=g))  # mostly causal
+        cases.append((lq, lk, w, br, causal))
+    return cases
+
+
+@pytest.mark.parametrize("lq,lk,w,br,causal", _schedule_cases())
+def test_schedule_covers_the_mask_exactly(lib, lq, lk, w, br, causal):
+    d = _desc(window_left=w, bottom_right=br)
+    d.causal = int(causal)
+    plan = api.sdpa_bwd_plan(d)
+    s = api.sdpa_bwd_schedule(plan, lq, lk)
+    Tq, Tk = s["tile_q"], s["tile_kv"]
+    m = oc.explicit_mask(lq, lk, causal, br, w) if lq and lk else torch.zeros(lq, lk, dtype=torch.bool)
+    nq, nk = s["n_q"], s["n_kv"]
+    assert nq == -(-lq // Tq) and nk == -(-lk // Tk)
+    # tile-level visibility from brute force
+    vis = torch.zeros(nq, nk, dtype=torch.bool)
+    for i in range(nq):
+        for j in range(nk):
+            vis[i, j] = bool(m[i * Tq:(i + 1) * Tq, j * Tk:(j + 1) * Tk].any())
+    visited = torch.zeros(nq, nk, dtype=torch.bool)
+    for j in range(nk):
+        lo, hi = s["q_lo"][j], s["q_hi"][j]
+        for i in range(max(lo, 0), min(hi, nq)):
+            visited[i, j] = True
+        if hi <= lo:
+            assert not vis[:, j].any(), f"kv-tile {j} stores zeros but has a visible pair"
+    # every visible pair is visited (the bound never cuts real work)
+    assert not (vis & ~visited).any()
+    # the bounds are tight up to tile rounding: for a full kv-tile whose
+    # bounding rows exist, q_lo and q_hi - 1 both touch the mask (a partial
+    # last tile keeps the formula's kv_base + tile_kv, so it may run long)
+    diag = (lk - lq) if br else 0
+    for j in range(nk):
+        lo, hi = s["q_lo"][j], s["q_hi"][j]
+        if hi > lo and vis[:, j].any():
+            first = int(torch.nonzero(vis[:, j])[0])
+            last = int(torch.nonzero(vis[:, j])[-1])
+            r_lo = j * Tk - diag
+            if causal and 0 <= r_lo < lq:
+                assert lo == first
+            r_hi = j * Tk + Tk - 1 + w - diag
+            if w >= 0 and (j + 1) * Tk <= lk and 0 <= r_hi < lq:
+                assert hi - 1 == last
+    # relay visitor ranges equal the visited set, contiguous
+    for i in range(nq):
+        vs = torch.nonzero(visited[i]).view(-1).tolist()
+        if vs:
+            assert vs == list(range(vs[0], vs[-1] + 1)), "visitors not contiguous"
+            assert s["kv_first"][i] == vs[0] and s["kv_last"][i] == vs[-1]
+        else:
+            assert s["kv_first"][i] > s["kv_last"][i] or s["kv_last"][i] < 0
+
+
+# ---- host simulation of the ordered relay ----------------------------------------
+
+
+def simulate_relay(s, kv_first=None, timeout_s=2.0):
+    """One thread per kv-tile visits its q-tiles in descending order; each
+    visit waits for its turn (j - kv_first(i)), logs itself, and passes the
+    turn on.  Returns (log per q-tile, expired waits)."""
+    kv_first = kv_first or s["kv_first"]
+    nq, nk = s["n_q"], s["n_kv"]
+    sem = [0] * nq
+    log = [[] for _ in range(nq)]
+    expired = []
+    lock = threading.Lock()
+
+    def visitor(j):
+        for i in range(s["q_hi"][j] - 1, s["q_lo"][j] - 1, -1):
+            turn = j - kv_first[i]
+            t0 = time.time()
+            while True:
+                with lock:
+                    if sem[i] == turn:
+                        break
+                if time.time() - t0 > timeout_s:
+                    with lock:
+                        expired.append((i, j))
+                    break
+                time.sleep(0.0005)
+            with lock:
+                log[i].append(j)
+                sem[i] = turn + 1
+
+    ts = [threading.Thread(target=visitor, args=(j,)) for j in range(nk)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return log, expired
+
+
+@pytest.mark.parametrize("lq,lk,w,br", [(640, 640, 128, False), (300, 700, 100, True), (500, 500, 0, False)])
+def test_relay_simulation_orders_every_q_tile(lib, lq, lk, w, br):
+    plan = api.sdpa_bwd_plan(_desc(window_left=w, bottom_right=br))
+    s = api.sdpa_bwd_schedule(plan, lq, lk)
+    log, expired = simulate_relay(s)
+    assert not expired
+    for i in range(s["n_q"]):
+        assert log[i] == list(range(s["kv_first"][i], s["kv_last"][i] + 1))
+
+
+def test_relay_simulation_with_wrong_first_visitor_times_out(lib):
+    # Counting turns from kv-tile 0 (the pre-window rule) instead of kv_first
+    # leaves every q-tile past the first window waiting for a turn that no
+    # visitor takes: the watchdog, not a hang, ends the run.
+    plan = api.sdpa_bwd_plan(_desc(window_left=64))
+    s = api.sdpa_bwd_schedule(plan, 512, 512)
+    log, expired = simulate_relay(s, kv_first=[0] * s["n_q"], timeout_s=0.3)
+    assert expired
