@@ -17,7 +17,7 @@ struct sdpa_bwd_plan {
   sdpa_attn_desc desc;
   swa::Problem prob;
   int64_t stat_rows;  // rows of the delta / dQ-accumulator workspace
-  size_t off_delta, off_acc, off_sem, off_ctl, off_sink, ws_bytes;
+  size_t off_delta, off_acc, off_stash, off_sem, off_ctl, off_sink, ws_bytes;
   int spin_limit;
 };
 
@@ -134,6 +134,25 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   }
   p.n_q_tiles = (d->seq_q + kTile - 1) / kTile;
   p.n_kv_tiles = (d->seq_kv + kTile - 1) / kTile;
+  // The streaming kernel covers multi-head attention with a causal mask and
+  // a left window of at most 128 keys at head_dim 64 (its ring of q-tile
+  // slots is sized for that); everything else runs the per-tile kernel.
+  p.stream = p.G == 1 && d->causal && d->window_left >= 0 && d->window_left <= 128 && d->head_dim == 64;
+  p.step_kv = p.stream ? 128 : kTile;
+  if (p.stream) {
+    // One block per CU: chunks of kv-steps sized so the grid is about one
+    // block per MI355X CU, never shorter than 2 steps (so a q-tile has at
+    // most two visiting chunks).
+    const int64_t steps_per_seq = (d->seq_kv + p.step_kv - 1) / p.step_kv;
+    const int64_t total = steps_per_seq * d->batch * d->heads_q;
+    int64_t chunk = (total + 255) / 256;
+    if (chunk < 2) chunk = 2;
+    p.chunk = (int)chunk;
+    p.n_chunks = (int)((steps_per_seq + chunk - 1) / chunk);
+  } else {
+    p.chunk = 1;
+    p.n_chunks = 0;
+  }
   return p;
 }
 
@@ -191,6 +210,8 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   off = align256(off + sizeof(float) * (size_t)pl->stat_rows);
   pl->off_acc = off;
   off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
+  pl->off_stash = off;
+  if (p.stream && desc->deterministic) off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
   pl->off_sem = off;
   off = align256(off + sizeof(int) * (size_t)p.B * p.Hq * p.n_q_tiles);
   pl->off_ctl = off;
@@ -264,6 +285,7 @@ sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensor
   char* base = static_cast<char*>(ws);
   a.delta = reinterpret_cast<float*>(base + pl->off_delta);
   a.dq_acc = reinterpret_cast<float*>(base + pl->off_acc);
+  a.dq_stash = reinterpret_cast<float*>(base + pl->off_stash);
   a.sem = reinterpret_cast<int*>(base + pl->off_sem);
   a.ctl = reinterpret_cast<int*>(base + pl->off_ctl);
   a.sink_part = reinterpret_cast<float*>(base + pl->off_sink);
@@ -298,9 +320,10 @@ sdpa_status sdpa_bwd_schedule(const sdpa_bwd_plan_t* pl, int32_t len_q, int32_t 
   if (!pl) return fail(SDPA_ERR_INVALID_ARG, "plan is NULL");
   if (len_q < 0 || len_kv < 0) return fail(SDPA_ERR_INVALID_ARG, "len_q %d / len_kv %d must be >= 0", len_q, len_kv);
   swa::SeqSched g;
-  g.init(len_q, len_kv, pl->desc.bottom_right, pl->desc.causal, pl->desc.window_left, kTile, kTile);
+  const int tkv = pl->prob.step_kv;
+  g.init(len_q, len_kv, pl->desc.bottom_right, pl->desc.causal, pl->desc.window_left, kTile, tkv);
   if (tile_q) *tile_q = kTile;
-  if (tile_kv) *tile_kv = kTile;
+  if (tile_kv) *tile_kv = tkv;
   if (n_q) *n_q = g.n_q_tiles;
   if (n_kv) *n_kv = g.n_kv_tiles;
   if ((q_lo || q_hi) && kv_cap < g.n_kv_tiles)

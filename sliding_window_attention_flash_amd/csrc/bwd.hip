@@ -44,6 +44,45 @@ __device__ __forceinline__ typename Elem<T>::vec8 lds_pair4(const T* p) {
   return __builtin_bit_cast(V8, r);
 }
 
+// ---- ordered dQ relay ------------------------------------------------------
+// One q-tile's fp32 partial is touched only through agent-scope atomics: the
+// first visitor exchanges its partial in, middle visitors add, the last
+// visitor's fetch-add returns the sum of all earlier turns, to which it adds
+// its own and writes the 16-bit result.  A single visitor writes directly.
+
+__device__ __forceinline__ void relay_wait(int* semp, int turn, int spin_limit, int* expiries) {
+  int spins = 0;
+  while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != turn) {
+    if (++spins > spin_limit) {  // watchdog: never hang the device
+      atomicAdd(expiries, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void relay_add(float* ap, float val, int turn, int nv, float scale, T* out) {
+  if (nv == 1) {
+    *out = Elem<T>::from_float(scale * val);
+  } else if (turn == 0) {
+    __hip_atomic_exchange(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (turn < nv - 1) {
+    __hip_atomic_fetch_add(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    const float old = __hip_atomic_fetch_add(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *out = Elem<T>::from_float(scale * (old + val));
+  }
+}
+
+// Every wave waits for its own atomics to complete, then one thread passes
+// the turn on.
+__device__ __forceinline__ void relay_release(int* semp, int turn, int nv, int tid) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0 && nv > 1) __hip_atomic_store(semp, turn + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Blocks are dealt to the 8 XCDs round-robin; renumber them so that each XCD
 // runs one contiguous range of logical tiles (neighbouring kv-tiles of one
 // head then share that XCD's L2).
@@ -105,25 +144,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
   }
 
   // Clearing for the main kernel.  Atomic mode: the fp32 accumulator rows of
-  // this tile.  Relay mode: dQ rows of a q-tile that no kv-tile visits (the
-  // relay's last visitor writes every other q-tile).
+  // a q-tile whose dQ is summed there (every q-tile for the per-tile kernel;
+  // for the streaming kernel, q-tiles visited by several chunks, or none).
+  // Relay mode: dQ rows of a q-tile that no kv-tile visits (the relay's last
+  // visitor writes every other q-tile).
   const int rows = min(kTile, s.cap_q - row_base);
   if (rows <= 0) return;
+  SeqSched g;
+  main_sched(p, s, g);
   if (!a.deterministic) {
+    if (p.stream && chunk_visitors(p, g, tile) == 1) return;
     float4* acc = reinterpret_cast<float4*>(a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D);
     const float4 z = {0.f, 0.f, 0.f, 0.f};
     for (int e = tid; e < rows * (D / 4); e += kThreads) acc[e] = z;
-  } else {
-    SeqSched g;
-    g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, kTile);
-    if (g.n_visitors(tile) == 0) {
-      T* dqp = static_cast<T*>(a.dq);
-      typename Elem<T>::vec8 z;
+  } else if (g.n_visitors(tile) == 0) {
+    T* dqp = static_cast<T*>(a.dq);
+    typename Elem<T>::vec8 z;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
-      for (int e = tid; e < rows * CH; e += kThreads)
-        st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
-    }
+    for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
+    for (int e = tid; e < rows * CH; e += kThreads)
+      st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
   }
 }
 
@@ -349,22 +389,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 
     const int64_t acc_row0 = s.stat0 + h * s.stat_hs + q0;
     if (RELAY) {
-      // Ordered relay: visitors of q-tile i add in kv-tile order.  The turn
-      // counts from i's first visitor kv_first(i).  Data moves through
-      // agent-scope atomics, so a turn only has to be ordered after the
-      // previous visitor's release.
+      // Ordered relay: visitors of q-tile i add in kv-tile order; a turn is
+      // counted from i's first visitor kv_first(i).  Every access to the
+      // fp32 partial is an agent-scope atomic read-modify-write (coherent
+      // across XCDs), so a release only has to wait until this block's
+      // atomics have completed (s_waitcnt) before passing the turn on; no
+      // L2 write-back is needed.
       const int turn = g.relay_turn(i, jt), nv = g.n_visitors(i);
       int* semp = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
-      if (tid == 0 && turn > 0) {
-        int spins = 0;
-        while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != turn) {
-          if (++spins > a.spin_limit) {
-            atomicAdd(&a.ctl[1], 1);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-      }
+      if (tid == 0 && turn > 0) relay_wait(semp, turn, a.spin_limit, a.ctl + 1);
       __syncthreads();
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -372,22 +405,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         for (int r = 0; r < 4; ++r) {
           const int lr = 16 * w + 4 * gq + r, qi = q0 + lr;
           if (qi >= s.cap_q) continue;
-          const float val = dQ[db][r];
-          float* ap = a.dq_acc + (acc_row0 + lr) * D + 16 * db + c;
-          if (nv == 1) {
-            dqp[elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * db + c] = Elem<T>::from_float(p.scale * val);
-          } else if (turn == 0) {
-            __hip_atomic_store(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else if (turn < nv - 1) {
-            __hip_atomic_fetch_add(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            const float old = __hip_atomic_fetch_add(ap, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            dqp[elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * db + c] = Elem<T>::from_float(p.scale * (old + val));
-          }
+          relay_add<T>(a.dq_acc + (acc_row0 + lr) * D + 16 * db + c, dQ[db][r], turn, nv, p.scale,
+                       dqp + elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * db + c);
         }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0 && nv > 1) __hip_atomic_store(semp, turn + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      relay_release(semp, turn, nv, tid);
     } else {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -429,6 +450,12 @@ __global__ __launch_bounds__(kThreads) void bwd_cvt_kernel(BwdArgs a) {
   const Seq s = load_seq(p, b);
   const int row_base = tile * kTile;
   const int rows = min(kTile, s.cap_q - row_base);
+  if (p.stream) {
+    // interior q-tiles were written by the streaming kernel itself
+    SeqSched g;
+    main_sched(p, s, g);
+    if (chunk_visitors(p, g, tile) == 1) return;
+  }
   constexpr int CH = D / 8;
   T* dqp = static_cast<T*>(a.dq);
   const float* acc = a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D;
@@ -492,6 +519,7 @@ static hipError_t main_td(const BwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t st) {
+  if (a.p.stream) return launch_bwd_stream(a, st);
   if (a.p.n_kv_tiles == 0) return hipSuccess;
   if (a.dtype == 0) return a.p.D == 64 ? main_td<__bf16, 64>(a, st) : main_td<__bf16, 128>(a, st);
   return a.p.D == 64 ? main_td<_Float16, 64>(a, st) : main_td<_Float16, 128>(a, st);

@@ -39,6 +39,12 @@ struct Problem {
   int64_t sq[3], sk[3], sv[3], so[3], sdo[3], sdq[3], sdk[3], sdv[3];
   int n_q_tiles;              // ceil(seq_q / kTile)
   int n_kv_tiles;             // ceil(seq_kv / kTile)
+  // streaming main kernel (see bwd_stream): kv-step width, kv-steps per
+  // chunk and chunks per sequence; stream == 0 selects the per-tile kernel
+  int stream;
+  int step_kv;
+  int chunk;
+  int n_chunks;
 };
 
 // One sequence (or dense batch entry): valid lengths, slot capacities,
@@ -125,5 +131,19 @@ __device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f3
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The schedule the main kernel runs: kv-tiles of kTile keys (per-tile
+// kernel) or kv-steps of step_kv keys (streaming kernel); q-tiles of kTile.
+__device__ __forceinline__ void main_sched(const Problem& p, const Seq& s, SeqSched& g) {
+  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, p.stream ? p.step_kv : kTile);
+}
+
+// Streaming kernel: number of chunks (blocks) that visit q-tile i.  A q-tile
+// with more than one visiting chunk is a boundary tile whose dQ goes through
+// the fp32 accumulator (relay or atomics); the others are written directly.
+__device__ __forceinline__ int chunk_visitors(const Problem& p, const SeqSched& g, int i) {
+  if (g.n_visitors(i) == 0) return 0;
+  return g.kv_last(i) / p.chunk - g.kv_first(i) / p.chunk + 1;
+}
 
 }  // namespace swa

@@ -26,6 +26,7 @@ struct BwdArgs {
   // workspace
   float* delta;      // [stat rows]
   float* dq_acc;     // [stat rows, D] fp32 dQ accumulator / relay partials
+  float* dq_stash;   // [stat rows, D] streaming relay: partials awaiting their turn
   int* sem;          // [B, Hq, n_q_tiles] relay turn counters
   int* ctl;          // [0] tile ticket, [1] relay watchdog expiries
   float* sink_part;  // [Hq, B, n_q_tiles] per-q-tile dSink partials
@@ -46,6 +47,7 @@ struct FwdArgs {
 
 hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_stream(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_cvt(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dsink(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

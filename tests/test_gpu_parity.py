@@ -32,6 +32,13 @@ SMALL = [
     _wl("sink_gqa_tl_w64_d128", BF16, 2, 6, 3, 128, 257, 257, window_left=64, sink=True),
     _wl("padded_bhsd_w33", F16, 2, 4, 2, 64, 200, 230, bottom_right=True, window_left=33,
         pad_len_q=(200, 77), pad_len_kv=(230, 140)),
+    # multi-head, causal, window <= 128, head_dim 64: the streaming kernel
+    _wl("stream_tl_w128_s1000", BF16, 2, 4, 4, 64, 1000, 1000, window_left=128, scale=0.125),
+    _wl("stream_br_w100_s300x700", BF16, 2, 4, 4, 64, 300, 700, bottom_right=True, window_left=100),
+    _wl("stream_br_w128_s777_f16", F16, 1, 3, 3, 64, 777, 777, bottom_right=True, window_left=128),
+    _wl("stream_padded_w61", F16, 2, 2, 2, 64, 640, 700, bottom_right=True, window_left=61,
+        pad_len_q=(640, 333), pad_len_kv=(700, 500)),
+    _wl("stream_sink_w96_s1500", BF16, 1, 2, 2, 64, 1500, 1500, window_left=96, sink=True),
 ]
 
 
@@ -44,21 +51,21 @@ def test_small_full_oracle(w, det):
     compare_full(w, inp, out)
 
 
-def _thd_small(sink=True, dtype=F16, D=64):
+def _thd_small(sink=True, dtype=F16, D=64, hkv=2):
     # one sequence with no query rows and one with no keys, slots padded
-    lq = (70, 0, 130, 5, 64)
-    lk = (300, 40, 130, 0, 200)
-    cq = (128, 64, 192, 64, 64)
-    ck = (300, 64, 150, 16, 200)
-    return Workload(f"thd_small_sink{int(sink)}_d{D}", dtype, 5, 8, 2, D, max(cq), max(ck),
+    lq = (70, 0, 130, 5, 64, 600)
+    lk = (300, 40, 130, 0, 200, 900)
+    cq = (128, 64, 192, 64, 64, 640)
+    ck = (300, 64, 150, 16, 200, 901)
+    return Workload(f"thd_small_sink{int(sink)}_d{D}_hkv{hkv}", dtype, 6, 8, hkv, D, max(cq), max(ck),
                     bottom_right=True, window_left=90, sink=sink, layout="thd",
                     len_q=lq, len_kv=lk, cap_q=cq, cap_kv=ck)
 
 
 @pytest.mark.parametrize("det", [False, True], ids=["atomic", "relay"])
-@pytest.mark.parametrize("D", [64, 128])
-def test_thd_padded_with_sinks(det, D):
-    w = _thd_small(D=D)
+@pytest.mark.parametrize("D,hkv", [(64, 2), (128, 2), (64, 8)])
+def test_thd_padded_with_sinks(det, D, hkv):
+    w = _thd_small(D=D, hkv=hkv)
     say(f"case {w.name} det={det}")
     inp, out, _ = run_gpu(w, seed=5, deterministic=det)
     compare_full(w, inp, out)

@@ -115,9 +115,11 @@ def _schedule_cases():
     return cases
 
 
+@pytest.mark.parametrize("mha", [False, True], ids=["gqa_tiles", "mha"])
 @pytest.mark.parametrize("lq,lk,w,br,causal", _schedule_cases())
-def test_schedule_covers_the_mask_exactly(lib, lq, lk, w, br, causal):
-    d = _desc(window_left=w, bottom_right=br)
+def test_schedule_covers_the_mask_exactly(lib, lq, lk, w, br, causal, mha):
+    # multi-head causal plans with a window <= 128 schedule 128-key kv-steps
+    d = _desc(window_left=w, bottom_right=br, Hkv=4 if mha else 2)
     d.causal = int(causal)
     plan = api.sdpa_bwd_plan(d)
     s = api.sdpa_bwd_schedule(plan, lq, lk)
@@ -203,9 +205,10 @@ def simulate_relay(s, kv_first=None, timeout_s=2.0):
     return log, expired
 
 
+@pytest.mark.parametrize("mha", [False, True])
 @pytest.mark.parametrize("lq,lk,w,br", [(640, 640, 128, False), (300, 700, 100, True), (500, 500, 0, False)])
-def test_relay_simulation_orders_every_q_tile(lib, lq, lk, w, br):
-    plan = api.sdpa_bwd_plan(_desc(window_left=w, bottom_right=br))
+def test_relay_simulation_orders_every_q_tile(lib, lq, lk, w, br, mha):
+    plan = api.sdpa_bwd_plan(_desc(window_left=w, bottom_right=br, Hkv=4 if mha else 2))
     s = api.sdpa_bwd_schedule(plan, lq, lk)
     log, expired = simulate_relay(s)
     assert not expired
