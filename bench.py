@@ -1,6 +1,9 @@
 """Benchmark of the sliding-window attention backward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload c3|c3_atomic|c2_4k|c2_8k]
+    python bench.py --copy-calibration ...      (appends a copy of known size)
+    python bench.py --summarize-stats DIR --out FILE --command CMD
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --out FILE --command CMD
 
 A step is one full backward, sdpa_bwd_run: the dot preprocess, the main
 window-bounded kernel with its dQ accumulation (ordered relay or fp32
@@ -11,12 +14,19 @@ a left window of 128, bf16, deterministic relay.  Prints one JSON line.
 
 FLOPs count attended (query, key) pairs only: 10 * head_dim per pair per
 query head.  The roofline entry is for the dominant kernel (bwd_main), timed
-with HIP events recorded on its launch stream around every launch.
+with HIP events recorded on its launch stream around every launch.  Its
+``traffic`` is the HBM bytes per launch that rocprofv3's FETCH_SIZE and
+WRITE_SIZE counters read for it, each divided by what the same counter reads
+per byte for an elementwise copy of known size; the figures are kept in a
+text summary under profiles/ together with a hash of the kernel's sources,
+and ``traffic`` is null when the sources no longer match.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +38,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "SWA backward ms & TFLOP/s (attended pairs), b2 h16 d64 W128 S=4k/8k/32k"
+
+# the dominant kernel of the default workload and the files that define it
+MAIN_KERNEL = "bwd_stream_kernel"
+MAIN_KERNEL_SOURCES = [
+    "sliding_window_attention_flash_amd/csrc/bwd_stream.hip",
+    "sliding_window_attention_flash_amd/csrc/common.h",
+    "sliding_window_attention_flash_amd/csrc/kernels.h",
+    "sliding_window_attention_flash_amd/csrc/swa_sched.h",
+    "sliding_window_attention_flash_amd/build.py",
+]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_stream_c3_s32768_hbm_traffic.txt")
+COPY_BYTES = 1 << 30  # calibration copy: reads and writes this many bytes
+COPY_KERNEL = "neg_kernel"
 
 
 def _hip():
@@ -96,6 +119,128 @@ def time_backward(w, steps, warmup, seed=0):
     return wall * 1e3, sum(main_ms) / len(main_ms), expiries
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in MAIN_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read() + b"\0")
+    return h.hexdigest()
+
+
+def stored_traffic(w):
+    """HBM bytes per launch of the main kernel from the committed counter
+    summary, or None if there is none for this workload or the kernel's
+    sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = [json.loads(x[len("TRAFFIC "):]) for x in fh if x.startswith("TRAFFIC ")]
+    except OSError:
+        return None
+    for r in rec:
+        if r.get("workload") == w.name and r.get("source_sha256") == kernel_source_hash():
+            return r["traffic_bytes_per_launch"]
+    return None
+
+
+def copy_calibration():
+    """An elementwise kernel that reads COPY_BYTES and writes COPY_BYTES
+    (torch.neg into a second buffer), launched three times."""
+    import torch
+    x = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    x.zero_()
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+
+
+# ---- profile summaries --------------------------------------------------------
+
+
+def _rows(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def summarize_stats(d, out, command, bench_json=None):
+    rows = _rows(_find(d, "kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel statistics, {MAIN_KERNEL} workload", "", "command:", f"    {command}", "",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    for r in rows:
+        name = r["Name"]
+        short = name if len(name) < 90 else name[:87] + "..."
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}  {short}")
+    if bench_json:
+        with open(bench_json) as fh:
+            b = json.loads([x for x in fh if x.startswith("{")][-1])
+        lines += ["", "bench line of the same run (HIP events on the launch stream, profiler attached):",
+                  f"    main_kernel_ms = {b['extra']['main_kernel_ms']:.4f}, ms_per_step = {b['ms_per_step']:.4f}"]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter_means(d, counter):
+    """{kernel name: (dispatches, mean counter value per dispatch)}"""
+    acc = {}
+    for r in _rows(_find(d, "counter_collection.csv")):
+        if r["Counter_Name"] != counter:
+            continue
+        k = r["Kernel_Name"]
+        n, v = acc.get(k, (0, 0.0))
+        acc[k] = (n + 1, v + float(r["Counter_Value"]))
+    return {k: (n, v / n) for k, (n, v) in acc.items()}
+
+
+def _pick(means, pat):
+    hits = [(k, nv) for k, nv in means.items() if pat in k]
+    if len(hits) != 1:
+        raise RuntimeError(f"expected one kernel matching {pat!r}, found {[k[:80] for k, _ in hits]}")
+    return hits[0][1]
+
+
+def summarize_traffic(fetch_dir, write_dir, out, command, workload):
+    w = workloads()[workload]
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    nf, kf = _pick(fetch, MAIN_KERNEL)
+    nw, kw = _pick(write, MAIN_KERNEL)
+    _, cf = _pick(fetch, COPY_KERNEL)
+    _, cw = _pick(write, COPY_KERNEL)
+    copy_kib = COPY_BYTES / 1024
+    ff, fw = cf / copy_kib, cw / copy_kib  # counter KiB per byte-KiB moved
+    traffic = kf * 1024 / ff + kw * 1024 / fw
+    algo = main_kernel_bytes(w)
+    rec = {"kernel": MAIN_KERNEL, "workload": w.name, "launches_fetch": nf, "launches_write": nw,
+           "fetch_kib_per_launch": kf, "write_kib_per_launch": kw, "copy_bytes": COPY_BYTES,
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_factor": ff, "write_factor": fw,
+           "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": algo,
+           "source_sha256": kernel_source_hash()}
+    lines = [f"# HBM traffic of {MAIN_KERNEL}, workload {w.name}", "",
+             "commands (FETCH_SIZE pass, then WRITE_SIZE pass):", *[f"    {c}" for c in command], "",
+             f"FETCH_SIZE per launch   {kf:14.1f} KiB  ({nf} launches)",
+             f"WRITE_SIZE per launch   {kw:14.1f} KiB  ({nw} launches)",
+             f"calibration copy of {COPY_BYTES} bytes ({COPY_KERNEL}): FETCH_SIZE {cf:.1f} KiB, "
+             f"WRITE_SIZE {cw:.1f} KiB",
+             f"factors (counter bytes per byte moved): fetch {ff:.4f}, write {fw:.4f}",
+             f"HBM traffic per launch  {traffic / 1e6:14.2f} MB  (fetch {kf * 1024 / ff / 1e6:.2f} MB, "
+             f"write {kw * 1024 / fw / 1e6:.2f} MB)",
+             f"algorithmic bytes       {algo / 1e6:14.2f} MB  (traffic / algorithmic = {traffic / algo:.3f})",
+             "", "TRAFFIC " + json.dumps(rec)]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(w):
     """The fp64 oracle's backward timed on a bounded slice of the workload
     (batch 0, one query head per host thread, each with its own kv head so
@@ -129,11 +274,23 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 4k / 8k / atomic side timings")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"after timing, copy {COPY_BYTES} bytes three times (counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--bench-json")
+    ap.add_argument("--out")
+    ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.out, " ".join(args.command), args.bench_json)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.out, args.command, args.workload)
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the per-GPU kernel is the one-GPU workload; see DESIGN.md for how it would shard)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the timed kernel is "
+              "one GPU's share of the work at its full shape", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -149,7 +306,9 @@ def main():
     tflops = fl / (ms * 1e-3) / 1e12
     nbytes = main_kernel_bytes(w)
     achieved = nbytes / (main_ms * 1e-3) / 1e9
-    extra = {"main_kernel_ms": main_ms, "main_kernel_attended_tflops": fl / (main_ms * 1e-3) / 1e12,
+    extra = {"main_kernel": MAIN_KERNEL, "main_kernel_ms": main_ms,
+             "main_kernel_algorithmic_bytes": nbytes,
+             "main_kernel_attended_tflops": fl / (main_ms * 1e-3) / 1e12,
              "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS, "relay_expiries": exp,
              "attended_flops": fl}
     if not args.no_extra:
@@ -167,12 +326,14 @@ def main():
                    "mask": "causal_bottom_right" if w.bottom_right else "causal_top_left",
                    "dq_mode": "relay" if w.deterministic else "atomic"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(w)},
         "extra": extra,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
-    print(json.dumps(line))
+    print(json.dumps(line), flush=True)
+    if args.copy_calibration:
+        copy_calibration()
 
 
 if __name__ == "__main__":

@@ -20,7 +20,7 @@ SOURCES = ["api.cpp", "bwd.hip", "bwd_stream.hip", "fwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
-    # packed fp32 instructions stay disabled ("Build")
+    # no packed fp32 instructions (v_pk_*_f32) in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
