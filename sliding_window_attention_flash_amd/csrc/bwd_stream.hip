@@ -21,21 +21,34 @@
 // while the current step computes.  One block of 8 waves runs per CU (two
 // waves per SIMD).
 //
-// Per visit (q-tile i of 64 rows, kv-step of 128 keys; wave w owns keys
-// 16w .. 16w + 15):
-//   S, dP  = Q_i K^T, dO_i V^T   A: Q / dO rows (LDS), B: the wave's K / V rows
-//   P, dS  = exp2(S c - LSE_i), P (dP - delta_i)           (fp32, masked)
-//   dV^T  += dO_i^T P,  dK^T += Q_i^T dS                   A: transposed reads
-//   dQ_i  += dS K   (wave w: rows 16 (w mod 4), head-dim half w / 4)
-// All products are v_mfma_f32_16x16x32 (bf16 / f16 in, fp32 accumulate).  A
-// wave skips the 16 x 16 blocks the mask hides entirely, and evaluates the
-// mask only in blocks it cuts.
+// One kv-step of 128 keys runs in two phases with one barrier between them.
 //
-// LDS tiles are 64 elements (128 bytes) per row, unpadded, with the 16-byte
-// chunks of row r permuted by XOR with (r mod 8).  Measured on gfx950
-// (SQ_LDS_BANK_CONFLICT): 16-byte row reads are conflict-free in any layout,
-// and this permutation also makes the transposed reads conflict-free (a
-// plain 128-byte pitch costs 4x, a 144-byte pitch 2x).
+// Phase 1 (per wave, no barrier): wave w owns keys 16w .. 16w + 15 and walks
+// only the 16-row query blocks its window band reaches -- rows
+// [key - diag, key + W - diag] of its keys, at most 10 blocks for W <= 128,
+// the same count for every wave -- two blocks at a time:
+//   S, dP  = Q K^T, dO V^T        A: Q / dO rows (LDS), B: K / V rows (regs)
+//   P, dS  = exp2(S c - LSE), P (dP - delta)          (fp32, masked)
+//   dV^T  += dO^T P,  dK^T += Q^T dS                  A: transposed LDS reads
+// and writes dS^T into its own LDS band: 16 keys x 12 block positions, where
+// position 1 + n holds the wave's n-th block and positions 0 and 11 (and
+// any position past its last block) hold zeros.
+//
+// Phase 2 (after the barrier): wave (r, h) = (w mod 4, w / 4) owns rows
+// 16 r .. 16 r + 15 of every q-tile the step feeds and head-dim half h, and
+// accumulates dQ^T += K^T dS^T over the key pairs whose bands reach those
+// rows; the band's zero positions stand in for blocks outside a band, so
+// no lane ever branches on the mask.
+//
+// All products are v_mfma_f32_16x16x32 (bf16 / f16 in, fp32 accumulate).
+//
+// LDS tiles of Q, dO and K are 64 elements (128 bytes) per row, unpadded,
+// with the 16-byte chunks of row r permuted by XOR with (r mod 8).
+// Measured on gfx950 (SQ_LDS_BANK_CONFLICT): 16-byte row reads are
+// conflict-free in any layout, and this permutation also makes the
+// transposed reads conflict-free (a plain 128-byte pitch costs 4x).  Band
+// rows are 208 elements apart (416 bytes): the 8 rows one half-wave's
+// transposed read touches then fall on 8 disjoint groups of 8 banks.
 // Transposed operands use ds_read_b64_tr_b16: within each 16-lane group,
 // lane i receives element (i % 4) of lanes i / 4 + 4e (e = 0..3), so a lane
 // pointing at row r0 + i / 4, column c0 + 4 (i % 4) receives rows
@@ -48,10 +61,14 @@ namespace {
 
 constexpr int SD = 64;        // head dim
 constexpr int STEP = 128;     // keys per kv-step
-constexpr int NSLOT = 6;      // ring slots: up to 5 active q-tiles + 1
+constexpr int NSLOT = 5;      // ring slots = most q-tiles one kv-step feeds
 constexpr int NACT = 5;       // most q-tiles one kv-step visits (W <= 128)
 constexpr int TROW = 64;      // elements per LDS tile row (128 bytes)
-constexpr int NTHR = 512;     // 8 waves
+constexpr int NWAVE = 8;
+constexpr int NTHR = 64 * NWAVE;
+constexpr int NPAIR = 5;      // block pairs a band holds
+constexpr int BPOS = 2 * NPAIR + 2;  // band block positions, guards included
+constexpr int BP = 208;       // band row pitch (elements), >= 16 * BPOS
 
 typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
 
@@ -75,14 +92,21 @@ __device__ __forceinline__ u32x2 ld_tr4(const T* lds_elem) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// 8 contraction values for lane (c, g): rows r0 + 4g + e (e < 4) and
-// r0 + 16 + 4g + (e - 4) of one column, from a lane offset.
+// 8 contraction values for lane (c, g) from two transposed reads: e < 4 from
+// the read at p0, e >= 4 from the read at p1.
 template <typename T>
-__device__ __forceinline__ typename Elem<T>::vec8 tr_pair(const T* p) {
-  const u32x2 lo = ld_tr4(p);
-  const u32x2 hi = ld_tr4(p + 16 * TROW);
+__device__ __forceinline__ typename Elem<T>::vec8 tr_two(const T* p0, const T* p1) {
+  const u32x2 lo = ld_tr4(p0);
+  const u32x2 hi = ld_tr4(p1);
   u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(typename Elem<T>::vec8, r);
+}
+
+template <typename T>
+__device__ __forceinline__ u32x2 pack4(float x0, float x1, float x2, float x3) {
+  T v[4] = {Elem<T>::from_float(x0), Elem<T>::from_float(x1), Elem<T>::from_float(x2),
+            Elem<T>::from_float(x3)};
+  return __builtin_bit_cast(u32x2, v);
 }
 
 }  // namespace
@@ -95,13 +119,13 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   __shared__ __align__(16) float sLse[NSLOT][kTile];
   __shared__ __align__(16) float sDelta[NSLOT][kTile];
   __shared__ __align__(16) T sK[STEP * TROW];
-  __shared__ __align__(16) T sdSt[2][STEP * TROW];  // dS^T [key][q], double-buffered by visit
+  __shared__ __align__(16) T sBand[NWAVE][16 * BP];  // dS^T [key][block position, row]
   __shared__ int sTicket;
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (scalar)
-  const int wr = w & 3, wd = w >> 2;                        // dQ rows 16 wr, head-dim half wd
+  const int wr = w & 3, wd = w >> 2;                        // phase 2: rows 16 wr, head-dim half wd
 
   // Chunk-major tickets: a chunk's relay predecessor (same head, chunk - 1)
   // always started earlier.
@@ -128,92 +152,80 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) zero8[e] = Elem<T>::from_float(0.f);
 
+  // bands start (and their guard positions stay) zero
+  for (int e = tid; e < NWAVE * 16 * BP / 8; e += NTHR) reinterpret_cast<V8*>(&sBand[0][0])[e] = zero8;
+
   // ---- per-lane LDS offsets (elements) --------------------------------------
-  int rd_off[2];  // row read: row c, chunk 4 ks + gq
+  int rd_off[2];  // row read of a 16-row block: row c, chunk 4 ks + gq
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) rd_off[ks] = tile_off(c, 4 * ks + gq);
-  int tr_off[4];  // transposed read of a 16-column block db
+  int tr_off[4];  // transposed read of a 16-row block, columns 16 db ..
 #pragma unroll
   for (int db = 0; db < 4; ++db) tr_off[db] = tr_lane_off(c, gq, db);
-  const int tr_off_q = tr_lane_off(c, gq, wr);  // dS^T columns 16 wr .. 16 wr + 15
   // K^T columns of this wave's dQ half (kept out of a runtime-indexed array,
   // which the compiler would place in scratch memory)
   const int tr_off_k0 = tr_lane_off(c, gq, 2 * wd), tr_off_k1 = tr_lane_off(c, gq, 2 * wd + 1);
-  int ds_off[2][2];  // dS^T write: row 16w + c, q 32 s2 + 16 hf + 4 gq
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      ds_off[s2][hf] = c * TROW + (((4 * s2 + 2 * hf + (gq >> 1)) ^ swz(c)) << 3) + 4 * (gq & 1);
+  const int band_wr = c * BP + 4 * gq;                         // dS^T write: key c, rows 4 gq ..
+  const int band_rd = (4 * gq + (c >> 2)) * BP + 4 * (c & 3);  // transposed read
+  T* const myband = sBand[w];
 
   // ---- loaders ------------------------------------------------------------
-  // V rows of the wave's 16 keys (B operand of dP = dO V^T); the K rows (B
-  // operand of S = Q K^T) are read from the step's LDS K tile.
-  V8 kB[2], vB[2], vBn[2];
-  auto load_v_regs = [&](int j, V8 (&vx)[2]) {
-    const int key = j * STEP + 16 * w + c;
-    const bool ok = key < s.len_kv;
-    const int64_t vo = elem_off(p, p.sv, b, s.row0_kv, h, ok ? key : 0);
+  // K and V rows of the wave's 16 keys in the MFMA B layout (key c, head-dim
+  // 32 ks + 8 gq ..); the K rows are also this wave's share of the LDS K
+  // tile.  Rows past the sequence are clamped to a valid row and zeroed
+  // when the registers are taken into use.
+  V8 kB[2], vB[2], kBn[2], vBn[2];
+  auto load_kv = [&](int j, V8 (&kx)[2], V8 (&vx)[2]) {
+    const int key = clampi(j * STEP + 16 * w + c, 0, max(s.cap_kv - 1, 0));
+    const int64_t ko = elem_off(p, p.sk, b, s.row0_kv, h, key);
+    const int64_t vo = elem_off(p, p.sv, b, s.row0_kv, h, key);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vx[ks] = ok ? gld8(vp + vo + 32 * ks + 8 * gq) : zero8;
-  };
-  auto read_k_regs = [&]() {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) kB[ks] = *reinterpret_cast<const V8*>(sK + 16 * w * TROW + rd_off[ks]);
-  };
-  V8 ktn[2];  // K rows of the next step: 128 rows x 8 chunks over 512 threads
-  auto load_k_rows = [&](int j) {
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const int r = (tid >> 3) + 64 * ps, ch = tid & 7, key = j * STEP + r;
-      ktn[ps] = key < s.len_kv ? gld8(kp + elem_off(p, p.sk, b, s.row0_kv, h, key) + 8 * ch) : zero8;
+    for (int ks = 0; ks < 2; ++ks) {
+      kx[ks] = gld8(kp + ko + 32 * ks + 8 * gq);
+      vx[ks] = gld8(vp + vo + 32 * ks + 8 * gq);
     }
   };
-  auto store_k_rows = [&]() {
+  auto take_kv = [&](int j, const V8 (&kx)[2], const V8 (&vx)[2]) {
+    const bool ok = j * STEP + 16 * w + c < s.len_kv;
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const int r = (tid >> 3) + 64 * ps, ch = tid & 7;
-      *reinterpret_cast<V8*>(&sK[tile_off(r, ch)]) = ktn[ps];
+    for (int ks = 0; ks < 2; ++ks) {
+      kB[ks] = ok ? kx[ks] : zero8;
+      vB[ks] = ok ? vx[ks] : zero8;
     }
   };
   struct QRegs {
     V8 q, o;
     float lse, delta;
+    int tile;
   };
+  // only called for q-tiles the schedule visits, so the sequence has rows
   auto load_q_tile = [&](int i, QRegs& r) {
-    const int row = tid >> 3, ch = tid & 7, qi = i * kTile + row;
-    if (qi < s.len_q) {
-      r.q = gld8(qp + elem_off(p, p.sq, b, s.row0_q, h, qi) + 8 * ch);
-      r.o = gld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, qi) + 8 * ch);
-    } else {
-      r.q = zero8;
-      r.o = zero8;
-    }
+    r.tile = i;
+    const int row = tid >> 3, ch = tid & 7, qi = min(i * kTile + row, s.len_q - 1);
+    r.q = gld8(qp + elem_off(p, p.sq, b, s.row0_q, h, qi) + 8 * ch);
+    r.o = gld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, qi) + 8 * ch);
     if (tid < kTile) {
-      const int q2 = i * kTile + tid;
-      if (q2 < s.len_q) {
-        const int64_t si = s.stat0 + h * s.stat_hs + q2;
-        r.lse = a.lse[si] * kLog2e;
-        r.delta = a.delta[si];
-      } else {
-        r.lse = INFINITY;  // exp2(x - inf) = 0: padding rows carry no weight
-        r.delta = 0.f;
-      }
+      const int64_t si = s.stat0 + h * s.stat_hs + min(i * kTile + tid, s.len_q - 1);
+      r.lse = a.lse[si];
+      r.delta = a.delta[si];
     }
   };
-  auto store_q_tile = [&](int i, const QRegs& r) {
-    const int sl = i % NSLOT, row = tid >> 3, ch = tid & 7;
-    *reinterpret_cast<V8*>(&sQ[sl][tile_off(row, ch)]) = r.q;
-    *reinterpret_cast<V8*>(&sdO[sl][tile_off(row, ch)]) = r.o;
+  auto store_q_tile = [&](const QRegs& r) {
+    const int sl = r.tile % NSLOT, row = tid >> 3, ch = tid & 7;
+    const bool ok = r.tile * kTile + row < s.len_q;
+    *reinterpret_cast<V8*>(&sQ[sl][tile_off(row, ch)]) = ok ? r.q : zero8;
+    *reinterpret_cast<V8*>(&sdO[sl][tile_off(row, ch)]) = ok ? r.o : zero8;
     if (tid < kTile) {
-      sLse[sl][tid] = r.lse;
-      sDelta[sl][tid] = r.delta;
+      const bool okr = r.tile * kTile + tid < s.len_q;
+      // exp2(x - inf) = 0: padding rows carry no weight
+      sLse[sl][tid] = okr ? r.lse * kLog2e : INFINITY;
+      sDelta[sl][tid] = okr ? r.delta : 0.f;
     }
   };
 
   // ---- accumulators -------------------------------------------------------
-  // dQ of q-tile q_lo(j) + k in dQa[k] (rows q = 16 wr + 4gq + r, d =
-  // 16 (2 wd + e) + c), shifted down when q_lo advances between kv-steps
+  // dQ^T of q-tile q_lo(j) + k in dQa[k][e]: head-dim 16 (2 wd + e) + 4 gq + r,
+  // row 16 wr + c; shifted down when q_lo advances between kv-steps
   f32x4 dQa[NACT][2];
   f32x4 dVa[4], dKa[4];  // dV^T / dK^T[d = 16db + 4gq + r][key = 16w + c]
 #pragma unroll
@@ -222,61 +234,67 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   for (int db = 0; db < 4; ++db) dVa[db] = dKa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- dQ of a retiring q-tile ------------------------------------------------
-  auto acc_ptr = [&](int i, int r, int e) -> float* {
-    const int qi = i * kTile + 16 * wr + 4 * gq + r;
-    return a.dq_acc + (s.stat0 + h * s.stat_hs + qi) * SD + 16 * (2 * wd + e) + c;
+  auto q_row = [&](int i) { return i * kTile + 16 * wr + c; };
+  auto acc_ptr = [&](int i, int e) -> float* {  // 4 consecutive head-dim values
+    return a.dq_acc + (s.stat0 + h * s.stat_hs + q_row(i)) * SD + 16 * (2 * wd + e) + 4 * gq;
   };
   auto retire = [&](int i, f32x4 (&acc)[2]) {  // block-uniform arguments
     const int first = g.kv_first(i) / p.chunk, last = g.kv_last(i) / p.chunk;
+    const int qi = q_row(i);
     if (first == last) {
+      if (qi < s.cap_q) {
+        T* row = dqp + elem_off(p, p.sdq, b, s.row0_q, h, qi) + 32 * wd + 4 * gq;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qi = i * kTile + 16 * wr + 4 * gq + r;
-        if (qi >= s.cap_q) continue;
-        T* row = dqp + elem_off(p, p.sdq, b, s.row0_q, h, qi) + 32 * wd + c;
-        row[0] = Elem<T>::from_float(p.scale * acc[0][r]);
-        row[16] = Elem<T>::from_float(p.scale * acc[1][r]);
+        for (int e = 0; e < 2; ++e)
+          *reinterpret_cast<u32x2*>(row + 16 * e) =
+              pack4<T>(p.scale * acc[e][0], p.scale * acc[e][1], p.scale * acc[e][2], p.scale * acc[e][3]);
       }
     } else if (!RELAY) {
+      if (qi < s.len_q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (i * kTile + 16 * wr + 4 * gq + r < s.len_q) {
-          unsafeAtomicAdd(acc_ptr(i, r, 0), acc[0][r]);
-          unsafeAtomicAdd(acc_ptr(i, r, 1), acc[1][r]);
-        }
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(acc_ptr(i, e) + r, acc[e][r]);
     } else if (first == chunk) {
       // first visiting chunk of a boundary tile: turn 0, no wait
       int* semp = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
+      if (qi < s.cap_q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (i * kTile + 16 * wr + 4 * gq + r < s.cap_q)
+        for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int e = 0; e < 2; ++e)
-            __hip_atomic_exchange(acc_ptr(i, r, e), acc[e][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int r = 0; r < 4; ++r)
+            __hip_atomic_exchange(acc_ptr(i, e) + r, acc[e][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) __hip_atomic_store(semp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       // a later turn: stash the partial; it is added in turn order once this
       // chunk has finished its own kv-steps
+      if (qi < s.cap_q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (i * kTile + 16 * wr + 4 * gq + r < s.cap_q)
-#pragma unroll
-          for (int e = 0; e < 2; ++e) a.dq_stash[acc_ptr(i, r, e) - a.dq_acc] = acc[e][r];
+        for (int e = 0; e < 2; ++e)
+          *reinterpret_cast<f32x4*>(a.dq_stash + (acc_ptr(i, e) - a.dq_acc)) = acc[e];
     }
     acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
+  // ---- band geometry ----------------------------------------------------------
+  // 16-row blocks that keys kv0 + 16 v .. + 15 see: rows t = row + diag - key
+  // in [0, W]; clipped to the step's q-tiles; empty past the keys.
+  auto band_lo = [&](int kv0, int v, int qlo) {
+    return max(floor_div(kv0 + 16 * v - g.diag, 16), 4 * qlo);
+  };
+  auto band_hi = [&](int kv0, int v, int qhi) {
+    if (kv0 + 16 * v >= s.len_kv) return INT32_MIN / 2;
+    return min(floor_div(kv0 + 16 * v + 15 + W - g.diag, 16), 4 * qhi - 1);
+  };
+
   // ---- prologue -------------------------------------------------------------
-  load_v_regs(j0, vB);
-  load_k_rows(j0);
-  store_k_rows();
+  load_kv(j0, kBn, vBn);
+  take_kv(j0, kBn, vBn);
   int loaded_hi = g.q_lo(j0);  // the ring holds q-tiles [.., loaded_hi)
   int acc_lo = g.q_lo(j0);     // q-tile held in dQa[0]
   QRegs pf[2];
-  int pf_lo = 0, pf_n = 0;
-  int vpar = 0;  // dS^T buffer of the current visit
 
   for (int j = j0; j < j1; ++j) {
     const int qlo = g.q_lo(j), nit = min(g.n_iters(j), NACT), qhi = qlo + nit;
@@ -284,10 +302,11 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     for (; loaded_hi < qhi; ++loaded_hi) {  // chunk start and gaps only
       QRegs t;
       load_q_tile(loaded_hi, t);
-      store_q_tile(loaded_hi, t);
+      store_q_tile(t);
     }
-    __syncthreads();  // ring and sK ready
-    read_k_regs();
+    __syncthreads();  // T: ring ready; sK and the bands are free
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<V8*>(&sK[tile_off(16 * w + c, 4 * ks + gq)]) = kB[ks];
     for (; acc_lo < qlo; ++acc_lo) {  // realign dQa[0] with q_lo(j)
 #pragma unroll
       for (int k = 0; k + 1 < NACT; ++k) {
@@ -297,106 +316,113 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       dQa[NACT - 1][0] = dQa[NACT - 1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // prefetch of the next kv-step: K / V rows and its new q-tiles
     const bool has_next = j + 1 < j1;
+    int pf_n = 0;
     if (has_next) {
-      load_v_regs(j + 1, vBn);
-      load_k_rows(j + 1);
+      load_kv(j + 1, kBn, vBn);
       const int nlo = g.q_lo(j + 1), nhi = nlo + min(g.n_iters(j + 1), NACT);
-      pf_lo = max(loaded_hi, nlo);
+      const int pf_lo = max(loaded_hi, nlo);
       pf_n = max(0, min(2, nhi - pf_lo));
       if (pf_n > 0) load_q_tile(pf_lo, pf[0]);
       if (pf_n > 1) load_q_tile(pf_lo + 1, pf[1]);
     }
 
+    // ---- phase 1: this wave's band --------------------------------------------
     const int kv0 = j * STEP;
     // t(row, key) = row + diag - key; visible iff 0 <= t <= W.  A key past
     // the sequence is pushed out of every window through its lane base.
     const int keyl = kv0 + 16 * w + c;
     const int tkey = keyl < s.len_kv ? g.diag - keyl : -(1 << 29);
-    const bool keys_ok = kv0 + STEP <= s.len_kv;  // no key past the sequence
-
+    const int blo = band_lo(kv0, w, qlo), bhi = band_hi(kv0, w, qhi);
+    const int npairs = min(max(bhi - blo + 2, 0) >> 1, NPAIR);
+    for (int pr = 0; pr < npairs; ++pr) {
+      const int b0 = blo + 2 * pr;
+      const bool has1 = b0 + 1 <= bhi;
+      const int b1 = has1 ? b0 + 1 : b0;  // a valid block either way
+      const int sl0 = (b0 >> 2) % NSLOT, sl1 = (b1 >> 2) % NSLOT;
+      const T* q0 = sQ[sl0] + 16 * (b0 & 3) * TROW;
+      const T* o0 = sdO[sl0] + 16 * (b0 & 3) * TROW;
+      const T* q1 = sQ[sl1] + 16 * (b1 & 3) * TROW;
+      const T* o1 = sdO[sl1] + 16 * (b1 & 3) * TROW;
+      f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, D0 = S0, S1 = S0, D1 = S0;
 #pragma unroll
-    for (int k = 0; k < NACT; ++k) {
-      if (k >= nit) break;
-      const int i = qlo + k, sl = i % NSLOT, q0 = i * kTile;
-      const T* tQ = sQ[sl];
-      const T* tO = sdO[sl];
-      // t of (row q0, key kv0 + 16w); block mb spans t in [u - 15, u + 15]
-      // with u = u0 + 16 mb
-      const int u0 = q0 + g.diag - (kv0 + 16 * w);
-      f32x4 S[4], dP[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        S[mb] = dP[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int um = u0 + 16 * mb;
-        if (um + 15 < 0 || um - 15 > W) continue;
+      for (int ks = 0; ks < 2; ++ks) {
+        S0 = mfma16(*reinterpret_cast<const V8*>(q0 + rd_off[ks]), kB[ks], S0);
+        D0 = mfma16(*reinterpret_cast<const V8*>(o0 + rd_off[ks]), vB[ks], D0);
+      }
+      if (has1) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          S[mb] = mfma16(*reinterpret_cast<const V8*>(tQ + 16 * mb * TROW + rd_off[ks]), kB[ks], S[mb]);
-          dP[mb] = mfma16(*reinterpret_cast<const V8*>(tO + 16 * mb * TROW + rd_off[ks]), vB[ks], dP[mb]);
+          S1 = mfma16(*reinterpret_cast<const V8*>(q1 + rd_off[ks]), kB[ks], S1);
+          D1 = mfma16(*reinterpret_cast<const V8*>(o1 + rd_off[ks]), vB[ks], D1);
         }
       }
-      // P and dS in the accumulator layout (rows 16mb + 4gq + r)
-      V8 pP[2], pS[2];
+      float pv[8], dsv[8];
+      {
+        const int r0 = 16 * (b0 & 3) + 4 * gq, r1 = 16 * (b1 & 3) + 4 * gq;
+        const float4 lse0 = *reinterpret_cast<const float4*>(&sLse[sl0][r0]);
+        const float4 del0 = *reinterpret_cast<const float4*>(&sDelta[sl0][r0]);
+        const float4 lse1 = *reinterpret_cast<const float4*>(&sLse[sl1][r1]);
+        const float4 del1 = *reinterpret_cast<const float4*>(&sDelta[sl1][r1]);
+        const float lsev[8] = {lse0.x, lse0.y, lse0.z, lse0.w, lse1.x, lse1.y, lse1.z, lse1.w};
+        const float delv[8] = {del0.x, del0.y, del0.z, del0.w, del1.x, del1.y, del1.z, del1.w};
+        const float sv[8] = {S0[0], S0[1], S0[2], S0[3], S1[0], S1[1], S1[2], S1[3]};
+        const float dv[8] = {D0[0], D0[1], D0[2], D0[3], D1[0], D1[1], D1[2], D1[3]};
+        const int tb0 = 16 * b0 + 4 * gq + tkey;
+        // block 1 is masked out entirely when it is past the band
+        const int tb1 = has1 ? 16 * b1 + 4 * gq + tkey : -(1 << 29);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int um = u0 + 16 * mb;
-        const bool any = um + 15 >= 0 && um - 15 <= W;
-        const bool full = keys_ok && um - 15 >= 0 && um + 15 <= W;
-        float pv[4] = {0.f, 0.f, 0.f, 0.f}, dsv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (any) {
-          const float4 lse4 = *reinterpret_cast<const float4*>(&sLse[sl][16 * mb + 4 * gq]);
-          const float4 del4 = *reinterpret_cast<const float4*>(&sDelta[sl][16 * mb + 4 * gq]);
-          const float lsev[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
-          const float delv[4] = {del4.x, del4.y, del4.z, del4.w};
-          const int tb = q0 + 16 * mb + 4 * gq + tkey;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x = S[mb][r] * p.scale_log2 - lsev[r];
-            if (!full) x = (unsigned)(tb + r) <= (unsigned)W ? x : -INFINITY;
-            pv[r] = fast_exp2(x);
-            dsv[r] = pv[r] * (dP[mb][r] - delv[r]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pP[mb >> 1][(mb & 1) * 4 + r] = Elem<T>::from_float(pv[r]);
-          pS[mb >> 1][(mb & 1) * 4 + r] = Elem<T>::from_float(dsv[r]);
+        for (int r = 0; r < 8; ++r) {
+          const int t = (r < 4 ? tb0 : tb1) + (r & 3);
+          const float x = sv[r] * p.scale_log2 - lsev[r];
+          pv[r] = (unsigned)t <= (unsigned)W ? fast_exp2(x) : 0.f;
+          dsv[r] = pv[r] * (dv[r] - delv[r]);
         }
       }
-      // dS^T into this visit's buffer: the visit before last read the same
-      // buffer for its dQ, and every wave finished that before it passed the
-      // previous visit's barrier
-      T* dst = sdSt[vpar];
-      vpar ^= 1;
+      const u32x2 p0 = pack4<T>(pv[0], pv[1], pv[2], pv[3]), p1 = pack4<T>(pv[4], pv[5], pv[6], pv[7]);
+      const u32x2 s0 = pack4<T>(dsv[0], dsv[1], dsv[2], dsv[3]);
+      const u32x2 s1 = pack4<T>(dsv[4], dsv[5], dsv[6], dsv[7]);
+      const V8 pP = __builtin_bit_cast(V8, u32x4{p0[0], p0[1], p1[0], p1[1]});
+      const V8 pS = __builtin_bit_cast(V8, u32x4{s0[0], s0[1], s1[0], s1[1]});
+      // dS^T of blocks b0, b1 at band positions 2 pr + 1, 2 pr + 2
+      *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 1)) = s0;
+      *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 2)) = s1;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const u32x4 v = __builtin_bit_cast(u32x4, pS[s2]);
-        T* base = dst + 16 * w * TROW;
-        *reinterpret_cast<u32x2*>(base + ds_off[s2][0]) = u32x2{v[0], v[1]};
-        *reinterpret_cast<u32x2*>(base + ds_off[s2][1]) = u32x2{v[2], v[3]};
+      for (int db = 0; db < 4; ++db) {
+        dVa[db] = mfma16(tr_two(o0 + tr_off[db], o1 + tr_off[db]), pP, dVa[db]);
+        dKa[db] = mfma16(tr_two(q0 + tr_off[db], q1 + tr_off[db]), pS, dKa[db]);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS  (skip 32-row halves whose P is zero)
+    }
+    for (int pr = npairs; pr < NPAIR; ++pr) {  // positions past the band
+      *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 1)) = u32x2{0u, 0u};
+      *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 2)) = u32x2{0u, 0u};
+    }
+
+    __syncthreads();  // A: bands and sK complete; ring slots of tiles before q_lo(j + 1) free
+    if (pf_n > 0) store_q_tile(pf[0]);
+    if (pf_n > 1) store_q_tile(pf[1]);
+    loaded_hi += pf_n;
+
+    // ---- phase 2: dQ^T += K^T dS^T ------------------------------------------
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int um0 = u0 + 32 * s2;  // blocks mb = 2 s2, 2 s2 + 1: t in [um0 - 15, um0 + 31]
-        if (um0 + 31 < 0 || um0 - 15 > W) continue;
+    for (int ks = 0; ks < 4; ++ks) {
+      const int wa = 2 * ks, wb = 2 * ks + 1;
+      const int lo_a = band_lo(kv0, wa, qlo), hi_a = band_hi(kv0, wa, qhi);
+      const int lo_b = band_lo(kv0, wb, qlo), hi_b = band_hi(kv0, wb, qhi);
+      if (hi_a < lo_a && hi_b < lo_b) continue;
+      const T* kr = sK + 32 * ks * TROW;
+      const V8 kt0 = tr_two(kr + tr_off_k0, kr + 16 * TROW + tr_off_k0);
+      const V8 kt1 = tr_two(kr + tr_off_k1, kr + 16 * TROW + tr_off_k1);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dVa[db] = mfma16(tr_pair(tO + 32 * s2 * TROW + tr_off[db]), pP[s2], dVa[db]);
-          dKa[db] = mfma16(tr_pair(tQ + 32 * s2 * TROW + tr_off[db]), pS[s2], dKa[db]);
-        }
-      }
-      __syncthreads();  // dS^T complete
-      // dQ rows 16 wr .. 16 wr + 15, head-dim half wd, += dS K over the 128 keys
-      const int ud = q0 + 16 * wr + g.diag - kv0;  // t of (row 16 wr, key 0)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int uk = ud - 32 * ks;  // rows +0..15, keys +0..31: t in [uk - 31, uk + 15]
-        if (uk + 15 < 0 || uk - 31 > W) continue;
-        const V8 as = tr_pair(dst + 32 * ks * TROW + tr_off_q);
-        dQa[k][0] = mfma16(as, tr_pair(sK + 32 * ks * TROW + tr_off_k0), dQa[k][0]);
-        dQa[k][1] = mfma16(as, tr_pair(sK + 32 * ks * TROW + tr_off_k1), dQa[k][1]);
+      for (int k = 0; k < NACT; ++k) {
+        if (k >= nit) break;
+        const int bb = 4 * (qlo + k) + wr;
+        if (!((bb >= lo_a && bb <= hi_a) || (bb >= lo_b && bb <= hi_b))) continue;
+        const int pa = clampi(bb - lo_a + 1, 0, BPOS - 1), pb = clampi(bb - lo_b + 1, 0, BPOS - 1);
+        const V8 st = tr_two(sBand[wa] + band_rd + 16 * pa, sBand[wb] + band_rd + 16 * pb);
+        dQa[k][0] = mfma16(kt0, st, dQa[k][0]);
+        dQa[k][1] = mfma16(kt1, st, dQa[k][1]);
       }
     }
 
@@ -410,28 +436,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       T* dvr = static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, h, keyl);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        T kx[4], vx[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          kx[r] = Elem<T>::from_float(p.scale * dKa[db][r]);
-          vx[r] = Elem<T>::from_float(dVa[db][r]);
-        }
-        *reinterpret_cast<u32x2*>(dkr + 16 * db + 4 * gq) = __builtin_bit_cast(u32x2, kx);
-        *reinterpret_cast<u32x2*>(dvr + 16 * db + 4 * gq) = __builtin_bit_cast(u32x2, vx);
+        *reinterpret_cast<u32x2*>(dkr + 16 * db + 4 * gq) =
+            pack4<T>(p.scale * dKa[db][0], p.scale * dKa[db][1], p.scale * dKa[db][2], p.scale * dKa[db][3]);
+        *reinterpret_cast<u32x2*>(dvr + 16 * db + 4 * gq) = pack4<T>(dVa[db][0], dVa[db][1], dVa[db][2], dVa[db][3]);
       }
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) dVa[db] = dKa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    __syncthreads();  // ring slots of retired tiles and sK are free
-    if (has_next) {
-      if (pf_n > 0) store_q_tile(pf_lo, pf[0]);
-      if (pf_n > 1) store_q_tile(pf_lo + 1, pf[1]);
-      if (pf_n > 0) loaded_hi = max(loaded_hi, pf_lo + pf_n);
-      store_k_rows();
-      vB[0] = vBn[0];
-      vB[1] = vBn[1];
-    }
+    if (has_next) take_kv(j + 1, kBn, vBn);
   }
 
   // ---- relay: boundary q-tiles this chunk joined after another chunk -------
@@ -452,21 +464,21 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         }
       }
       __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qi = i * kTile + 16 * wr + 4 * gq + r;
-        if (qi >= s.cap_q) continue;
+      const int qi = q_row(i);
+      if (qi < s.cap_q) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float* ap = acc_ptr(i, r, e);
-          const float mine = a.dq_stash[ap - a.dq_acc];
-          if (turn < nv - 1) {
-            __hip_atomic_fetch_add(ap, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            const float old = __hip_atomic_fetch_add(ap, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            dqp[elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * (2 * wd + e) + c] =
-                Elem<T>::from_float(p.scale * (old + mine));
+          float* ap = acc_ptr(i, e);
+          const f32x4 mine = *reinterpret_cast<const f32x4*>(a.dq_stash + (ap - a.dq_acc));
+          float out[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float old = __hip_atomic_fetch_add(ap + r, mine[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            out[r] = p.scale * (old + mine[r]);
           }
+          if (turn == nv - 1)
+            *reinterpret_cast<u32x2*>(dqp + elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * (2 * wd + e) + 4 * gq) =
+                pack4<T>(out[0], out[1], out[2], out[3]);
         }
       }
       __builtin_amdgcn_s_waitcnt(0);
