@@ -137,7 +137,12 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   // The streaming kernel covers multi-head attention with a causal mask and
   // a left window of at most 128 keys at head_dim 64 (its ring of q-tile
   // slots is sized for that); everything else runs the per-tile kernel.
-  p.stream = p.G == 1 && d->causal && d->window_left >= 0 && d->window_left <= 128 && d->head_dim == 64;
+  // It addresses rows with 32-bit row strides.
+  bool small_rows = true;
+  for (const int64_t rs : {p.sq[2], p.sk[2], p.sv[2], p.sdo[2], p.sdq[2], p.sdk[2], p.sdv[2]})
+    small_rows &= rs > 0 && rs <= INT32_MAX;
+  p.stream = p.G == 1 && d->causal && d->window_left >= 0 && d->window_left <= 128 && d->head_dim == 64 &&
+             small_rows;
   p.step_kv = p.stream ? 128 : kTile;
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one

@@ -143,11 +143,31 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   const int j1 = min(j0 + p.chunk, n_cap_steps);
   const int W = p.window;
 
-  const T* qp = static_cast<const T*>(a.q);
-  const T* kp = static_cast<const T*>(a.k);
-  const T* vp = static_cast<const T*>(a.v);
-  const T* dop = static_cast<const T*>(a.dO);
-  T* dqp = static_cast<T*>(a.dq);
+  // The schedule of SeqSched at this kernel's fixed tiles (q-tiles of 64
+  // rows, kv-steps of 128 keys, causal): floor / ceil division by a power
+  // of two is an arithmetic shift.
+  const int diag = g.diag, nqt = g.n_q_tiles, nkt = g.n_kv_tiles;
+  auto q_lo = [&](int j) { return max((j * STEP - diag) >> 6, 0); };
+  auto q_hi = [&](int j) { return min(-((diag - j * STEP - STEP - W) >> 6), nqt); };
+  auto n_iters = [&](int j) { return j < nkt ? max(q_hi(j) - q_lo(j), 0) : 0; };
+  auto kv_first = [&](int i) { return max((i * kTile + diag - W) >> 7, 0); };
+  auto kv_last = [&](int i) { return min(-((-(i + 1) * kTile - diag) >> 7) - 1, nkt - 1); };
+
+  // (b, h) bases; row r of a tensor is at base + r * row stride
+  const T* qb = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, 0);
+  const T* kb = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, h, 0);
+  const T* vb = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, h, 0);
+  const T* dob = static_cast<const T*>(a.dO) + elem_off(p, p.sdo, b, s.row0_q, h, 0);
+  T* dqb = static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, h, 0);
+  T* dkb = static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, h, 0);
+  T* dvb = static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, h, 0);
+  const int rs_q = (int)p.sq[2], rs_k = (int)p.sk[2], rs_v = (int)p.sv[2], rs_do = (int)p.sdo[2];
+  const int rs_dq = (int)p.sdq[2], rs_dk = (int)p.sdk[2], rs_dv = (int)p.sdv[2];
+  const float* lseb = a.lse + s.stat0 + h * s.stat_hs;
+  const float* deltab = a.delta + s.stat0 + h * s.stat_hs;
+  float* accb = a.dq_acc + (s.stat0 + h * s.stat_hs) * SD;
+  float* stashb = a.dq_stash + (s.stat0 + h * s.stat_hs) * SD;
+  int* semb = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles;
   V8 zero8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) zero8[e] = Elem<T>::from_float(0.f);
@@ -177,12 +197,12 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   V8 kB[2], vB[2], kBn[2], vBn[2];
   auto load_kv = [&](int j, V8 (&kx)[2], V8 (&vx)[2]) {
     const int key = clampi(j * STEP + 16 * w + c, 0, max(s.cap_kv - 1, 0));
-    const int64_t ko = elem_off(p, p.sk, b, s.row0_kv, h, key);
-    const int64_t vo = elem_off(p, p.sv, b, s.row0_kv, h, key);
+    const T* kr = kb + (int64_t)key * rs_k + 8 * gq;
+    const T* vr = vb + (int64_t)key * rs_v + 8 * gq;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      kx[ks] = gld8(kp + ko + 32 * ks + 8 * gq);
-      vx[ks] = gld8(vp + vo + 32 * ks + 8 * gq);
+      kx[ks] = gld8(kr + 32 * ks);
+      vx[ks] = gld8(vr + 32 * ks);
     }
   };
   auto take_kv = [&](int j, const V8 (&kx)[2], const V8 (&vx)[2]) {
@@ -202,12 +222,12 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   auto load_q_tile = [&](int i, QRegs& r) {
     r.tile = i;
     const int row = tid >> 3, ch = tid & 7, qi = min(i * kTile + row, s.len_q - 1);
-    r.q = gld8(qp + elem_off(p, p.sq, b, s.row0_q, h, qi) + 8 * ch);
-    r.o = gld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, qi) + 8 * ch);
+    r.q = gld8(qb + (int64_t)qi * rs_q + 8 * ch);
+    r.o = gld8(dob + (int64_t)qi * rs_do + 8 * ch);
     if (tid < kTile) {
-      const int64_t si = s.stat0 + h * s.stat_hs + min(i * kTile + tid, s.len_q - 1);
-      r.lse = a.lse[si];
-      r.delta = a.delta[si];
+      const int si = min(i * kTile + tid, s.len_q - 1);
+      r.lse = lseb[si];
+      r.delta = deltab[si];
     }
   };
   auto store_q_tile = [&](const QRegs& r) {
@@ -235,15 +255,17 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 
   // ---- dQ of a retiring q-tile ------------------------------------------------
   auto q_row = [&](int i) { return i * kTile + 16 * wr + c; };
-  auto acc_ptr = [&](int i, int e) -> float* {  // 4 consecutive head-dim values
-    return a.dq_acc + (s.stat0 + h * s.stat_hs + q_row(i)) * SD + 16 * (2 * wd + e) + 4 * gq;
+  auto acc_off = [&](int i, int e) {  // 4 consecutive head-dim values
+    return (int64_t)q_row(i) * SD + 16 * (2 * wd + e) + 4 * gq;
   };
+  // a q-tile is visited by the kv-steps [kv_first, kv_last]; this chunk runs
+  // the steps [j0, j1)
   auto retire = [&](int i, f32x4 (&acc)[2]) {  // block-uniform arguments
-    const int first = g.kv_first(i) / p.chunk, last = g.kv_last(i) / p.chunk;
+    const bool earlier = kv_first(i) < j0, later = kv_last(i) >= j1;
     const int qi = q_row(i);
-    if (first == last) {
+    if (!earlier && !later) {
       if (qi < s.cap_q) {
-        T* row = dqp + elem_off(p, p.sdq, b, s.row0_q, h, qi) + 32 * wd + 4 * gq;
+        T* row = dqb + (int64_t)qi * rs_dq + 32 * wd + 4 * gq;
 #pragma unroll
         for (int e = 0; e < 2; ++e)
           *reinterpret_cast<u32x2*>(row + 16 * e) =
@@ -254,26 +276,24 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(acc_ptr(i, e) + r, acc[e][r]);
-    } else if (first == chunk) {
+          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(accb + acc_off(i, e) + r, acc[e][r]);
+    } else if (!earlier) {
       // first visiting chunk of a boundary tile: turn 0, no wait
-      int* semp = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
       if (qi < s.cap_q)
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            __hip_atomic_exchange(acc_ptr(i, e) + r, acc[e][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_exchange(accb + acc_off(i, e) + r, acc[e][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(semp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(semb + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       // a later turn: stash the partial; it is added in turn order once this
       // chunk has finished its own kv-steps
       if (qi < s.cap_q)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-          *reinterpret_cast<f32x4*>(a.dq_stash + (acc_ptr(i, e) - a.dq_acc)) = acc[e];
+        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4*>(stashb + acc_off(i, e)) = acc[e];
     }
     acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
@@ -282,22 +302,22 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   // 16-row blocks that keys kv0 + 16 v .. + 15 see: rows t = row + diag - key
   // in [0, W]; clipped to the step's q-tiles; empty past the keys.
   auto band_lo = [&](int kv0, int v, int qlo) {
-    return max(floor_div(kv0 + 16 * v - g.diag, 16), 4 * qlo);
+    return max((kv0 + 16 * v - diag) >> 4, 4 * qlo);
   };
   auto band_hi = [&](int kv0, int v, int qhi) {
     if (kv0 + 16 * v >= s.len_kv) return INT32_MIN / 2;
-    return min(floor_div(kv0 + 16 * v + 15 + W - g.diag, 16), 4 * qhi - 1);
+    return min((kv0 + 16 * v + 15 + W - diag) >> 4, 4 * qhi - 1);
   };
 
   // ---- prologue -------------------------------------------------------------
   load_kv(j0, kBn, vBn);
   take_kv(j0, kBn, vBn);
-  int loaded_hi = g.q_lo(j0);  // the ring holds q-tiles [.., loaded_hi)
-  int acc_lo = g.q_lo(j0);     // q-tile held in dQa[0]
+  int loaded_hi = q_lo(j0);  // the ring holds q-tiles [.., loaded_hi)
+  int acc_lo = q_lo(j0);     // q-tile held in dQa[0]
   QRegs pf[2];
 
   for (int j = j0; j < j1; ++j) {
-    const int qlo = g.q_lo(j), nit = min(g.n_iters(j), NACT), qhi = qlo + nit;
+    const int qlo = q_lo(j), nit = min(n_iters(j), NACT), qhi = qlo + nit;
     if (loaded_hi < qlo) loaded_hi = qlo;
     for (; loaded_hi < qhi; ++loaded_hi) {  // chunk start and gaps only
       QRegs t;
@@ -307,13 +327,21 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     __syncthreads();  // T: ring ready; sK and the bands are free
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<V8*>(&sK[tile_off(16 * w + c, 4 * ks + gq)]) = kB[ks];
-    for (; acc_lo < qlo; ++acc_lo) {  // realign dQa[0] with q_lo(j)
+    // realign dQa[0] with q_lo(j); q_lo advances by two q-tiles per step
+    // except where it is clamped at the sequence start
+    while (acc_lo < qlo) {
+      const int sh = min(qlo - acc_lo, 2);
 #pragma unroll
-      for (int k = 0; k + 1 < NACT; ++k) {
-        dQa[k][0] = dQa[k + 1][0];
-        dQa[k][1] = dQa[k + 1][1];
+      for (int k = 0; k < NACT; ++k) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 a0 = k + 2 < NACT ? dQa[min(k + 2, NACT - 1)][0] : z;
+        const f32x4 a1 = k + 2 < NACT ? dQa[min(k + 2, NACT - 1)][1] : z;
+        const f32x4 b0 = k + 1 < NACT ? dQa[min(k + 1, NACT - 1)][0] : z;
+        const f32x4 b1 = k + 1 < NACT ? dQa[min(k + 1, NACT - 1)][1] : z;
+        dQa[k][0] = sh == 2 ? a0 : b0;
+        dQa[k][1] = sh == 2 ? a1 : b1;
       }
-      dQa[NACT - 1][0] = dQa[NACT - 1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_lo += sh;
     }
 
     // prefetch of the next kv-step: K / V rows and its new q-tiles
@@ -321,7 +349,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     int pf_n = 0;
     if (has_next) {
       load_kv(j + 1, kBn, vBn);
-      const int nlo = g.q_lo(j + 1), nhi = nlo + min(g.n_iters(j + 1), NACT);
+      const int nlo = q_lo(j + 1), nhi = nlo + min(n_iters(j + 1), NACT);
       const int pf_lo = max(loaded_hi, nlo);
       pf_n = max(0, min(2, nhi - pf_lo));
       if (pf_n > 0) load_q_tile(pf_lo, pf[0]);
@@ -333,52 +361,71 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     // t(row, key) = row + diag - key; visible iff 0 <= t <= W.  A key past
     // the sequence is pushed out of every window through its lane base.
     const int keyl = kv0 + 16 * w + c;
-    const int tkey = keyl < s.len_kv ? g.diag - keyl : -(1 << 29);
+    const int tkey = keyl < s.len_kv ? diag - keyl : -(1 << 29);
     const int blo = band_lo(kv0, w, qlo), bhi = band_hi(kv0, w, qhi);
     const int npairs = min(max(bhi - blo + 2, 0) >> 1, NPAIR);
-    for (int pr = 0; pr < npairs; ++pr) {
-      const int b0 = blo + 2 * pr;
-      const bool has1 = b0 + 1 <= bhi;
-      const int b1 = has1 ? b0 + 1 : b0;  // a valid block either way
+    // Pair pr holds blocks b0 = blo + 2 pr and b1 = b0 + 1; a b1 past the
+    // band reads block b0 again and is masked out entirely.
+    struct PairSD {
+      f32x4 S0, D0, S1, D1;
+    };
+    auto pair_rows = [&](int pr, int& b0, int& b1, bool& has1) {
+      b0 = blo + 2 * pr;
+      has1 = b0 + 1 <= bhi;
+      b1 = has1 ? b0 + 1 : b0;
+    };
+    // S = Q K^T and dP = dO V^T of both blocks
+    auto stage_sdp = [&](int pr) {
+      int b0, b1;
+      bool has1;
+      pair_rows(pr, b0, b1, has1);
+      const T* q0 = sQ[(b0 >> 2) % NSLOT] + 16 * (b0 & 3) * TROW;
+      const T* o0 = sdO[(b0 >> 2) % NSLOT] + 16 * (b0 & 3) * TROW;
+      const T* q1 = sQ[(b1 >> 2) % NSLOT] + 16 * (b1 & 3) * TROW;
+      const T* o1 = sdO[(b1 >> 2) % NSLOT] + 16 * (b1 & 3) * TROW;
+      PairSD r;
+      r.S0 = r.D0 = r.S1 = r.D1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        r.S0 = mfma16(*reinterpret_cast<const V8*>(q0 + rd_off[ks]), kB[ks], r.S0);
+        r.D0 = mfma16(*reinterpret_cast<const V8*>(o0 + rd_off[ks]), vB[ks], r.D0);
+        r.S1 = mfma16(*reinterpret_cast<const V8*>(q1 + rd_off[ks]), kB[ks], r.S1);
+        r.D1 = mfma16(*reinterpret_cast<const V8*>(o1 + rd_off[ks]), vB[ks], r.D1);
+      }
+      return r;
+    };
+    // P, dS, the band write and dV^T += dO^T P, dK^T += Q^T dS
+    auto stage_grad = [&](int pr, const PairSD& r) {
+      int b0, b1;
+      bool has1;
+      pair_rows(pr, b0, b1, has1);
       const int sl0 = (b0 >> 2) % NSLOT, sl1 = (b1 >> 2) % NSLOT;
       const T* q0 = sQ[sl0] + 16 * (b0 & 3) * TROW;
       const T* o0 = sdO[sl0] + 16 * (b0 & 3) * TROW;
       const T* q1 = sQ[sl1] + 16 * (b1 & 3) * TROW;
       const T* o1 = sdO[sl1] + 16 * (b1 & 3) * TROW;
-      f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, D0 = S0, S1 = S0, D1 = S0;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        S0 = mfma16(*reinterpret_cast<const V8*>(q0 + rd_off[ks]), kB[ks], S0);
-        D0 = mfma16(*reinterpret_cast<const V8*>(o0 + rd_off[ks]), vB[ks], D0);
-      }
-      if (has1) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          S1 = mfma16(*reinterpret_cast<const V8*>(q1 + rd_off[ks]), kB[ks], S1);
-          D1 = mfma16(*reinterpret_cast<const V8*>(o1 + rd_off[ks]), vB[ks], D1);
-        }
-      }
+      const int r0 = 16 * (b0 & 3) + 4 * gq, r1 = 16 * (b1 & 3) + 4 * gq;
+      const float4 lse0 = *reinterpret_cast<const float4*>(&sLse[sl0][r0]);
+      const float4 del0 = *reinterpret_cast<const float4*>(&sDelta[sl0][r0]);
+      const float4 lse1 = *reinterpret_cast<const float4*>(&sLse[sl1][r1]);
+      const float4 del1 = *reinterpret_cast<const float4*>(&sDelta[sl1][r1]);
+      const float lsev[8] = {lse0.x, lse0.y, lse0.z, lse0.w, lse1.x, lse1.y, lse1.z, lse1.w};
+      const float delv[8] = {del0.x, del0.y, del0.z, del0.w, del1.x, del1.y, del1.z, del1.w};
+      const float sv[8] = {r.S0[0], r.S0[1], r.S0[2], r.S0[3], r.S1[0], r.S1[1], r.S1[2], r.S1[3]};
+      const float dv[8] = {r.D0[0], r.D0[1], r.D0[2], r.D0[3], r.D1[0], r.D1[1], r.D1[2], r.D1[3]};
+      const int tb0 = 16 * b0 + 4 * gq + tkey;
+      const int tb1 = has1 ? 16 * b1 + 4 * gq + tkey : -(1 << 29);
       float pv[8], dsv[8];
-      {
-        const int r0 = 16 * (b0 & 3) + 4 * gq, r1 = 16 * (b1 & 3) + 4 * gq;
-        const float4 lse0 = *reinterpret_cast<const float4*>(&sLse[sl0][r0]);
-        const float4 del0 = *reinterpret_cast<const float4*>(&sDelta[sl0][r0]);
-        const float4 lse1 = *reinterpret_cast<const float4*>(&sLse[sl1][r1]);
-        const float4 del1 = *reinterpret_cast<const float4*>(&sDelta[sl1][r1]);
-        const float lsev[8] = {lse0.x, lse0.y, lse0.z, lse0.w, lse1.x, lse1.y, lse1.z, lse1.w};
-        const float delv[8] = {del0.x, del0.y, del0.z, del0.w, del1.x, del1.y, del1.z, del1.w};
-        const float sv[8] = {S0[0], S0[1], S0[2], S0[3], S1[0], S1[1], S1[2], S1[3]};
-        const float dv[8] = {D0[0], D0[1], D0[2], D0[3], D1[0], D1[1], D1[2], D1[3]};
-        const int tb0 = 16 * b0 + 4 * gq + tkey;
-        // block 1 is masked out entirely when it is past the band
-        const int tb1 = has1 ? 16 * b1 + 4 * gq + tkey : -(1 << 29);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int t = (r < 4 ? tb0 : tb1) + (r & 3);
-          const float x = sv[r] * p.scale_log2 - lsev[r];
-          pv[r] = (unsigned)t <= (unsigned)W ? fast_exp2(x) : 0.f;
-          dsv[r] = pv[r] * (dv[r] - delv[r]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int t = (e < 4 ? tb0 : tb1) + (e & 3);
+        // masked elements take exp2(-inf) = 0.  The empty asm makes x opaque
+        // so that the compiler keeps a select instead of branching around
+        // the LSE read and the multiply-add.
+        float x = sv[e] * p.scale_log2 - lsev[e];
+        asm("" : "+v"(x));
+        pv[e] = fast_exp2((unsigned)t <= (unsigned)W ? x : -INFINITY);
+        dsv[e] = pv[e] * (dv[e] - delv[e]);
       }
       const u32x2 p0 = pack4<T>(pv[0], pv[1], pv[2], pv[3]), p1 = pack4<T>(pv[4], pv[5], pv[6], pv[7]);
       const u32x2 s0 = pack4<T>(dsv[0], dsv[1], dsv[2], dsv[3]);
@@ -393,6 +440,20 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         dVa[db] = mfma16(tr_two(o0 + tr_off[db], o1 + tr_off[db]), pP, dVa[db]);
         dKa[db] = mfma16(tr_two(q0 + tr_off[db], q1 + tr_off[db]), pS, dKa[db]);
       }
+    };
+    // Software pipeline: the products of pair pr + 1 are issued in the same
+    // straight-line block as the softmax and gradients of pair pr.
+    PairSD sdp[2];
+    if (npairs > 0) sdp[0] = stage_sdp(0);
+#pragma unroll
+    for (int pr = 0; pr < NPAIR; ++pr) {
+      if (pr >= npairs) break;
+      if (pr + 1 < npairs) {
+        sdp[(pr + 1) & 1] = stage_sdp(pr + 1);
+        stage_grad(pr, sdp[pr & 1]);
+      } else {
+        stage_grad(pr, sdp[pr & 1]);
+      }
     }
     for (int pr = npairs; pr < NPAIR; ++pr) {  // positions past the band
       *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 1)) = u32x2{0u, 0u};
@@ -400,40 +461,23 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     }
 
     __syncthreads();  // A: bands and sK complete; ring slots of tiles before q_lo(j + 1) free
+    // Everything prefetched is taken into use here, before this step issues
+    // any global store: vector-memory operations complete in order, so a
+    // wait placed after the stores would also wait for their write-back.
+    // The loads were issued before phase 1 and the last stores before that,
+    // so this wait is normally free; it also tells the compiler that no load
+    // is outstanding past this point.
+    __builtin_amdgcn_s_waitcnt(0);
     if (pf_n > 0) store_q_tile(pf[0]);
     if (pf_n > 1) store_q_tile(pf[1]);
     loaded_hi += pf_n;
+    if (has_next) take_kv(j + 1, kBn, vBn);  // kB / vB of step j are no longer read
 
-    // ---- phase 2: dQ^T += K^T dS^T ------------------------------------------
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int wa = 2 * ks, wb = 2 * ks + 1;
-      const int lo_a = band_lo(kv0, wa, qlo), hi_a = band_hi(kv0, wa, qhi);
-      const int lo_b = band_lo(kv0, wb, qlo), hi_b = band_hi(kv0, wb, qhi);
-      if (hi_a < lo_a && hi_b < lo_b) continue;
-      const T* kr = sK + 32 * ks * TROW;
-      const V8 kt0 = tr_two(kr + tr_off_k0, kr + 16 * TROW + tr_off_k0);
-      const V8 kt1 = tr_two(kr + tr_off_k1, kr + 16 * TROW + tr_off_k1);
-#pragma unroll
-      for (int k = 0; k < NACT; ++k) {
-        if (k >= nit) break;
-        const int bb = 4 * (qlo + k) + wr;
-        if (!((bb >= lo_a && bb <= hi_a) || (bb >= lo_b && bb <= hi_b))) continue;
-        const int pa = clampi(bb - lo_a + 1, 0, BPOS - 1), pb = clampi(bb - lo_b + 1, 0, BPOS - 1);
-        const V8 st = tr_two(sBand[wa] + band_rd + 16 * pa, sBand[wb] + band_rd + 16 * pb);
-        dQa[k][0] = mfma16(kt0, st, dQa[k][0]);
-        dQa[k][1] = mfma16(kt1, st, dQa[k][1]);
-      }
-    }
-
-    // q-tiles whose last visitor in this chunk was this step
-#pragma unroll
-    for (int k = 0; k < NACT; ++k)
-      if (k < nit && min(g.kv_last(qlo + k), j1 - 1) == j) retire(qlo + k, dQa[k]);
-    // dK / dV of this step (zeros if it visited nothing)
+    // dK / dV of this step (zeros if it visited nothing): this wave's keys are
+    // complete after its phase 1
     if (keyl < s.cap_kv) {
-      T* dkr = static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, h, keyl);
-      T* dvr = static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, h, keyl);
+      T* dkr = dkb + (int64_t)keyl * rs_dk;
+      T* dvr = dvb + (int64_t)keyl * rs_dv;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         *reinterpret_cast<u32x2*>(dkr + 16 * db + 4 * gq) =
@@ -443,16 +487,60 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) dVa[db] = dKa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (has_next) take_kv(j + 1, kBn, vBn);
+
+    // ---- phase 2: dQ^T += K^T dS^T ------------------------------------------
+    // Wave v's band starts at block max(L + v, 4 q_lo) and ends at
+    // min(H + v, 4 q_hi - 1); waves from vmax on hold no valid key.  Row
+    // block bb therefore meets the bands of waves [bb - H, bb - L], and its
+    // position in wave v's band is min(bb - L - v, bb - 4 q_lo) + 1, with
+    // positions outside [1, band length] holding zeros.
+    {
+      const int Lb = (kv0 - diag) >> 4, Hb = (kv0 + 15 + W - diag) >> 4;
+      const int vmax = min((s.len_kv - kv0 + 15) >> 4, NWAVE);
+      int k_lo[NACT], k_hi[NACT], Dk[NACT], Ek[NACT];  // per tile: key pairs, offsets
+#pragma unroll
+      for (int k = 0; k < NACT; ++k) {
+        const int bb = 4 * (qlo + k) + wr;
+        Dk[k] = bb - Lb;
+        Ek[k] = bb - 4 * qlo;
+        const int vlo = max(bb - Hb, 0), vhi = min(Dk[k], vmax - 1);
+        k_lo[k] = k < nit && vlo <= vhi ? vlo >> 1 : 4;
+        k_hi[k] = k < nit && vlo <= vhi ? vhi >> 1 : -1;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bool any = false;
+#pragma unroll
+        for (int k = 0; k < NACT; ++k) any |= k_lo[k] <= ks && ks <= k_hi[k];
+        if (!any) continue;
+        const T* kr = sK + 32 * ks * TROW;
+        const V8 kt0 = tr_two(kr + tr_off_k0, kr + 16 * TROW + tr_off_k0);
+        const V8 kt1 = tr_two(kr + tr_off_k1, kr + 16 * TROW + tr_off_k1);
+#pragma unroll
+        for (int k = 0; k < NACT; ++k) {
+          if (!(k_lo[k] <= ks && ks <= k_hi[k])) continue;
+          const int pa = clampi(min(Dk[k] - 2 * ks, Ek[k]) + 1, 0, BPOS - 1);
+          const int pb = clampi(min(Dk[k] - 2 * ks - 1, Ek[k]) + 1, 0, BPOS - 1);
+          const V8 st = tr_two(sBand[2 * ks] + band_rd + 16 * pa, sBand[2 * ks + 1] + band_rd + 16 * pb);
+          dQa[k][0] = mfma16(kt0, st, dQa[k][0]);
+          dQa[k][1] = mfma16(kt1, st, dQa[k][1]);
+        }
+      }
+    }
+
+    // q-tiles whose last visitor in this chunk was this step
+#pragma unroll
+    for (int k = 0; k < NACT; ++k)
+      if (k < nit && min(kv_last(qlo + k), j1 - 1) == j) retire(qlo + k, dQa[k]);
   }
 
   // ---- relay: boundary q-tiles this chunk joined after another chunk -------
-  if (RELAY && j0 < g.n_kv_tiles) {
-    for (int i = g.q_lo(j0); i < g.n_q_tiles && i < g.q_hi(j0); ++i) {
-      const int first = g.kv_first(i) / p.chunk;
+  if (RELAY && j0 < nkt) {
+    for (int i = q_lo(j0); i < nqt && i < q_hi(j0); ++i) {
+      const int first = kv_first(i) / p.chunk;
       if (first >= chunk) break;  // kv_first is nondecreasing in i
-      const int turn = chunk - first, nv = g.kv_last(i) / p.chunk - first + 1;
-      int* semp = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
+      const int turn = chunk - first, nv = kv_last(i) / p.chunk - first + 1;
+      int* semp = semb + i;
       if (tid == 0) {
         int spins = 0;
         while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != turn) {
@@ -468,8 +556,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       if (qi < s.cap_q) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float* ap = acc_ptr(i, e);
-          const f32x4 mine = *reinterpret_cast<const f32x4*>(a.dq_stash + (ap - a.dq_acc));
+          float* ap = accb + acc_off(i, e);
+          const f32x4 mine = *reinterpret_cast<const f32x4*>(stashb + acc_off(i, e));
           float out[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -477,7 +565,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
             out[r] = p.scale * (old + mine[r]);
           }
           if (turn == nv - 1)
-            *reinterpret_cast<u32x2*>(dqp + elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * (2 * wd + e) + 4 * gq) =
+            *reinterpret_cast<u32x2*>(dqb + (int64_t)qi * rs_dq + 16 * (2 * wd + e) + 4 * gq) =
                 pack4<T>(out[0], out[1], out[2], out[3]);
         }
       }
