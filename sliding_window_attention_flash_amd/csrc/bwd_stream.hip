@@ -104,9 +104,30 @@ __device__ __forceinline__ typename Elem<T>::vec8 tr_two(const T* p0, const T* p
 
 template <typename T>
 __device__ __forceinline__ u32x2 pack4(float x0, float x1, float x2, float x3) {
-  T v[4] = {Elem<T>::from_float(x0), Elem<T>::from_float(x1), Elem<T>::from_float(x2),
-            Elem<T>::from_float(x3)};
+  typedef T t2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const t2 a = __builtin_convertvector(f2{x0, x1}, t2), b = __builtin_convertvector(f2{x2, x3}, t2);
+  return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
+// LDS byte addresses.  Reads through an explicit 32-bit address let the
+// compiler fold constant displacements into the instruction's offset field.
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_byte*)p;
+}
+template <typename V>
+__device__ __forceinline__ V lds_ld(uint32_t a) {
+  return *(const __attribute__((address_space(3))) V*)(uintptr_t)a;
+}
+__device__ __forceinline__ u32x2 lds_tr4(uint32_t a) {
+  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(uintptr_t)a);
   return __builtin_bit_cast(u32x2, v);
+}
+// a value the compiler must keep in a register as computed (no re-derivation)
+__device__ __forceinline__ uint32_t pin(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
 }
 
 }  // namespace
@@ -114,10 +135,9 @@ __device__ __forceinline__ u32x2 pack4(float x0, float x1, float x2, float x3) {
 template <typename T, bool RELAY>
 __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
-  __shared__ __align__(16) T sQ[NSLOT][kTile * TROW];
-  __shared__ __align__(16) T sdO[NSLOT][kTile * TROW];
-  __shared__ __align__(16) float sLse[NSLOT][kTile];
-  __shared__ __align__(16) float sDelta[NSLOT][kTile];
+  // ring slot: Q tile, then the dO tile (QO_DO bytes further); LSE, then delta
+  __shared__ __align__(16) T sQO[NSLOT][2][kTile * TROW];
+  __shared__ __align__(16) float sLD[NSLOT][2][kTile];
   __shared__ __align__(16) T sK[STEP * TROW];
   __shared__ __align__(16) T sBand[NWAVE][16 * BP];  // dS^T [key][block position, row]
   __shared__ int sTicket;
@@ -179,9 +199,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   int rd_off[2];  // row read of a 16-row block: row c, chunk 4 ks + gq
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) rd_off[ks] = tile_off(c, 4 * ks + gq);
-  int tr_off[4];  // transposed read of a 16-row block, columns 16 db ..
+  // the same in bytes, for the explicit-address reads of the ring
+  uint32_t rd_off_b[2], tr_off_b[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) tr_off[db] = tr_lane_off(c, gq, db);
+  for (int ks = 0; ks < 2; ++ks) rd_off_b[ks] = rd_off[ks] * sizeof(T);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) tr_off_b[db] = tr_lane_off(c, gq, db) * sizeof(T);
+  const uint32_t ld_off_b = 4 * gq * sizeof(float);  // LSE / delta of rows 4 gq ..
+  const uint32_t ring_q = lds_addr(&sQO[0][0][0]), ring_ld = lds_addr(&sLD[0][0][0]);
   // K^T columns of this wave's dQ half (kept out of a runtime-indexed array,
   // which the compiler would place in scratch memory)
   const int tr_off_k0 = tr_lane_off(c, gq, 2 * wd), tr_off_k1 = tr_lane_off(c, gq, 2 * wd + 1);
@@ -233,13 +258,13 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   auto store_q_tile = [&](const QRegs& r) {
     const int sl = r.tile % NSLOT, row = tid >> 3, ch = tid & 7;
     const bool ok = r.tile * kTile + row < s.len_q;
-    *reinterpret_cast<V8*>(&sQ[sl][tile_off(row, ch)]) = ok ? r.q : zero8;
-    *reinterpret_cast<V8*>(&sdO[sl][tile_off(row, ch)]) = ok ? r.o : zero8;
+    *reinterpret_cast<V8*>(&sQO[sl][0][tile_off(row, ch)]) = ok ? r.q : zero8;
+    *reinterpret_cast<V8*>(&sQO[sl][1][tile_off(row, ch)]) = ok ? r.o : zero8;
     if (tid < kTile) {
       const bool okr = r.tile * kTile + tid < s.len_q;
       // exp2(x - inf) = 0: padding rows carry no weight
-      sLse[sl][tid] = okr ? r.lse * kLog2e : INFINITY;
-      sDelta[sl][tid] = okr ? r.delta : 0.f;
+      sLD[sl][0][tid] = okr ? r.lse * kLog2e : INFINITY;
+      sLD[sl][1][tid] = okr ? r.delta : 0.f;
     }
   };
 
@@ -374,23 +399,27 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       has1 = b0 + 1 <= bhi;
       b1 = has1 ? b0 + 1 : b0;
     };
+    // LDS byte address of 16-row block b of its q-tile's ring slot (Q; the
+    // dO rows are QO_DO bytes further), and of its LSE values (delta: LD_DL
+    // bytes further)
+    constexpr uint32_t QO_DO = kTile * TROW * sizeof(T), LD_DL = kTile * sizeof(float);
+    auto blk_addr = [&](int b) { return ring_q + (uint32_t)((b >> 2) % NSLOT) * (2 * QO_DO) + (b & 3) * (16 * TROW * sizeof(T)); };
+    auto ld_addr = [&](int b) { return ring_ld + (uint32_t)((b >> 2) % NSLOT) * (2 * LD_DL) + (b & 3) * (16 * sizeof(float)); };
     // S = Q K^T and dP = dO V^T of both blocks
     auto stage_sdp = [&](int pr) {
       int b0, b1;
       bool has1;
       pair_rows(pr, b0, b1, has1);
-      const T* q0 = sQ[(b0 >> 2) % NSLOT] + 16 * (b0 & 3) * TROW;
-      const T* o0 = sdO[(b0 >> 2) % NSLOT] + 16 * (b0 & 3) * TROW;
-      const T* q1 = sQ[(b1 >> 2) % NSLOT] + 16 * (b1 & 3) * TROW;
-      const T* o1 = sdO[(b1 >> 2) % NSLOT] + 16 * (b1 & 3) * TROW;
+      const uint32_t a0 = blk_addr(b0), a1 = blk_addr(b1);
       PairSD r;
       r.S0 = r.D0 = r.S1 = r.D1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        r.S0 = mfma16(*reinterpret_cast<const V8*>(q0 + rd_off[ks]), kB[ks], r.S0);
-        r.D0 = mfma16(*reinterpret_cast<const V8*>(o0 + rd_off[ks]), vB[ks], r.D0);
-        r.S1 = mfma16(*reinterpret_cast<const V8*>(q1 + rd_off[ks]), kB[ks], r.S1);
-        r.D1 = mfma16(*reinterpret_cast<const V8*>(o1 + rd_off[ks]), vB[ks], r.D1);
+        const uint32_t x0 = pin(a0 + rd_off_b[ks]), x1 = pin(a1 + rd_off_b[ks]);
+        r.S0 = mfma16(lds_ld<V8>(x0), kB[ks], r.S0);
+        r.D0 = mfma16(lds_ld<V8>(x0 + QO_DO), vB[ks], r.D0);
+        r.S1 = mfma16(lds_ld<V8>(x1), kB[ks], r.S1);
+        r.D1 = mfma16(lds_ld<V8>(x1 + QO_DO), vB[ks], r.D1);
       }
       return r;
     };
@@ -399,16 +428,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       int b0, b1;
       bool has1;
       pair_rows(pr, b0, b1, has1);
-      const int sl0 = (b0 >> 2) % NSLOT, sl1 = (b1 >> 2) % NSLOT;
-      const T* q0 = sQ[sl0] + 16 * (b0 & 3) * TROW;
-      const T* o0 = sdO[sl0] + 16 * (b0 & 3) * TROW;
-      const T* q1 = sQ[sl1] + 16 * (b1 & 3) * TROW;
-      const T* o1 = sdO[sl1] + 16 * (b1 & 3) * TROW;
-      const int r0 = 16 * (b0 & 3) + 4 * gq, r1 = 16 * (b1 & 3) + 4 * gq;
-      const float4 lse0 = *reinterpret_cast<const float4*>(&sLse[sl0][r0]);
-      const float4 del0 = *reinterpret_cast<const float4*>(&sDelta[sl0][r0]);
-      const float4 lse1 = *reinterpret_cast<const float4*>(&sLse[sl1][r1]);
-      const float4 del1 = *reinterpret_cast<const float4*>(&sDelta[sl1][r1]);
+      const uint32_t a0 = blk_addr(b0), a1 = blk_addr(b1);
+      const uint32_t l0 = pin(ld_addr(b0) + ld_off_b), l1 = pin(ld_addr(b1) + ld_off_b);
+      const float4 lse0 = lds_ld<float4>(l0), del0 = lds_ld<float4>(l0 + LD_DL);
+      const float4 lse1 = lds_ld<float4>(l1), del1 = lds_ld<float4>(l1 + LD_DL);
       const float lsev[8] = {lse0.x, lse0.y, lse0.z, lse0.w, lse1.x, lse1.y, lse1.z, lse1.w};
       const float delv[8] = {del0.x, del0.y, del0.z, del0.w, del1.x, del1.y, del1.z, del1.w};
       const float sv[8] = {r.S0[0], r.S0[1], r.S0[2], r.S0[3], r.S1[0], r.S1[1], r.S1[2], r.S1[3]};
@@ -437,8 +460,11 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 2)) = s1;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dVa[db] = mfma16(tr_two(o0 + tr_off[db], o1 + tr_off[db]), pP, dVa[db]);
-        dKa[db] = mfma16(tr_two(q0 + tr_off[db], q1 + tr_off[db]), pS, dKa[db]);
+        const uint32_t y0 = pin(a0 + tr_off_b[db]), y1 = pin(a1 + tr_off_b[db]);
+        const u32x2 o_lo = lds_tr4(y0 + QO_DO), o_hi = lds_tr4(y1 + QO_DO);
+        const u32x2 q_lo = lds_tr4(y0), q_hi = lds_tr4(y1);
+        dVa[db] = mfma16(__builtin_bit_cast(V8, u32x4{o_lo[0], o_lo[1], o_hi[0], o_hi[1]}), pP, dVa[db]);
+        dKa[db] = mfma16(__builtin_bit_cast(V8, u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}), pS, dKa[db]);
       }
     };
     // Software pipeline: the products of pair pr + 1 are issued in the same
