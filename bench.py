@@ -270,7 +270,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c3", choices=sorted(workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 4k / 8k / atomic side timings")
@@ -315,7 +315,7 @@ def main():
         for name in ("c3_atomic", "c2_4k", "c2_8k"):
             if name == args.workload:
                 continue
-            m2, mm2, _ = time_backward(wl[name], max(5, args.steps // 2), 3)
+            m2, mm2, _ = time_backward(wl[name], max(5, args.steps // 2), args.warmup)
             extra[name] = {"ms": m2, "tflops": flops(wl[name]) / (m2 * 1e-3) / 1e12, "main_ms": mm2}
     line = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

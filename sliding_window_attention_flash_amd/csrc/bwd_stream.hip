@@ -369,17 +369,23 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       acc_lo += sh;
     }
 
-    // prefetch of the next kv-step: K / V rows and its new q-tiles
+    // Prefetch of the next kv-step -- its K / V rows and new q-tiles -- is
+    // issued over the first pairs of phase 1, and this step's dK / dV are
+    // stored over phase 2: every CU runs the same step pattern, so memory
+    // traffic issued in bursts at fixed points of the step would reach the
+    // memory system from all of them at once.
     const bool has_next = j + 1 < j1;
-    int pf_n = 0;
+    int pf_n = 0, pf_lo = 0;
     if (has_next) {
-      load_kv(j + 1, kBn, vBn);
       const int nlo = q_lo(j + 1), nhi = nlo + min(n_iters(j + 1), NACT);
-      const int pf_lo = max(loaded_hi, nlo);
+      pf_lo = max(loaded_hi, nlo);
       pf_n = max(0, min(2, nhi - pf_lo));
-      if (pf_n > 0) load_q_tile(pf_lo, pf[0]);
-      if (pf_n > 1) load_q_tile(pf_lo + 1, pf[1]);
     }
+    auto issue_pf = [&](int m) {
+      if (m == 0 && has_next) load_kv(j + 1, kBn, vBn);
+      if (m == 1 && pf_n > 0) load_q_tile(pf_lo, pf[0]);
+      if (m == 2 && pf_n > 1) load_q_tile(pf_lo + 1, pf[1]);
+    };
 
     // ---- phase 1: this wave's band --------------------------------------------
     const int kv0 = j * STEP;
@@ -430,10 +436,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       pair_rows(pr, b0, b1, has1);
       const uint32_t a0 = blk_addr(b0), a1 = blk_addr(b1);
       const uint32_t l0 = pin(ld_addr(b0) + ld_off_b), l1 = pin(ld_addr(b1) + ld_off_b);
-      const float4 lse0 = lds_ld<float4>(l0), del0 = lds_ld<float4>(l0 + LD_DL);
-      const float4 lse1 = lds_ld<float4>(l1), del1 = lds_ld<float4>(l1 + LD_DL);
-      const float lsev[8] = {lse0.x, lse0.y, lse0.z, lse0.w, lse1.x, lse1.y, lse1.z, lse1.w};
-      const float delv[8] = {del0.x, del0.y, del0.z, del0.w, del1.x, del1.y, del1.z, del1.w};
+      const f32x4 lse0 = lds_ld<f32x4>(l0), del0 = lds_ld<f32x4>(l0 + LD_DL);
+      const f32x4 lse1 = lds_ld<f32x4>(l1), del1 = lds_ld<f32x4>(l1 + LD_DL);
+      const float lsev[8] = {lse0[0], lse0[1], lse0[2], lse0[3], lse1[0], lse1[1], lse1[2], lse1[3]};
+      const float delv[8] = {del0[0], del0[1], del0[2], del0[3], del1[0], del1[1], del1[2], del1[3]};
       const float sv[8] = {r.S0[0], r.S0[1], r.S0[2], r.S0[3], r.S1[0], r.S1[1], r.S1[2], r.S1[3]};
       const float dv[8] = {r.D0[0], r.D0[1], r.D0[2], r.D0[3], r.D1[0], r.D1[1], r.D1[2], r.D1[3]};
       const int tb0 = 16 * b0 + 4 * gq + tkey;
@@ -474,6 +480,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
     for (int pr = 0; pr < NPAIR; ++pr) {
       if (pr >= npairs) break;
+      if (pr < 3) issue_pf(pr);
       if (pr + 1 < npairs) {
         sdp[(pr + 1) & 1] = stage_sdp(pr + 1);
         stage_grad(pr, sdp[pr & 1]);
@@ -481,6 +488,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         stage_grad(pr, sdp[pr & 1]);
       }
     }
+    for (int m = max(npairs, 0); m < 3; ++m) issue_pf(m);
     for (int pr = npairs; pr < NPAIR; ++pr) {  // positions past the band
       *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 1)) = u32x2{0u, 0u};
       *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 2)) = u32x2{0u, 0u};
@@ -499,20 +507,18 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     loaded_hi += pf_n;
     if (has_next) take_kv(j + 1, kBn, vBn);  // kB / vB of step j are no longer read
 
-    // dK / dV of this step (zeros if it visited nothing): this wave's keys are
-    // complete after its phase 1
-    if (keyl < s.cap_kv) {
-      T* dkr = dkb + (int64_t)keyl * rs_dk;
-      T* dvr = dvb + (int64_t)keyl * rs_dv;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
+    // dK / dV of this step (zeros if it visited nothing) are complete after
+    // this wave's phase 1; head-dim block db is stored in phase-2 round db
+    auto store_dkdv = [&](int db) {
+      if (keyl < s.cap_kv) {
+        T* dkr = dkb + (int64_t)keyl * rs_dk;
+        T* dvr = dvb + (int64_t)keyl * rs_dv;
         *reinterpret_cast<u32x2*>(dkr + 16 * db + 4 * gq) =
             pack4<T>(p.scale * dKa[db][0], p.scale * dKa[db][1], p.scale * dKa[db][2], p.scale * dKa[db][3]);
         *reinterpret_cast<u32x2*>(dvr + 16 * db + 4 * gq) = pack4<T>(dVa[db][0], dVa[db][1], dVa[db][2], dVa[db][3]);
       }
-    }
-#pragma unroll
-    for (int db = 0; db < 4; ++db) dVa[db] = dKa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dVa[db] = dKa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
 
     // ---- phase 2: dQ^T += K^T dS^T ------------------------------------------
     // Wave v's band starts at block max(L + v, 4 q_lo) and ends at
@@ -535,6 +541,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        store_dkdv(ks);
         bool any = false;
 #pragma unroll
         for (int k = 0; k < NACT; ++k) any |= k_lo[k] <= ks && ks <= k_hi[k];
