@@ -68,8 +68,12 @@ def workloads():
     return {
         "c3": c3,
         "c3_atomic": c3.with_(name=c3.name.replace("_det", "_atomic"), deterministic=False),
+        "c1": CONFIGS["c1"],
         "c2_4k": CONFIGS["c2_4k"],
         "c2_8k": CONFIGS["c2_8k"],
+        "c4": CONFIGS["c4"],
+        "c4_f16": CONFIGS["c4_f16"],
+        "c5": CONFIGS["c5"],
     }
 
 
@@ -90,7 +94,10 @@ def time_backward(w, steps, warmup, seed=0):
 
     inp = make_inputs(w, device="cuda", seed=seed)
     mk = dict(causal=w.causal, bottom_right=w.bottom_right, window_left=w.window_left,
-              scale=w.softmax_scale)
+              scale=w.softmax_scale, cu_seqlens_q=inp["cu_seqlens_q"], cu_seqlens_kv=inp["cu_seqlens_kv"],
+              seq_lens_q=inp["seq_lens_q"], seq_lens_kv=inp["seq_lens_kv"])
+    if w.layout == "thd":
+        mk.update(max_seqlen_q=w.seq_q, max_seqlen_kv=w.seq_kv)
     o, lse = api.forward(inp["q"], inp["k"], inp["v"], sink=inp["sink"], **mk)
     bw = api.Backward(inp["q"], inp["k"], inp["v"], o, inp["dO"], lse, deterministic=w.deterministic,
                       sink=inp["sink"], **mk)
@@ -312,11 +319,17 @@ def main():
              "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS, "relay_expiries": exp,
              "attended_flops": fl}
     if not args.no_extra:
-        for name in ("c3_atomic", "c2_4k", "c2_8k"):
+        # every other workload, timed the same way (the large GQA one with
+        # fewer steps); each entry names its workload's shape
+        for name in ("c3_atomic", "c1", "c2_4k", "c2_8k", "c4", "c4_f16", "c5"):
             if name == args.workload:
                 continue
-            m2, mm2, _ = time_backward(wl[name], max(5, args.steps // 2), args.warmup)
-            extra[name] = {"ms": m2, "tflops": flops(wl[name]) / (m2 * 1e-3) / 1e12, "main_ms": mm2}
+            wx = wl[name]
+            big = wx.batch * wx.heads_q * wx.seq_q * wx.head_dim > (1 << 30)
+            st, wu = (max(3, args.steps // 4), max(3, args.warmup // 10)) if big else (max(5, args.steps // 2), args.warmup)
+            m2, mm2, _ = time_backward(wx, st, wu)
+            extra[name] = {"workload": wx.name, "ms": m2, "tflops": flops(wx) / (m2 * 1e-3) / 1e12, "main_ms": mm2,
+                           "frac_bf16_mfma_peak": flops(wx) / (m2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
     line = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
