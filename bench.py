@@ -249,28 +249,28 @@ def summarize_traffic(fetch_dir, write_dir, out, command, workload):
 
 
 def cpu_baseline(w):
-    """The fp64 oracle's backward timed on a bounded slice of the workload
-    (batch 0, one query head per host thread, each with its own kv head so
-    the oracle's (sequence, kv head) units spread over every thread), scaled
-    to attended TFLOP/s."""
+    """The fp64 oracle's backward timed on the whole workload when it is a
+    dense multi-head one (the oracle runs one (sequence, kv head) unit per
+    host thread), scaled to attended TFLOP/s; other workloads are sampled to
+    one sequence."""
     import oracle
     from sliding_window_attention_flash_amd.synth import make_inputs
 
-    budget_heads = max(1, min(oracle.num_threads(), w.heads_q))
-    ws = w.with_(batch=1, heads_q=budget_heads, heads_kv=budget_heads, name=w.name + "_slice")
+    ws = w if w.layout == "bhsd" and w.batch * w.heads_kv <= 64 else w.with_(batch=1, name=w.name + "_b0")
     inp = make_inputs(ws, device="cpu", seed=0)
-    p = oracle.Problem.dense(1, budget_heads, budget_heads, w.seq_q, w.seq_kv, w.head_dim,
-                             causal=w.causal, bottom_right=w.bottom_right,
-                             window_left=w.window_left, scale=w.softmax_scale)
+    p = oracle.Problem.dense(ws.batch, ws.heads_q, ws.heads_kv, ws.seq_q, ws.seq_kv, ws.head_dim,
+                             causal=ws.causal, bottom_right=ws.bottom_right,
+                             window_left=ws.window_left, scale=ws.softmax_scale)
     t0 = time.perf_counter()
     oracle.backward(p, inp["q"], inp["k"], inp["v"], inp["dO"], None)
     dt = time.perf_counter() - t0
-    pairs = oracle.attended_pairs(p) * budget_heads
-    flops = 10.0 * w.head_dim * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(oracle.num_threads(), budget_heads),
+    pairs = oracle.attended_pairs(p) * ws.heads_q
+    flops = 10.0 * ws.head_dim * pairs
+    units = ws.batch * ws.heads_kv
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(oracle.num_threads(), units),
             "kind": "oracle",
-            "sample": f"fp64 oracle backward (forward recompute included) on batch 0, "
-                      f"{budget_heads} head(s) of {w.name}: {pairs} attended pairs in {dt:.2f} s"}
+            "sample": f"fp64 oracle backward (forward recompute included) on {ws.batch} sequence(s) x "
+                      f"{ws.heads_q} head(s) of {w.name}: {pairs} attended pairs in {dt:.2f} s"}
 
 
 def main():
