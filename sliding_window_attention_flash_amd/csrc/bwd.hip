@@ -93,53 +93,70 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dot: one block per (q-tile, query head, sequence).
+// bwd_dot: one block per (group of DOT_TILES q-tiles, query head, sequence).
+// Every thread issues all of its O / dO loads before the first product, so
+// a block keeps DOT_TILES * 64 rows of loads in flight.
+
+constexpr int DOT_TILES = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
+  typedef typename Elem<T>::vec8 V8;
   const Problem& p = a.p;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int tile0 = blockIdx.x * DOT_TILES, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const Seq s = load_seq(p, b);
-  if (tile == 0 && h == 0 && b == 0 && tid < 2) a.ctl[tid] = 0;
-  if (a.deterministic && tid == 0) a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile] = 0;
+  if (tile0 == 0 && h == 0 && b == 0 && tid < 2) a.ctl[tid] = 0;
+  if (a.deterministic && tid < DOT_TILES && tile0 + tid < p.n_q_tiles)
+    a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile0 + tid] = 0;
 
   constexpr int CH = D / 8;           // 16-byte chunks per row
   constexpr int RPP = kThreads / CH;  // rows per pass
-  __shared__ float s_term[kTile];
+  constexpr int NPT = kTile / RPP;    // passes per q-tile
+  constexpr int NP = DOT_TILES * NPT;
+  __shared__ float s_term[DOT_TILES * kTile];
   const int c = tid % CH, rl = tid / CH;
-  const int row_base = tile * kTile;
-  const T* op = static_cast<const T*>(a.o);
-  const T* dop = static_cast<const T*>(a.dO);
-  for (int r0 = 0; r0 < kTile; r0 += RPP) {
-    const int row = row_base + r0 + rl;
-    float acc = 0.f;
-    if (row < s.len_q) {
-      const auto ov = ld8(op + elem_off(p, p.so, b, s.row0_q, h, row) + 8 * c);
-      const auto gv = ld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, row) + 8 * c);
+  const T* __restrict__ ob = static_cast<const T*>(a.o) + elem_off(p, p.so, b, s.row0_q, h, 0) + 8 * c;
+  const T* __restrict__ gb = static_cast<const T*>(a.dO) + elem_off(p, p.sdo, b, s.row0_q, h, 0) + 8 * c;
+  const int64_t rs_o = p.so[2], rs_g = p.sdo[2];
+  V8 ov[NP], gv[NP];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gv[e];
+  for (int ps = 0; ps < NP; ++ps) {  // rows past the sequence read row 0 and are dropped
+    const int row = tile0 * kTile + ps * RPP + rl;
+    const int rr = row < s.len_q ? row : 0;
+    if (s.len_q > 0) {
+      ov[ps] = *reinterpret_cast<const V8*>(ob + rr * rs_o);
+      gv[ps] = *reinterpret_cast<const V8*>(gb + rr * rs_g);
     }
+  }
+  float* __restrict__ delta = a.delta + s.stat0 + h * s.stat_hs;
+  const float* __restrict__ lse = a.lse + s.stat0 + h * s.stat_hs;
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    const int row = tile0 * kTile + ps * RPP + rl;
+    float acc = 0.f;
+    if (row < s.len_q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += Elem<T>::to_float(ov[ps][e]) * Elem<T>::to_float(gv[ps][e]);
 #pragma unroll
     for (int off = CH / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if (c == 0) {
       float t = 0.f;
       if (row < s.cap_q) {
-        const int64_t si = s.stat0 + h * s.stat_hs + row;
-        a.delta[si] = acc;
+        delta[row] = acc;
         if (p.has_sink && row < s.len_q) {
-          const float l = a.lse[si];
+          const float l = lse[row];
           t = (l == -INFINITY) ? 0.f : expf(a.sink[h] - l) * acc;
         }
       }
-      s_term[r0 + rl] = t;
+      s_term[ps * RPP + rl] = t;
     }
   }
   if (p.has_sink) {
     __syncthreads();
-    if (tid == 0) {
+    if (tid < DOT_TILES && tile0 + tid < p.n_q_tiles) {
       float sum = 0.f;
-      for (int r = 0; r < kTile; ++r) sum += s_term[r];
-      a.sink_part[((int64_t)h * p.B + b) * p.n_q_tiles + tile] = sum;
+      for (int r = 0; r < kTile; ++r) sum += s_term[tid * kTile + r];
+      a.sink_part[((int64_t)h * p.B + b) * p.n_q_tiles + tile0 + tid] = sum;
     }
   }
 
@@ -148,22 +165,25 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
   // for the streaming kernel, q-tiles visited by several chunks, or none).
   // Relay mode: dQ rows of a q-tile that no kv-tile visits (the relay's last
   // visitor writes every other q-tile).
-  const int rows = min(kTile, s.cap_q - row_base);
-  if (rows <= 0) return;
   SeqSched g;
   main_sched(p, s, g);
-  if (!a.deterministic) {
-    if (p.stream && chunk_visitors(p, g, tile) == 1) return;
-    float4* acc = reinterpret_cast<float4*>(a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D);
-    const float4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int e = tid; e < rows * (D / 4); e += kThreads) acc[e] = z;
-  } else if (g.n_visitors(tile) == 0) {
-    T* dqp = static_cast<T*>(a.dq);
-    typename Elem<T>::vec8 z;
+  for (int t = 0; t < DOT_TILES; ++t) {
+    const int tile = tile0 + t, row_base = tile * kTile;
+    const int rows = min(kTile, s.cap_q - row_base);
+    if (tile >= p.n_q_tiles || rows <= 0) break;
+    if (!a.deterministic) {
+      if (p.stream && chunk_visitors(p, g, tile) == 1) continue;
+      float4* acc = reinterpret_cast<float4*>(a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D);
+      const float4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int e = tid; e < rows * (D / 4); e += kThreads) acc[e] = z;
+    } else if (g.n_visitors(tile) == 0) {
+      T* dqp = static_cast<T*>(a.dq);
+      V8 z;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
-    for (int e = tid; e < rows * CH; e += kThreads)
-      st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
+      for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
+      for (int e = tid; e < rows * CH; e += kThreads)
+        st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
+    }
   }
 }
 
@@ -495,7 +515,7 @@ __global__ __launch_bounds__(64) void bwd_dsink_kernel(BwdArgs a) {
 
 template <typename T>
 static hipError_t dot_t(const BwdArgs& a, hipStream_t st) {
-  dim3 grid(a.p.n_q_tiles, a.p.Hq, a.p.B);
+  dim3 grid((a.p.n_q_tiles + DOT_TILES - 1) / DOT_TILES, a.p.Hq, a.p.B);
   if (a.p.D == 64)
     hipLaunchKernelGGL((bwd_dot_kernel<T, 64>), grid, dim3(kThreads), 0, st, a);
   else
