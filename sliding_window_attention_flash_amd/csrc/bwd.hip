@@ -124,7 +124,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
     const int row = tile0 * kTile + ps * RPP + rl;
     const int rr = row < s.len_q ? row : 0;
     if (s.len_q > 0) {
-      ov[ps] = *reinterpret_cast<const V8*>(ob + rr * rs_o);
+      // O is read only here: keep it from displacing dO, which the main
+      // kernel reads next
+      ov[ps] = __builtin_nontemporal_load(reinterpret_cast<const V8*>(ob + rr * rs_o));
       gv[ps] = *reinterpret_cast<const V8*>(gb + rr * rs_g);
     }
   }
