@@ -135,9 +135,12 @@ __device__ __forceinline__ uint32_t pin(uint32_t x) {
 template <typename T, bool RELAY>
 __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
-  // ring slot: Q tile, then the dO tile (QO_DO bytes further); LSE, then delta
-  __shared__ __align__(16) T sQO[NSLOT][2][kTile * TROW];
-  __shared__ __align__(16) float sLD[NSLOT][2][kTile];
+  // The ring is a circle of NRB 16-row blocks: row r of q-tile t is row
+  // r mod 16 of block (4 t + r / 16) mod NRB.  All Q blocks, then all dO
+  // blocks (QO_DO bytes further); LSE, then delta (LD_DL bytes further).
+  constexpr int NRB = 4 * NSLOT;
+  __shared__ __align__(16) T sRing[2][NRB][16 * TROW];
+  __shared__ __align__(16) float sLD[2][NRB][16];
   __shared__ __align__(16) T sK[STEP * TROW];
   __shared__ __align__(16) T sBand[NWAVE][16 * BP];  // dS^T [key][block position, row]
   __shared__ int sTicket;
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) tr_off_b[db] = tr_lane_off(c, gq, db) * sizeof(T);
   const uint32_t ld_off_b = 4 * gq * sizeof(float);  // LSE / delta of rows 4 gq ..
-  const uint32_t ring_q = lds_addr(&sQO[0][0][0]), ring_ld = lds_addr(&sLD[0][0][0]);
+  const uint32_t ring_q = lds_addr(&sRing[0][0][0]), ring_ld = lds_addr(&sLD[0][0][0]);
   // K^T columns of this wave's dQ half (kept out of a runtime-indexed array,
   // which the compiler would place in scratch memory)
   const int tr_off_k0 = tr_lane_off(c, gq, 2 * wd), tr_off_k1 = tr_lane_off(c, gq, 2 * wd + 1);
@@ -256,15 +259,15 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     }
   };
   auto store_q_tile = [&](const QRegs& r) {
-    const int sl = r.tile % NSLOT, row = tid >> 3, ch = tid & 7;
+    const int mb = (r.tile % NSLOT) * 4, row = tid >> 3, ch = tid & 7;  // first block of the tile
     const bool ok = r.tile * kTile + row < s.len_q;
-    *reinterpret_cast<V8*>(&sQO[sl][0][tile_off(row, ch)]) = ok ? r.q : zero8;
-    *reinterpret_cast<V8*>(&sQO[sl][1][tile_off(row, ch)]) = ok ? r.o : zero8;
+    *reinterpret_cast<V8*>(&sRing[0][mb + (row >> 4)][tile_off(row & 15, ch)]) = ok ? r.q : zero8;
+    *reinterpret_cast<V8*>(&sRing[1][mb + (row >> 4)][tile_off(row & 15, ch)]) = ok ? r.o : zero8;
     if (tid < kTile) {
       const bool okr = r.tile * kTile + tid < s.len_q;
       // exp2(x - inf) = 0: padding rows carry no weight
-      sLD[sl][0][tid] = okr ? r.lse * kLog2e : INFINITY;
-      sLD[sl][1][tid] = okr ? r.delta : 0.f;
+      sLD[0][mb + (tid >> 4)][tid & 15] = okr ? r.lse * kLog2e : INFINITY;
+      sLD[1][mb + (tid >> 4)][tid & 15] = okr ? r.delta : 0.f;
     }
   };
 
@@ -400,23 +403,28 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     struct PairSD {
       f32x4 S0, D0, S1, D1;
     };
-    auto pair_rows = [&](int pr, int& b0, int& b1, bool& has1) {
+    // Pair pr holds the band's blocks 2 pr and 2 pr + 1, at ring positions
+    // m0, m1 (consecutive modulo NRB from the band's first block's).
+    const int mlo = blo >= 0 ? blo % NRB : 0;
+    auto pair_rows = [&](int pr, int& b0, int& m0, int& m1, bool& has1) {
       b0 = blo + 2 * pr;
       has1 = b0 + 1 <= bhi;
-      b1 = has1 ? b0 + 1 : b0;
+      m0 = mlo + 2 * pr;
+      m0 = m0 >= NRB ? m0 - NRB : m0;
+      m1 = m0 + 1 == NRB ? 0 : m0 + 1;
+      m1 = has1 ? m1 : m0;
     };
-    // LDS byte address of 16-row block b of its q-tile's ring slot (Q; the
-    // dO rows are QO_DO bytes further), and of its LSE values (delta: LD_DL
-    // bytes further)
-    constexpr uint32_t QO_DO = kTile * TROW * sizeof(T), LD_DL = kTile * sizeof(float);
-    auto blk_addr = [&](int b) { return ring_q + (uint32_t)((b >> 2) % NSLOT) * (2 * QO_DO) + (b & 3) * (16 * TROW * sizeof(T)); };
-    auto ld_addr = [&](int b) { return ring_ld + (uint32_t)((b >> 2) % NSLOT) * (2 * LD_DL) + (b & 3) * (16 * sizeof(float)); };
+    // LDS byte addresses of ring block m (Q; the dO rows are QO_DO bytes
+    // further) and of its LSE values (delta: LD_DL bytes further)
+    constexpr uint32_t QO_DO = NRB * 16 * TROW * sizeof(T), LD_DL = NRB * 16 * sizeof(float);
+    auto blk_addr = [&](int m) { return ring_q + (uint32_t)m * (16 * TROW * sizeof(T)); };
+    auto ld_addr = [&](int m) { return ring_ld + (uint32_t)m * (16 * sizeof(float)); };
     // S = Q K^T and dP = dO V^T of both blocks
     auto stage_sdp = [&](int pr) {
-      int b0, b1;
+      int b0, m0, m1;
       bool has1;
-      pair_rows(pr, b0, b1, has1);
-      const uint32_t a0 = blk_addr(b0), a1 = blk_addr(b1);
+      pair_rows(pr, b0, m0, m1, has1);
+      const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
       PairSD r;
       r.S0 = r.D0 = r.S1 = r.D1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -431,11 +439,11 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     };
     // P, dS, the band write and dV^T += dO^T P, dK^T += Q^T dS
     auto stage_grad = [&](int pr, const PairSD& r) {
-      int b0, b1;
+      int b0, m0, m1;
       bool has1;
-      pair_rows(pr, b0, b1, has1);
-      const uint32_t a0 = blk_addr(b0), a1 = blk_addr(b1);
-      const uint32_t l0 = pin(ld_addr(b0) + ld_off_b), l1 = pin(ld_addr(b1) + ld_off_b);
+      pair_rows(pr, b0, m0, m1, has1);
+      const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
+      const uint32_t l0 = pin(ld_addr(m0) + ld_off_b), l1 = pin(ld_addr(m1) + ld_off_b);
       const f32x4 lse0 = lds_ld<f32x4>(l0), del0 = lds_ld<f32x4>(l0 + LD_DL);
       const f32x4 lse1 = lds_ld<f32x4>(l1), del1 = lds_ld<f32x4>(l1 + LD_DL);
       const float lsev[8] = {lse0[0], lse0[1], lse0[2], lse0[3], lse1[0], lse1[1], lse1[2], lse1[3]};
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const float sv[8] = {r.S0[0], r.S0[1], r.S0[2], r.S0[3], r.S1[0], r.S1[1], r.S1[2], r.S1[3]};
       const float dv[8] = {r.D0[0], r.D0[1], r.D0[2], r.D0[3], r.D1[0], r.D1[1], r.D1[2], r.D1[3]};
       const int tb0 = 16 * b0 + 4 * gq + tkey;
-      const int tb1 = has1 ? 16 * b1 + 4 * gq + tkey : -(1 << 29);
+      const int tb1 = has1 ? 16 * (b0 + 1) + 4 * gq + tkey : -(1 << 29);
       float pv[8], dsv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
