@@ -216,6 +216,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   const int band_wr = c * BP + 4 * gq;                         // dS^T write: key c, rows 4 gq ..
   const int band_rd = (4 * gq + (c >> 2)) * BP + 4 * (c & 3);  // transposed read
   T* const myband = sBand[w];
+  const uint32_t band0 = lds_addr(&sBand[0][0]);
 
   // ---- loaders ------------------------------------------------------------
   // K and V rows of the wave's 16 keys in the MFMA B layout (key c, head-dim
@@ -327,11 +328,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   };
 
   // ---- band geometry ----------------------------------------------------------
-  // 16-row blocks that keys kv0 + 16 v .. + 15 see: rows t = row + diag - key
-  // in [0, W]; clipped to the step's q-tiles; empty past the keys.
-  auto band_lo = [&](int kv0, int v, int qlo) {
-    return max((kv0 + 16 * v - diag) >> 4, 4 * qlo);
-  };
+  // 16-row blocks that keys kv0 + 16 v .. + 15 see (rows t = row + diag - key
+  // in [0, W]): from (kv0 + 16 v - diag) / 16 -- not clipped, so blocks
+  // before row 0 can start a band -- up to the last one, clipped to the
+  // step's q-tiles; empty past the keys.
   auto band_hi = [&](int kv0, int v, int qhi) {
     if (kv0 + 16 * v >= s.len_kv) return INT32_MIN / 2;
     return min((kv0 + 16 * v + 15 + W - diag) >> 4, 4 * qhi - 1);
@@ -396,23 +396,25 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     // the sequence is pushed out of every window through its lane base.
     const int keyl = kv0 + 16 * w + c;
     const int tkey = keyl < s.len_kv ? diag - keyl : -(1 << 29);
-    const int blo = band_lo(kv0, w, qlo), bhi = band_hi(kv0, w, qhi);
-    const int npairs = min(max(bhi - blo + 2, 0) >> 1, NPAIR);
-    // Pair pr holds blocks b0 = blo + 2 pr and b1 = b0 + 1; a b1 past the
-    // band reads block b0 again and is masked out entirely.
+    const int blo = (kv0 + 16 * w - diag) >> 4, bhi = band_hi(kv0, w, qhi);
+    const int npairs = nit == 0 || bhi < 0 ? 0 : min(max(bhi - blo + 2, 0) >> 1, NPAIR);
     struct PairSD {
       f32x4 S0, D0, S1, D1;
     };
-    // Pair pr holds the band's blocks 2 pr and 2 pr + 1, at ring positions
-    // m0, m1 (consecutive modulo NRB from the band's first block's).
-    const int mlo = blo >= 0 ? blo % NRB : 0;
-    auto pair_rows = [&](int pr, int& b0, int& m0, int& m1, bool& has1) {
+    // Pair pr holds the band's blocks b0 = blo + 2 pr and b0 + 1, at ring
+    // positions m0, m1 (consecutive modulo NRB).  A block before row 0 (only
+    // at a sequence start, where q-tile 0 is in the ring) reads block 0, and a
+    // block past the band reads its partner; both are masked out entirely.
+    const int mlo = ((blo % NRB) + NRB) % NRB;
+    auto pair_rows = [&](int pr, int& b0, int& m0, int& m1, bool& has0, bool& has1) {
       b0 = blo + 2 * pr;
-      has1 = b0 + 1 <= bhi;
-      m0 = mlo + 2 * pr;
-      m0 = m0 >= NRB ? m0 - NRB : m0;
-      m1 = m0 + 1 == NRB ? 0 : m0 + 1;
-      m1 = has1 ? m1 : m0;
+      has0 = b0 >= 0;
+      has1 = b0 + 1 >= 0 && b0 + 1 <= bhi;
+      int mm = mlo + 2 * pr;
+      mm = mm >= NRB ? mm - NRB : mm;
+      const int mn = mm + 1 == NRB ? 0 : mm + 1;
+      m0 = has0 ? mm : 0;
+      m1 = has1 ? mn : (b0 + 1 < 0 ? 0 : m0);
     };
     // LDS byte addresses of ring block m (Q; the dO rows are QO_DO bytes
     // further) and of its LSE values (delta: LD_DL bytes further)
@@ -422,8 +424,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     // S = Q K^T and dP = dO V^T of both blocks
     auto stage_sdp = [&](int pr) {
       int b0, m0, m1;
-      bool has1;
-      pair_rows(pr, b0, m0, m1, has1);
+      bool has0, has1;
+      pair_rows(pr, b0, m0, m1, has0, has1);
       const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
       PairSD r;
       r.S0 = r.D0 = r.S1 = r.D1 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -440,8 +442,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     // P, dS, the band write and dV^T += dO^T P, dK^T += Q^T dS
     auto stage_grad = [&](int pr, const PairSD& r) {
       int b0, m0, m1;
-      bool has1;
-      pair_rows(pr, b0, m0, m1, has1);
+      bool has0, has1;
+      pair_rows(pr, b0, m0, m1, has0, has1);
       const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
       const uint32_t l0 = pin(ld_addr(m0) + ld_off_b), l1 = pin(ld_addr(m1) + ld_off_b);
       const f32x4 lse0 = lds_ld<f32x4>(l0), del0 = lds_ld<f32x4>(l0 + LD_DL);
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const float delv[8] = {del0[0], del0[1], del0[2], del0[3], del1[0], del1[1], del1[2], del1[3]};
       const float sv[8] = {r.S0[0], r.S0[1], r.S0[2], r.S0[3], r.S1[0], r.S1[1], r.S1[2], r.S1[3]};
       const float dv[8] = {r.D0[0], r.D0[1], r.D0[2], r.D0[3], r.D1[0], r.D1[1], r.D1[2], r.D1[3]};
-      const int tb0 = 16 * b0 + 4 * gq + tkey;
+      const int tb0 = has0 ? 16 * b0 + 4 * gq + tkey : -(1 << 29);
       const int tb1 = has1 ? 16 * (b0 + 1) + 4 * gq + tkey : -(1 << 29);
       float pv[8], dsv[8];
 #pragma unroll
@@ -529,50 +531,46 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     };
 
     // ---- phase 2: dQ^T += K^T dS^T ------------------------------------------
-    // Wave v's band starts at block max(L + v, 4 q_lo) and ends at
-    // min(H + v, 4 q_hi - 1); waves from vmax on hold no valid key.  Row
-    // block bb therefore meets the bands of waves [bb - H, bb - L], and its
-    // position in wave v's band is min(bb - L - v, bb - 4 q_lo) + 1, with
-    // positions outside [1, band length] holding zeros.
+    // Wave v's band starts at block L + v (L = (kv0 - diag) / 16) and spans
+    // nb = H - L + 1 blocks, so row block bb = 4 (q_lo + k) + wr sits at
+    // position pa = 4 k - 2 ks + c0 of wave 2 ks and pb = pa - 1 of wave
+    // 2 ks + 1, with c0 = wr + 1 + 4 q_lo - L; the pair of waves is active iff
+    // 1 <= pa <= nb + 1.  Positions of clipped or missing blocks hold zeros,
+    // so the positions are compile-time offsets from one per-wave address.
     {
-      const int Lb = (kv0 - diag) >> 4, Hb = (kv0 + 15 + W - diag) >> 4;
-      const int vmax = min((s.len_kv - kv0 + 15) >> 4, NWAVE);
-      int k_lo[NACT], k_hi[NACT], Dk[NACT], Ek[NACT];  // per tile: key pairs, offsets
-#pragma unroll
-      for (int k = 0; k < NACT; ++k) {
-        const int bb = 4 * (qlo + k) + wr;
-        Dk[k] = bb - Lb;
-        Ek[k] = bb - 4 * qlo;
-        const int vlo = max(bb - Hb, 0), vhi = min(Dk[k], vmax - 1);
-        k_lo[k] = k < nit && vlo <= vhi ? vlo >> 1 : 4;
-        k_hi[k] = k < nit && vlo <= vhi ? vhi >> 1 : -1;
-      }
+      const int Lb = (kv0 - diag) >> 4, nb = ((kv0 + 15 + W - diag) >> 4) - Lb + 1;
+      const int c0 = wr + 1 + 4 * qlo - Lb;
+      const uint32_t bbase = pin(band0 + band_rd * sizeof(T) + 32 * c0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         store_dkdv(ks);
         bool any = false;
 #pragma unroll
-        for (int k = 0; k < NACT; ++k) any |= k_lo[k] <= ks && ks <= k_hi[k];
+        for (int k = 0; k < NACT; ++k) any |= k < nit && (unsigned)(4 * k - 2 * ks + c0 - 1) <= (unsigned)nb;
         if (!any) continue;
         const T* kr = sK + 32 * ks * TROW;
         const V8 kt0 = tr_two(kr + tr_off_k0, kr + 16 * TROW + tr_off_k0);
         const V8 kt1 = tr_two(kr + tr_off_k1, kr + 16 * TROW + tr_off_k1);
 #pragma unroll
         for (int k = 0; k < NACT; ++k) {
-          if (!(k_lo[k] <= ks && ks <= k_hi[k])) continue;
-          const int pa = clampi(min(Dk[k] - 2 * ks, Ek[k]) + 1, 0, BPOS - 1);
-          const int pb = clampi(min(Dk[k] - 2 * ks - 1, Ek[k]) + 1, 0, BPOS - 1);
-          const V8 st = tr_two(sBand[2 * ks] + band_rd + 16 * pa, sBand[2 * ks + 1] + band_rd + 16 * pb);
+          if (k >= nit) break;
+          if ((unsigned)(4 * k - 2 * ks + c0 - 1) > (unsigned)nb) continue;
+          const uint32_t ya = bbase + (uint32_t)(2 * ks * 16 * BP * sizeof(T)) + 32 * (4 * k - 2 * ks);
+          const u32x2 lo = lds_tr4(ya), hi = lds_tr4(ya + 16 * BP * sizeof(T) - 32);
+          const V8 st = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
           dQa[k][0] = mfma16(kt0, st, dQa[k][0]);
           dQa[k][1] = mfma16(kt1, st, dQa[k][1]);
         }
       }
     }
 
-    // q-tiles whose last visitor in this chunk was this step
+    // q-tiles whose last visitor in this chunk was this step: kv_last(i) is
+    // nondecreasing in i, and below the last kv-step of the sequence
+    // kv_last(i) <= j iff i <= (128 (j + 1) - diag) / 64 - 1
+    const int nret = j + 1 == j1 || j + 1 >= nkt ? nit : min(((STEP * (j + 1) - diag) >> 6) - qlo, nit);
 #pragma unroll
     for (int k = 0; k < NACT; ++k)
-      if (k < nit && min(kv_last(qlo + k), j1 - 1) == j) retire(qlo + k, dQa[k]);
+      if (k < nret) retire(qlo + k, dQa[k]);
   }
 
   // ---- relay: boundary q-tiles this chunk joined after another chunk -------
