@@ -190,41 +190,76 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_main: one block (4 waves) per (kv-tile of 64 keys, kv head, sequence).
+// bwd_main: one block (4 waves) per (kv-tile of 64 keys, kv head, sequence);
+// two blocks per CU.
 //
 // Each wave owns 16 keys of the tile.  For every query head of the kv
 // head's group and every q-tile i in [q_lo, q_hi) (descending i):
-//   S  = Q_i K^T,  dP = dO_i V^T            (A: Q / dO rows from LDS,
-//                                             B: the wave's K / V rows, regs)
-//   P  = exp2(S * scale * log2e - LSE_i * log2e),  dS = P (dP - delta_i)
-//   dV^T += dO_i^T P,  dK^T += Q_i^T dS      (B: P / dS straight from the
-//                                             accumulator, A: transposed tile)
-//   dQ_i += dS K                              (dS through LDS, K^T in regs)
-// dQ_i is added into the fp32 accumulator with atomics, or through the
-// ordered relay.  All products are 16x16x32 MFMAs, fp32 accumulation.
+//   S  = Q_i K^T,  dP = dO_i V^T         A: Q / dO rows (LDS), B: the wave's
+//                                         K / V rows (registers)
+//   P  = exp2(S c - LSE_i),  dS = P (dP - delta_i)             (fp32, masked)
+//   dV^T += dO_i^T P,  dK^T += Q_i^T dS   A: transposed reads of the Q / dO
+//                                         tile, B: P / dS from the accumulator
+//   dQ_i = dS K                           A: transposed reads of dS^T,
+//                                         B: transposed reads of the K tile
+// and dQ_i is added into the fp32 accumulator with atomics, or through the
+// ordered relay.  A wave skips the 16-row blocks its keys cannot see.  The
+// next visit's Q / dO tile is loaded into registers while the current one
+// computes.  All products are 16x16x32 MFMAs with fp32 accumulation.
+//
+// Tiles are row-major with the 16-byte chunks of row r permuted by XOR with
+// (r mod 8) (64-wide rows) or 2 (r mod 8) (128-wide rows, moving whole
+// 32-byte pairs): the 8 rows a half-wave's transposed read touches then
+// fall on disjoint banks.
+
+namespace {
+
+template <int D>
+__device__ __forceinline__ int tsw(int r) { return D == 64 ? (r & 7) : ((r & 7) << 1); }
+// element offset of (row r, 16-byte chunk ch) in a D-wide swizzled tile
+template <int D>
+__device__ __forceinline__ int toff(int r, int ch) { return r * D + ((ch ^ tsw<D>(r)) << 3); }
+// lane offset of a transposed read: row 4 g + c / 4, column 16 cb + 4 (c % 4)
+template <int D>
+__device__ __forceinline__ int troff(int c, int g, int cb) {
+  const int r = 4 * g + (c >> 2);
+  return r * D + (((2 * cb + ((c & 3) >> 1)) ^ tsw<D>(r)) << 3) + 4 * (c & 1);
+}
+typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+template <typename T>
+__device__ __forceinline__ u32x2 ldtr(const T* p) {
+  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+// 8 contraction values for lane (c, g): e < 4 from the read at p0, e >= 4 from p1
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::vec8 trpair(const T* p0, const T* p1) {
+  const u32x2 lo = ldtr(p0), hi = ldtr(p1);
+  return __builtin_bit_cast(typename Elem<T>::vec8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+}  // namespace
 
 template <typename T, int D, bool RELAY>
-__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
   constexpr int NS = D / 32;       // k-steps over the head dim
   constexpr int NDB = D / 16;      // 16-column blocks of the head dim
-  constexpr int LDR = D + 8;       // pitch of row-major tiles (elements)
-  constexpr int LDT = kTile + 8;   // pitch of transposed tiles
   constexpr int CH = D / 8;        // 16-byte chunks per row
   constexpr int RPP = kThreads / CH;
   constexpr int NPASS = kTile / RPP;
 
-  __shared__ __align__(16) T sQ[kTile * LDR];
-  __shared__ __align__(16) T sdO[kTile * LDR];
-  __shared__ __align__(16) T sQt[D * LDT];
-  __shared__ __align__(16) T sdOt[D * LDT];
-  __shared__ __align__(16) T sdS[kTile * LDT];
-  __shared__ __align__(16) T sKt[D * LDT];
-  __shared__ float sLse[kTile], sDelta[kTile];
+  __shared__ __align__(16) T sQ[kTile * D];
+  __shared__ __align__(16) T sdO[kTile * D];
+  __shared__ __align__(16) T sK[kTile * D];
+  __shared__ __align__(16) T sdSt[kTile * kTile];  // dS^T [key][q], 64-wide swizzled rows
+  __shared__ __align__(16) float sLse[kTile];
+  __shared__ __align__(16) float sDelta[kTile];
   __shared__ int sTicket;
 
   const Problem& p = a.p;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int L;
   if (RELAY) {
@@ -256,100 +291,97 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int nvisit = nit * p.G;
 
   const T* qp = static_cast<const T*>(a.q);
-  const T* kp = static_cast<const T*>(a.k);
-  const T* vp = static_cast<const T*>(a.v);
   const T* dop = static_cast<const T*>(a.dO);
-
   V8 zero8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) zero8[e] = Elem<T>::from_float(0.f);
 
-  // K / V rows of this wave's 16 keys: B operands of S = Q K^T, dP = dO V^T.
+  // Mask: with t = row + diag - key, an element is visible iff
+  // tlo <= t <= thi (tlo = 0 if causal, thi = W if windowed; otherwise far
+  // out of reach).  A key past the sequence is pushed below tlo through its
+  // lane term, and rows past the sequence carry LSE = +inf.
+  const int tlo = p.causal ? 0 : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
+  const unsigned trange = (unsigned)(thi - tlo);
   const int key = kv0 + 16 * w + c;
+  const int tkey = key < s.len_kv ? g.diag - key - tlo : -(1 << 30);  // t - tlo = row + tkey
+
+  // K / V rows of this wave's 16 keys (B operands of S = Q K^T, dP = dO V^T)
+  // and the whole K tile in LDS (A operand of dQ^T = K^T dS^T).
   V8 kB[NS], vB[NS];
   {
     const bool ok = key < s.len_kv;
-    const int64_t ko = elem_off(p, p.sk, b, s.row0_kv, hk, ok ? key : 0);
-    const int64_t vo = elem_off(p, p.sv, b, s.row0_kv, hk, ok ? key : 0);
+    const int kr = min(key, max(s.len_kv - 1, 0));
+    const T* krow = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, kr) + 8 * gq;
+    const T* vrow = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, kr) + 8 * gq;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      kB[st] = ok ? ld8(kp + ko + 32 * st + 8 * gq) : zero8;
-      vB[st] = ok ? ld8(vp + vo + 32 * st + 8 * gq) : zero8;
+      kB[st] = ok ? ld8(krow + 32 * st) : zero8;
+      vB[st] = ok ? ld8(vrow + 32 * st) : zero8;
     }
   }
-  // K^T of the whole tile through LDS: B operands of dQ = dS K.
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = tid / CH + ps * RPP, ch = tid % CH, kk = kv0 + r;
-    V8 x = zero8;
-    if (kk < s.len_kv) x = ld8(kp + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sKt[(8 * ch + e) * LDT + r] = x[e];
+    const V8 x = kk < s.len_kv
+                     ? ld8(static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch)
+                     : zero8;
+    *reinterpret_cast<V8*>(&sK[toff<D>(r, ch)]) = x;
   }
-  __syncthreads();
-  V8 kdq[2][NDB];
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) kdq[s2][db] = lds_pair4(&sKt[(16 * db + c) * LDT + 32 * s2 + 4 * gq]);
 
   f32x4 dV[NDB], dK[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dV[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dK[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int db = 0; db < NDB; ++db) dV[db] = dK[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Staging of one visit's Q / dO tile (registers first, then LDS).
   V8 rq[NPASS], rdo[NPASS];
   float rlse = 0.f, rdelta = 0.f;
+  int st_i = 0;
   auto visit_hi = [&](int v, int& h, int& i) {
     h = hk * p.G + v / nit;
     i = qlo + (nit - 1 - v % nit);  // descending q-tiles within a head
   };
-  auto stage_load = [&](int v) {
+  auto stage_load = [&](int v) {  // a visited q-tile: the sequence has rows
     int h, i;
     visit_hi(v, h, i);
+    st_i = i;
+    const int row0 = i * kTile;
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = tid / CH + ps * RPP, ch = tid % CH, qi = i * kTile + r;
-      if (qi < s.len_q) {
-        rq[ps] = ld8(qp + elem_off(p, p.sq, b, s.row0_q, h, qi) + 8 * ch);
-        rdo[ps] = ld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, qi) + 8 * ch);
-      } else {
-        rq[ps] = zero8;
-        rdo[ps] = zero8;
-      }
+      const int qi = min(row0 + tid / CH + ps * RPP, s.len_q - 1), ch = tid % CH;
+      rq[ps] = ld8(qp + elem_off(p, p.sq, b, s.row0_q, h, qi) + 8 * ch);
+      rdo[ps] = ld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, qi) + 8 * ch);
     }
     if (tid < kTile) {
-      const int qi = i * kTile + tid;
-      if (qi < s.len_q) {
-        const int64_t si = s.stat0 + h * s.stat_hs + qi;
-        rlse = a.lse[si] * kLog2e;
-        rdelta = a.delta[si];
-      } else {
-        rlse = INFINITY;  // exp2(x - inf) = 0: padding rows carry no weight
-        rdelta = 0.f;
-      }
+      const int64_t si = s.stat0 + h * s.stat_hs + min(row0 + tid, s.len_q - 1);
+      rlse = a.lse[si];
+      rdelta = a.delta[si];
     }
   };
   auto stage_store = [&]() {
+    const int row0 = st_i * kTile;
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int r = tid / CH + ps * RPP, ch = tid % CH;
-      st8(&sQ[r * LDR + 8 * ch], rq[ps]);
-      st8(&sdO[r * LDR + 8 * ch], rdo[ps]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sQt[(8 * ch + e) * LDT + r] = rq[ps][e];
-        sdOt[(8 * ch + e) * LDT + r] = rdo[ps][e];
-      }
+      const bool ok = row0 + r < s.len_q;
+      *reinterpret_cast<V8*>(&sQ[toff<D>(r, ch)]) = ok ? rq[ps] : zero8;
+      *reinterpret_cast<V8*>(&sdO[toff<D>(r, ch)]) = ok ? rdo[ps] : zero8;
     }
     if (tid < kTile) {
-      sLse[tid] = rlse;
-      sDelta[tid] = rdelta;
+      const bool ok = row0 + tid < s.len_q;
+      sLse[tid] = ok ? rlse * kLog2e : INFINITY;  // exp2(x - inf) = 0: padding rows carry no weight
+      sDelta[tid] = ok ? rdelta : 0.f;
     }
   };
+
+  // per-lane LDS offsets (elements)
+  int rd_off[NS], tr_off[NDB], ds_w[4];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) rd_off[st] = toff<D>(c, 4 * st + gq);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) tr_off[db] = troff<D>(c, gq, db);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) ds_w[mb] = toff<kTile>(16 * w + c, 2 * mb + (gq >> 1)) + 4 * (gq & 1);
+  const int ds_tr = troff<kTile>(c, gq, w);  // dS^T columns (q) 16 w ..
 
   if (nvisit > 0) {
     stage_load(0);
@@ -362,54 +394,79 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     int h, i;
     visit_hi(v, h, i);
     if (v + 1 < nvisit) stage_load(v + 1);
+    const int q0 = i * kTile;
+    // t - tlo of (row q0, key kv0 + 16 w); block mb spans [u_mb - 15, u_mb + 15]
+    const int u0 = q0 + g.diag - (kv0 + 16 * w) - tlo;
 
     f32x4 S[4], dP[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      S[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dP[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      S[mb] = dP[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int um = u0 + 16 * mb;
+      if (um + 15 < 0 || um - 15 > (int)trange) continue;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const V8 aq = *reinterpret_cast<const V8*>(&sQ[(16 * mb + c) * LDR + 32 * st + 8 * gq]);
-        const V8 ado = *reinterpret_cast<const V8*>(&sdO[(16 * mb + c) * LDR + 32 * st + 8 * gq]);
-        S[mb] = mfma16(aq, kB[st], S[mb]);
-        dP[mb] = mfma16(ado, vB[st], dP[mb]);
+        S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[st]]), kB[st], S[mb]);
+        dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[st]]), vB[st], dP[mb]);
       }
     }
     V8 pP[2], pS[2];
-    const int q0 = i * kTile;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb) {
+      const int um = u0 + 16 * mb;
+      const bool any = um + 15 >= 0 && um - 15 <= (int)trange;
+      float pv[4] = {0.f, 0.f, 0.f, 0.f}, dsv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (any) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&sLse[16 * mb + 4 * gq]);
+        const f32x4 del4 = *reinterpret_cast<const f32x4*>(&sDelta[16 * mb + 4 * gq]);
+        const int tb = q0 + 16 * mb + 4 * gq + tkey;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = S[mb][r] * p.scale_log2 - lse4[r];
+          asm("" : "+v"(x));
+          pv[r] = fast_exp2((unsigned)(tb + r) <= trange ? x : -INFINITY);
+          dsv[r] = pv[r] * (dP[mb][r] - del4[r]);
+        }
+      }
+      T pk[4], sk[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int lr = 16 * mb + 4 * gq + r;
-        const bool vis = visible(g, q0 + lr, key);
-        const float pv = vis ? fast_exp2(S[mb][r] * p.scale_log2 - sLse[lr]) : 0.f;
-        const float dsv = vis ? pv * (dP[mb][r] - sDelta[lr]) : 0.f;
-        pP[mb >> 1][(mb & 1) * 4 + r] = Elem<T>::from_float(pv);
-        pS[mb >> 1][(mb & 1) * 4 + r] = Elem<T>::from_float(dsv);
-        sdS[lr * LDT + 16 * w + c] = Elem<T>::from_float(dsv);
+        pk[r] = Elem<T>::from_float(pv[r]);
+        sk[r] = Elem<T>::from_float(dsv[r]);
+        pP[mb >> 1][(mb & 1) * 4 + r] = pk[r];
+        pS[mb >> 1][(mb & 1) * 4 + r] = sk[r];
       }
+      *reinterpret_cast<u32x2*>(&sdSt[ds_w[mb]]) = __builtin_bit_cast(u32x2, sk);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over 32-row halves that see any key
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int um = u0 + 32 * s2;  // rows +0..31: t - tlo in [um - 15, um + 31]
+      if (um + 31 < 0 || um - 15 > (int)trange) continue;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        dV[db] = mfma16(lds_pair4(&sdOt[(16 * db + c) * LDT + 32 * s2 + 4 * gq]), pP[s2], dV[db]);
-        dK[db] = mfma16(lds_pair4(&sQt[(16 * db + c) * LDT + 32 * s2 + 4 * gq]), pS[s2], dK[db]);
+      for (int db = 0; db < NDB; ++db) {
+        dV[db] = mfma16(trpair(&sdO[32 * s2 * D + tr_off[db]], &sdO[(32 * s2 + 16) * D + tr_off[db]]), pP[s2], dV[db]);
+        dK[db] = mfma16(trpair(&sQ[32 * s2 * D + tr_off[db]], &sQ[(32 * s2 + 16) * D + tr_off[db]]), pS[s2], dK[db]);
       }
-    __syncthreads();  // dS complete; the Q / dO tiles are free
+    }
+    __syncthreads();  // dS^T complete; the Q / dO tile is free
     if (v + 1 < nvisit) stage_store();
 
+    // dQ rows q0 + 16 w + 4 gq + r, d = 16 db + c: each accumulator add
+    // covers 16 consecutive floats of 4 rows
     f32x4 dQ[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      dQ[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < NDB; ++db) dQ[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        dQ[db] = mfma16(lds_pair4(&sdS[(16 * w + c) * LDT + 32 * s2 + 4 * gq]), kdq[s2][db], dQ[db]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const V8 as = trpair(&sdSt[32 * ks * kTile + ds_tr], &sdSt[(32 * ks + 16) * kTile + ds_tr]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dQ[db] = mfma16(as, trpair(&sK[32 * ks * D + tr_off[db]], &sK[(32 * ks + 16) * D + tr_off[db]]), dQ[db]);
     }
 
-    const int64_t acc_row0 = s.stat0 + h * s.stat_hs + q0;
+    const int qr0 = q0 + 16 * w + 4 * gq;  // row of dQ[.][0]
+    float* accr = a.dq_acc + (s.stat0 + h * s.stat_hs + qr0) * D + c;
     if (RELAY) {
       // Ordered relay: visitors of q-tile i add in kv-tile order; a turn is
       // counted from i's first visitor kv_first(i).  Every access to the
@@ -422,25 +479,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       if (tid == 0 && turn > 0) relay_wait(semp, turn, a.spin_limit, a.ctl + 1);
       __syncthreads();
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int r = 0; r < 4; ++r) {
+        if (qr0 + r >= s.cap_q) continue;
+        T* outr = dqp + elem_off(p, p.sdq, b, s.row0_q, h, qr0 + r) + c;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = 16 * w + 4 * gq + r, qi = q0 + lr;
-          if (qi >= s.cap_q) continue;
-          relay_add<T>(a.dq_acc + (acc_row0 + lr) * D + 16 * db + c, dQ[db][r], turn, nv, p.scale,
-                       dqp + elem_off(p, p.sdq, b, s.row0_q, h, qi) + 16 * db + c);
-        }
+        for (int db = 0; db < NDB; ++db)
+          relay_add<T>(accr + r * D + 16 * db, dQ[db][r], turn, nv, p.scale, outr + 16 * db);
+      }
       relay_release(semp, turn, nv, tid);
     } else {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int r = 0; r < 4; ++r)
+        if (qr0 + r < s.len_q)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = 16 * w + 4 * gq + r;
-          if (q0 + lr < s.len_q) unsafeAtomicAdd(a.dq_acc + (acc_row0 + lr) * D + 16 * db + c, dQ[db][r]);
-        }
+          for (int db = 0; db < NDB; ++db) unsafeAtomicAdd(accr + r * D + 16 * db, dQ[db][r]);
     }
-    __syncthreads();  // next tile staged; dS reads done
+    __syncthreads();  // next tile staged; dS^T reads done
   }
 
   // Epilogue: dK = scale * sum dS^T Q, dV = sum P^T dO; a tile that visited
