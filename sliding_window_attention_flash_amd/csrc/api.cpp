@@ -144,6 +144,9 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   p.stream = p.G == 1 && d->causal && d->window_left >= 0 && d->window_left <= 128 && d->head_dim == 64 &&
              small_rows;
   p.step_kv = p.stream ? 128 : kTile;
+  // The per-tile kernel in unordered mode leaves dQ to a q-major pass (no
+  // fp32 accumulator); in deterministic mode dQ goes through the relay.
+  p.split_dq = !p.stream && !d->deterministic;
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one
     // block per MI355X CU, never shorter than 2 steps (so a q-tile has at
@@ -214,7 +217,7 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   pl->off_delta = off;
   off = align256(off + sizeof(float) * (size_t)pl->stat_rows);
   pl->off_acc = off;
-  off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
+  if (!p.split_dq) off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
   pl->off_stash = off;
   if (p.stream && desc->deterministic) off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
   pl->off_sem = off;
@@ -306,7 +309,9 @@ sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensor
     return fail(SDPA_ERR_HIP, "bwd_main launch: %s", hipGetErrorString(e));
   if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if (!d.deterministic && (e = swa::launch_bwd_cvt(a, stream)) != hipSuccess)
+  if (a.p.split_dq && (e = swa::launch_bwd_dq(a, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "bwd_dq launch: %s", hipGetErrorString(e));
+  if (!d.deterministic && !a.p.split_dq && (e = swa::launch_bwd_cvt(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_cvt launch: %s", hipGetErrorString(e));
   if (d.has_sink && (e = swa::launch_bwd_dsink(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dsink launch: %s", hipGetErrorString(e));

@@ -3,7 +3,9 @@
 //   bwd_dot   delta_i = <dO_i, O_i>, per-q-tile dSink partials, clearing of
 //             the relay counters and of the dQ accumulator
 //   bwd_main  kv-tile-stationary backward with the window-bounded q-loop
-//   bwd_cvt   fp32 dQ accumulator -> 16-bit dQ (atomic mode)
+//             (dK, dV; dQ too in deterministic mode, through the relay)
+//   bwd_dq    q-tile-stationary dQ pass (unordered mode)
+//   bwd_cvt   fp32 dQ accumulator -> 16-bit dQ (streaming kernel, atomic mode)
 //   bwd_dsink fixed-order dSink reduction
 //
 // Method sources (web pages): cudnn-frontend PR #866 "frost(sdpa): bound the
@@ -162,11 +164,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
     }
   }
 
-  // Clearing for the main kernel.  Atomic mode: the fp32 accumulator rows of
-  // a q-tile whose dQ is summed there (every q-tile for the per-tile kernel;
-  // for the streaming kernel, q-tiles visited by several chunks, or none).
-  // Relay mode: dQ rows of a q-tile that no kv-tile visits (the relay's last
-  // visitor writes every other q-tile).
+  // Clearing for the main kernel.  Atomic mode (streaming kernel only; the
+  // per-tile kernel's dQ pass keeps no accumulator): the fp32 accumulator
+  // rows of q-tiles visited by several chunks, or none.  Relay mode: dQ rows
+  // of a q-tile that no kv-tile visits (the relay's last visitor writes
+  // every other q-tile).
   SeqSched g;
   main_sched(p, s, g);
   for (int t = 0; t < DOT_TILES; ++t) {
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
     const int rows = min(kTile, s.cap_q - row_base);
     if (tile >= p.n_q_tiles || rows <= 0) break;
     if (!a.deterministic) {
-      if (p.stream && chunk_visitors(p, g, tile) == 1) continue;
+      if (p.split_dq || chunk_visitors(p, g, tile) == 1) continue;
       float4* acc = reinterpret_cast<float4*>(a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D);
       const float4 z = {0.f, 0.f, 0.f, 0.f};
       for (int e = tid; e < rows * (D / 4); e += kThreads) acc[e] = z;
@@ -202,8 +204,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
 //                                         tile, B: P / dS from the accumulator
 //   dQ_i = dS K                           A: transposed reads of dS^T,
 //                                         B: transposed reads of the K tile
-// and dQ_i is added into the fp32 accumulator with atomics, or through the
-// ordered relay.  A wave skips the 16-row blocks its keys cannot see.  The
+// and dQ_i is added into q-tile i's fp32 partial through the ordered relay
+// (deterministic mode); in unordered mode dQ is left to bwd_dq and the two
+// dS^T / dQ steps drop out.  A wave skips the 16-row blocks its keys cannot see.  The
 // next visit's Q / dO tile is loaded into registers while the current one
 // computes.  All products are 16x16x32 MFMAs with fp32 accumulation.
 //
@@ -319,13 +322,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
       vB[st] = ok ? ld8(vrow + 32 * st) : zero8;
     }
   }
+  if (RELAY) {
 #pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int r = tid / CH + ps * RPP, ch = tid % CH, kk = kv0 + r;
-    const V8 x = kk < s.len_kv
-                     ? ld8(static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch)
-                     : zero8;
-    *reinterpret_cast<V8*>(&sK[toff<D>(r, ch)]) = x;
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int r = tid / CH + ps * RPP, ch = tid % CH, kk = kv0 + r;
+      const V8 x = kk < s.len_kv
+                       ? ld8(static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch)
+                       : zero8;
+      *reinterpret_cast<V8*>(&sK[toff<D>(r, ch)]) = x;
+    }
   }
 
   f32x4 dV[NDB], dK[NDB];
@@ -436,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
         pP[mb >> 1][(mb & 1) * 4 + r] = pk[r];
         pS[mb >> 1][(mb & 1) * 4 + r] = sk[r];
       }
-      *reinterpret_cast<u32x2*>(&sdSt[ds_w[mb]]) = __builtin_bit_cast(u32x2, sk);
+      if (RELAY) *reinterpret_cast<u32x2*>(&sdSt[ds_w[mb]]) = __builtin_bit_cast(u32x2, sk);
     }
     // dV^T += dO^T P, dK^T += Q^T dS over 32-row halves that see any key
 #pragma unroll
@@ -451,9 +456,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
     }
     __syncthreads();  // dS^T complete; the Q / dO tile is free
     if (v + 1 < nvisit) stage_store();
+    if (!RELAY) {
+      __syncthreads();  // next tile staged
+      continue;
+    }
 
-    // dQ rows q0 + 16 w + 4 gq + r, d = 16 db + c: each accumulator add
-    // covers 16 consecutive floats of 4 rows
+    // dQ rows q0 + 16 w + 4 gq + r, d = 16 db + c: each relay add covers 16
+    // consecutive floats of 4 rows
     f32x4 dQ[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dQ[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -465,35 +474,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
         dQ[db] = mfma16(as, trpair(&sK[32 * ks * D + tr_off[db]], &sK[(32 * ks + 16) * D + tr_off[db]]), dQ[db]);
     }
 
+    // Ordered relay: visitors of q-tile i add in kv-tile order; a turn is
+    // counted from i's first visitor kv_first(i).  Every access to the fp32
+    // partial is an agent-scope atomic read-modify-write (coherent across
+    // XCDs), so a release only has to wait until this block's atomics have
+    // completed (s_waitcnt) before passing the turn on; no L2 write-back is
+    // needed.
     const int qr0 = q0 + 16 * w + 4 * gq;  // row of dQ[.][0]
     float* accr = a.dq_acc + (s.stat0 + h * s.stat_hs + qr0) * D + c;
-    if (RELAY) {
-      // Ordered relay: visitors of q-tile i add in kv-tile order; a turn is
-      // counted from i's first visitor kv_first(i).  Every access to the
-      // fp32 partial is an agent-scope atomic read-modify-write (coherent
-      // across XCDs), so a release only has to wait until this block's
-      // atomics have completed (s_waitcnt) before passing the turn on; no
-      // L2 write-back is needed.
-      const int turn = g.relay_turn(i, jt), nv = g.n_visitors(i);
-      int* semp = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
-      if (tid == 0 && turn > 0) relay_wait(semp, turn, a.spin_limit, a.ctl + 1);
-      __syncthreads();
+    const int turn = g.relay_turn(i, jt), nv = g.n_visitors(i);
+    int* semp = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
+    if (tid == 0 && turn > 0) relay_wait(semp, turn, a.spin_limit, a.ctl + 1);
+    __syncthreads();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (qr0 + r >= s.cap_q) continue;
-        T* outr = dqp + elem_off(p, p.sdq, b, s.row0_q, h, qr0 + r) + c;
+    for (int r = 0; r < 4; ++r) {
+      if (qr0 + r >= s.cap_q) continue;
+      T* outr = dqp + elem_off(p, p.sdq, b, s.row0_q, h, qr0 + r) + c;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          relay_add<T>(accr + r * D + 16 * db, dQ[db][r], turn, nv, p.scale, outr + 16 * db);
-      }
-      relay_release(semp, turn, nv, tid);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (qr0 + r < s.len_q)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) unsafeAtomicAdd(accr + r * D + 16 * db, dQ[db][r]);
+      for (int db = 0; db < NDB; ++db)
+        relay_add<T>(accr + r * D + 16 * db, dQ[db][r], turn, nv, p.scale, outr + 16 * db);
     }
+    relay_release(semp, turn, nv, tid);
     __syncthreads();  // next tile staged; dS^T reads done
   }
 
@@ -512,6 +513,184 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
       }
       *reinterpret_cast<u32x2*>(dkp + 16 * db + 4 * gq) = __builtin_bit_cast(u32x2, kx);
       *reinterpret_cast<u32x2*>(dvp + 16 * db + 4 * gq) = __builtin_bit_cast(u32x2, vx);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dq: q-tile-stationary dQ pass of the unordered mode, one block (4
+// waves) per (q-tile i of 64 rows, query head, sequence); two blocks per CU.
+//
+// Each wave owns 16 query rows; a lane keeps its row's Q and dO slices (the
+// B operands below), LSE and delta in registers.  For every kv-tile j in
+// [kv_first(i), kv_last(i)] (K and V staged in LDS, double-buffered, the
+// next tile loaded into registers while the current one computes):
+//   S^T = K Q^T,  dP^T = V dO^T       A: K / V rows (LDS), B: Q / dO
+//   P^T = exp2(S^T c - LSE),  dS^T = P^T (dP^T - delta)        (fp32, masked)
+//   dQ^T += K^T dS^T                   A: transposed reads of the K tile,
+//                                      B: dS^T straight from the accumulator
+// Every dQ row is produced by one wave and leaves as 16-bit values once, so
+// no fp32 accumulator or conversion pass exists.  The transposed orientation
+// leaves each lane with 4 consecutive head-dim values of one row: one 8-byte
+// store per 16 columns.  A wave skips the 16-key blocks its rows cannot see.
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  typedef typename Elem<T>::vec8 V8;
+  constexpr int NS = D / 32;   // k-steps over the head dim
+  constexpr int NDB = D / 16;  // 16-column blocks of the head dim
+  constexpr int CH = D / 8;    // 16-byte chunks per row
+  constexpr int RPP = kThreads / CH;
+  constexpr int NPASS = kTile / RPP;
+
+  __shared__ __align__(16) T sK[2][kTile * D];
+  __shared__ __align__(16) T sV[2][kTile * D];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // block -> (sequence, kv head, q-tile, head within the group): the heads
+  // that share a kv head, and neighbouring q-tiles, read the same K / V
+  // tiles and run next to each other on one XCD
+  int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int hg = L % p.G;
+  L /= p.G;
+  const int i = L % p.n_q_tiles;
+  L /= p.n_q_tiles;
+  const int hk = L % p.Hkv, b = L / p.Hkv, h = hk * p.G + hg;
+  const Seq s = load_seq(p, b);
+  const int q0 = i * kTile;
+  if (q0 >= s.cap_q) return;
+  SeqSched g;
+  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, kTile);
+  const int nv = g.n_visitors(i), jf = g.kv_first(i);  // nv > 0 implies len_q, len_kv > 0
+
+  const int row = q0 + 16 * w + c;  // this lane's query row
+  V8 qB[NS], oB[NS];
+  float lse2 = INFINITY, del = 0.f;  // padding rows: P = exp2(-inf) = 0
+  if (nv > 0) {
+    const int qr = min(row, s.len_q - 1);
+    const T* qrow = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, qr) + 8 * gq;
+    const T* orow = static_cast<const T*>(a.dO) + elem_off(p, p.sdo, b, s.row0_q, h, qr) + 8 * gq;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      qB[st] = ld8(qrow + 32 * st);
+      oB[st] = ld8(orow + 32 * st);
+    }
+    if (row < s.len_q) {
+      const int64_t si = s.stat0 + h * s.stat_hs + row;
+      lse2 = a.lse[si] * kLog2e;
+      del = a.delta[si];
+    }
+  }
+
+  // K / V staging; rows past the sequence repeat its last key (finite
+  // values; the mask gives them zero weight)
+  const T* kp = static_cast<const T*>(a.k);
+  const T* vp = static_cast<const T*>(a.v);
+  V8 rk[NPASS], rv[NPASS];
+  auto load_kv = [&](int j) {
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int kk = min(j * kTile + tid / CH + ps * RPP, s.len_kv - 1), ch = tid % CH;
+      rk[ps] = ld8(kp + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch);
+      rv[ps] = ld8(vp + elem_off(p, p.sv, b, s.row0_kv, hk, kk) + 8 * ch);
+    }
+  };
+  auto store_kv = [&](int buf) {
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int r = tid / CH + ps * RPP, ch = tid % CH;
+      *reinterpret_cast<V8*>(&sK[buf][toff<D>(r, ch)]) = rk[ps];
+      *reinterpret_cast<V8*>(&sV[buf][toff<D>(r, ch)]) = rv[ps];
+    }
+  };
+
+  // per-lane LDS offsets (elements)
+  int rd_off[NS], tr_off[NDB];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) rd_off[st] = toff<D>(c, 4 * st + gq);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) tr_off[db] = troff<D>(c, gq, db);
+
+  // Mask as in bwd_main: with t = row + diag - key, visible iff
+  // 0 <= t - tlo <= trange, and the key lies inside the sequence.
+  const int tlo = p.causal ? 0 : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
+  const unsigned trange = (unsigned)(thi - tlo);
+
+  f32x4 dQt[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dQt[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nv > 0) {
+    load_kv(jf);
+    store_kv(0);
+  }
+  __syncthreads();
+  for (int n = 0; n < nv; ++n) {
+    const int kv0 = (jf + n) * kTile, buf = n & 1;
+    if (n + 1 < nv) load_kv(jf + n + 1);
+    const T* cK = sK[buf];
+    const T* cV = sV[buf];
+    const int kvn = s.len_kv - kv0;                      // keys of this tile inside the sequence
+    const int u0 = q0 + 16 * w + g.diag - tlo - kv0;     // t - tlo at (row q0 + 16 w, key kv0)
+    const int tq = u0 + c - 4 * gq;                      // t - tlo at (row, key kv0 + 4 gq), minus 16 nb + r
+
+    f32x4 St[4], dPt[4];
+    bool live[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      St[nb] = dPt[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int um = u0 - 16 * nb;  // the block spans t - tlo in [um - 15, um + 15]
+      live[nb] = um + 15 >= 0 && um - 15 <= (int)trange && 16 * nb < kvn;
+      if (!live[nb]) continue;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[st]]), qB[st], St[nb]);
+        dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[st]]), oB[st], dPt[nb]);
+      }
+    }
+    // dS^T of key 16 nb + 4 gq + r, row `row`; blocks 2 ks and 2 ks + 1
+    // form the 32-key B operand of step ks
+    V8 bS[2];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      float dsv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (live[nb]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = St[nb][r] * p.scale_log2 - lse2;
+          asm("" : "+v"(x));
+          const bool vis = (unsigned)(tq - 16 * nb - r) <= trange && 16 * nb + 4 * gq + r < kvn;
+          dsv[r] = fast_exp2(vis ? x : -INFINITY) * (dPt[nb][r] - del);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bS[nb >> 1][(nb & 1) * 4 + r] = Elem<T>::from_float(dsv[r]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (!live[2 * ks] && !live[2 * ks + 1]) continue;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dQt[db] = mfma16(trpair(&cK[32 * ks * D + tr_off[db]], &cK[(32 * ks + 16) * D + tr_off[db]]), bS[ks],
+                         dQt[db]);
+    }
+    if (n + 1 < nv) store_kv(buf ^ 1);
+    __syncthreads();  // buffer buf is free; the next one is staged
+  }
+
+  // dQ = scale * dS K; lane holds d = 16 db + 4 gq + r of row `row`.  Rows
+  // past the sequence and q-tiles no kv-tile visits store zeros.
+  if (row < s.cap_q) {
+    T* dqr = static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, h, row) + 4 * gq;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      T x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = Elem<T>::from_float(p.scale * dQt[db][r]);
+      *reinterpret_cast<u32x2*>(dqr + 16 * db) = __builtin_bit_cast(u32x2, x);
     }
   }
 }
@@ -599,6 +778,21 @@ hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t st) {
   if (a.p.n_kv_tiles == 0) return hipSuccess;
   if (a.dtype == 0) return a.p.D == 64 ? main_td<__bf16, 64>(a, st) : main_td<__bf16, 128>(a, st);
   return a.p.D == 64 ? main_td<_Float16, 64>(a, st) : main_td<_Float16, 128>(a, st);
+}
+
+template <typename T>
+static hipError_t dq_t(const BwdArgs& a, hipStream_t st) {
+  const int n = a.p.B * a.p.Hq * a.p.n_q_tiles;
+  if (a.p.D == 64)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, 64>), dim3(n), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, 128>), dim3(n), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
+  if (a.p.n_q_tiles == 0) return hipSuccess;
+  return a.dtype == 0 ? dq_t<__bf16>(a, st) : dq_t<_Float16>(a, st);
 }
 
 template <typename T>

@@ -41,6 +41,7 @@ struct Problem {
   int n_kv_tiles;             // ceil(seq_kv / kTile)
   // streaming main kernel (see bwd_stream): kv-step width, kv-steps per
   // chunk and chunks per sequence; stream == 0 selects the per-tile kernel
+  int split_dq;  // general path, unordered mode: dQ by its own q-major pass
   int stream;
   int step_kv;
   int chunk;

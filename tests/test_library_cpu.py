@@ -87,12 +87,15 @@ def test_run_validates_workspace_and_tensors_before_touching_a_device(lib):
     assert b"256-byte" in lib.sdpa_last_error()
 
 
-def test_workspace_size_formula(lib):
-    plan = api.sdpa_bwd_plan(_desc(B=2, Hq=4, Hkv=2, D=64, Sq=300, Skv=300))
+@pytest.mark.parametrize("det", [False, True])
+def test_workspace_size_formula(lib, det):
+    # delta, fp32 dQ partials (relay only: the unordered general path computes
+    # dQ in its own q-major pass), relay counters, control words, dSink partials
+    plan = api.sdpa_bwd_plan(_desc(B=2, Hq=4, Hkv=2, D=64, Sq=300, Skv=300, deterministic=int(det)))
     rows = 2 * 4 * 300
     ntq = 5
     expect = 0
-    for nbytes in (4 * rows, 4 * rows * 64, 4 * 2 * 4 * ntq, 16, 4 * 4 * 2 * ntq):
+    for nbytes in (4 * rows, 4 * rows * 64 if det else 0, 4 * 2 * 4 * ntq, 16, 4 * 4 * 2 * ntq):
         expect = (expect + nbytes + 255) // 256 * 256
     assert plan.workspace_bytes == expect
 
