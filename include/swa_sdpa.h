@@ -61,9 +61,11 @@ typedef enum sdpa_layout { SDPA_LAYOUT_BHSD = 0, SDPA_LAYOUT_THD = 1 } sdpa_layo
  *
  * Mask ([PR866] commit message): query row i of a sequence has the anchor
  * a(i) = i (top-left) or i + s_kv - s_q (bottom-right), in-sequence indices.
- * Key j is visible when j < s_kv, i < s_q, j <= a(i) if causal, and
- * a(i) - j <= window_left if window_left >= 0 (an inclusive left window of
- * window_left + 1 keys).  With a sink ([PR557] Summary) the per-query-head
+ * Key j is visible when j < s_kv, i < s_q, j <= a(i) + window_right if
+ * causal, and a(i) - j <= window_left if window_left >= 0 (an inclusive left
+ * window of window_left + 1 keys).  window_right is the right-band widening
+ * of [PR557] (Summary), which names it without a formula; it is read here
+ * as an inclusive right bound, 0 giving the plain causal mask.  With a sink ([PR557] Summary) the per-query-head
  * logit sink[h] (not multiplied by scale) joins each row's softmax
  * denominator.  GQA / MQA ([PR557] Summary): query head h reads kv head
  * h / (heads_q / heads_kv).
@@ -82,6 +84,8 @@ typedef struct sdpa_attn_desc {
   int32_t causal;       /* 1: mask keys after the anchor                     */
   int32_t bottom_right; /* 1: anchor i + s_kv - s_q; 0: anchor i             */
   int32_t window_left;  /* -1: none; >= 0: inclusive left window W           */
+  int32_t window_right; /* >= 0, causal only: keys up to a(i) + window_right
+                           are visible (0: plain causal)                      */
   float scale;          /* softmax scale on Q.K (> 0), e.g. 1/sqrt(D)        */
   int32_t deterministic; /* backward dQ: 1 ordered relay (bitwise repeatable),
                             0 unordered fp32 atomics                         */

@@ -44,6 +44,7 @@ class _Problem(ctypes.Structure):
         ("causal", ctypes.c_int),
         ("bottom_right", ctypes.c_int),
         ("window_left", ctypes.c_int),
+        ("window_right", ctypes.c_int),
         ("dense", ctypes.c_int),
         ("has_sink", ctypes.c_int),
         ("scale", ctypes.c_double),
@@ -128,11 +129,12 @@ class Problem:
     dense_scan: bool = False
     q_numel: int = 0
     kv_numel: int = 0
+    window_right: int = 0  # causal only: inclusive right band (0: plain causal)
     _keep: list = field(default_factory=list, repr=False)
 
     @staticmethod
     def dense(B, Hq, Hkv, Sq, Skv, D, *, causal=True, bottom_right=False, window_left=-1,
-              scale=None, has_sink=False, len_q=None, len_kv=None) -> "Problem":
+              window_right=0, scale=None, has_sink=False, len_q=None, len_kv=None) -> "Problem":
         """Contiguous ``[B, H, S, D]`` tensors; ``len_q`` / ``len_kv`` (int
         sequences or tensors of length B) give valid lengths, default S."""
         lq = torch.full((B,), Sq, dtype=torch.int32) if len_q is None else torch.as_tensor(len_q, dtype=torch.int32).clone()
@@ -142,11 +144,12 @@ class Problem:
                        torch.arange(B, dtype=torch.int64) * (Hkv * Skv),
                        Sq * D, D, Skv * D, D, Sq, causal, bottom_right, window_left,
                        (D ** -0.5) if scale is None else float(scale), has_sink,
-                       q_numel=B * Hq * Sq * D, kv_numel=B * Hkv * Skv * D)
+                       q_numel=B * Hq * Sq * D, kv_numel=B * Hkv * Skv * D, window_right=window_right)
 
     @staticmethod
     def packed(Hq, Hkv, D, cu_q, cu_kv, len_q, len_kv, total_q, total_kv, *, causal=True,
-               bottom_right=False, window_left=-1, scale=None, has_sink=False) -> "Problem":
+               bottom_right=False, window_left=-1, window_right=0, scale=None,
+               has_sink=False) -> "Problem":
         """Contiguous ``[T, H, D]`` tensors; sequence b starts at row
         ``cu_q[b]`` and has ``len_q[b]`` valid rows (similarly for kv)."""
         cu_q = torch.as_tensor(cu_q, dtype=torch.int64)
@@ -158,7 +161,8 @@ class Problem:
         return Problem(B, Hq, Hkv, D, lq, lk, cu_q[:B].clone(), cu_kv[:B].clone(),
                        D, Hq * D, D, Hkv * D, max(stat_ld, 1), causal, bottom_right,
                        window_left, (D ** -0.5) if scale is None else float(scale), has_sink,
-                       q_numel=int(total_q) * Hq * D, kv_numel=int(total_kv) * Hkv * D)
+                       q_numel=int(total_q) * Hq * D, kv_numel=int(total_kv) * Hkv * D,
+                       window_right=window_right)
 
     def _c(self, dtype_code: int) -> _Problem:
         self._keep = [self.len_q.contiguous(), self.len_kv.contiguous(),
@@ -166,7 +170,7 @@ class Problem:
         lq, lk, rq, rk = self._keep
         return _Problem(dtype_code, self.batch, self.heads_q, self.heads_kv, self.head_dim,
                         int(self.causal), int(self.bottom_right), int(self.window_left),
-                        int(self.dense_scan), int(self.has_sink), float(self.scale),
+                        int(self.window_right), int(self.dense_scan), int(self.has_sink), float(self.scale),
                         lq.data_ptr(), lk.data_ptr(), rq.data_ptr(), rk.data_ptr(),
                         self.q_stride_h, self.q_stride_r, self.kv_stride_h, self.kv_stride_r,
                         self.stat_ld)

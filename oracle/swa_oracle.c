@@ -74,7 +74,9 @@ static int kv_head_of(const oracle_problem* p, int h) {
  * in-sequence indices of the row's own sequence.  Key j is visible from row
  * i when both lie inside their sequences' valid lengths, j <= anchor(i) if
  * causal, and anchor(i) - j <= window_left if a window is set (inclusive:
- * window_left + 1 keys including the diagonal). */
+ * window_left + 1 keys including the diagonal).  Right-band widening
+ * ([PR557] Summary names it, without a formula) moves the causal bound to
+ * j <= anchor(i) + window_right, read as inclusive like the left window. */
 static long anchor_of(const oracle_problem* p, int b, int i) {
 #if ORACLE_MUTANT == 6
   return p->bottom_right ? (long)i + p->len_q[b] - p->len_kv[b] : (long)i;
@@ -86,7 +88,11 @@ static long anchor_of(const oracle_problem* p, int b, int i) {
 static int visible(const oracle_problem* p, int b, int i, int j) {
   if (i < 0 || i >= p->len_q[b] || j < 0 || j >= p->len_kv[b]) return 0;
   long a = anchor_of(p, b, i);
-  if (p->causal && j > a) return 0;
+#if ORACLE_MUTANT == 9
+  if (p->causal && j - a >= (p->window_right > 0 ? p->window_right : 1)) return 0;
+#else
+  if (p->causal && j > a + p->window_right) return 0;
+#endif
 #if ORACLE_MUTANT == 2
   if (p->window_left >= 0 && a - j >= p->window_left) return 0;
 #else
@@ -106,7 +112,7 @@ static void key_range(const oracle_problem* p, int b, int i, int* lo, int* hi) {
   long a = anchor_of(p, b, i);
   long l = 0, r = p->len_kv[b] - 1;
   if (p->window_left >= 0 && a - p->window_left > l) l = a - p->window_left;
-  if (p->causal && a < r) r = a;
+  if (p->causal && a + p->window_right < r) r = a + p->window_right;
   *lo = (int)l;
   *hi = (int)r;
 }

@@ -46,6 +46,8 @@ typedef struct oracle_problem {
   int causal;           /* 1: keys right of the anchor are masked            */
   int bottom_right;     /* 1: anchor(i) = i + len_kv - len_q, else i         */
   int window_left;      /* < 0: no window; else keep anchor - j <= window    */
+  int window_right;     /* causal only, >= 0: keep j - anchor <= window_right
+                           (right-band widening; 0 is plain causal)          */
   int dense;            /* 1: scan every key and test the mask (slow check)  */
   int has_sink;         /* sink[h_q]: an extra logit in each row's softmax   */
   double scale;         /* multiplies <Q_i, K_j>; the sink is not scaled     */

@@ -2,6 +2,7 @@
 // launch sequence of the forward and the backward.  Host code only.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -40,6 +41,12 @@ sdpa_status fail(sdpa_status st, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// A window (left) or band (right) of at least s_q + s_kv keys masks nothing
+// that a shorter one of that length would not; negative stays negative.
+int clamp_band(int w, int64_t sq, int64_t skv) {
+  return w < 0 ? w : (int)std::min<int64_t>(w, sq + skv);
+}
+
 sdpa_status check_strides(const char* name, const int64_t* st, const sdpa_attn_desc* d) {
   const int first = d->layout == SDPA_LAYOUT_THD ? 1 : 0;
   for (int k = first; k < 3; ++k) {
@@ -73,6 +80,9 @@ sdpa_status check_desc(const sdpa_attn_desc* d, bool backward) {
   if (d->bottom_right != 0 && d->bottom_right != 1)
     return fail(SDPA_ERR_INVALID_ARG, "bottom_right %d is not 0/1", d->bottom_right);
   if (d->window_left < -1) return fail(SDPA_ERR_INVALID_ARG, "window_left %d < -1", d->window_left);
+  if (d->window_right < 0) return fail(SDPA_ERR_INVALID_ARG, "window_right %d < 0", d->window_right);
+  if (d->window_right > 0 && !d->causal)
+    return fail(SDPA_ERR_INVALID_ARG, "window_right %d widens the causal band and needs causal = 1", d->window_right);
   if (!(d->scale > 0.f) || !std::isfinite(d->scale))
     return fail(SDPA_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)d->scale);
   if (d->deterministic != 0 && d->deterministic != 1)
@@ -118,7 +128,10 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   p.total_kv = d->layout == SDPA_LAYOUT_THD ? d->total_kv : (int64_t)d->batch * d->seq_kv;
   p.causal = d->causal;
   p.bottom_right = d->bottom_right;
-  p.window = d->window_left;
+  // A band wider than both sequences together masks nothing more; clamping
+  // keeps the schedule's integer arithmetic far from overflow.
+  p.window = clamp_band(d->window_left, d->seq_q, d->seq_kv);
+  p.right = d->causal ? clamp_band(d->window_right, d->seq_q, d->seq_kv) : 0;
   p.scale = d->scale;
   p.scale_log2 = d->scale * swa::kLog2e;
   p.has_sink = d->has_sink;
@@ -141,8 +154,8 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   bool small_rows = true;
   for (const int64_t rs : {p.sq[2], p.sk[2], p.sv[2], p.sdo[2], p.sdq[2], p.sdk[2], p.sdv[2]})
     small_rows &= rs > 0 && rs <= INT32_MAX;
-  p.stream = p.G == 1 && d->causal && d->window_left >= 0 && d->window_left <= 128 && d->head_dim == 64 &&
-             small_rows;
+  p.stream = p.G == 1 && d->causal && p.right == 0 && d->window_left >= 0 && d->window_left <= 128 &&
+             d->head_dim == 64 && small_rows;
   p.step_kv = p.stream ? 128 : kTile;
   // The per-tile kernel in unordered mode leaves dQ to a q-major pass (no
   // fp32 accumulator); in deterministic mode dQ goes through the relay.
@@ -331,7 +344,8 @@ sdpa_status sdpa_bwd_schedule(const sdpa_bwd_plan_t* pl, int32_t len_q, int32_t 
   if (len_q < 0 || len_kv < 0) return fail(SDPA_ERR_INVALID_ARG, "len_q %d / len_kv %d must be >= 0", len_q, len_kv);
   swa::SeqSched g;
   const int tkv = pl->prob.step_kv;
-  g.init(len_q, len_kv, pl->desc.bottom_right, pl->desc.causal, pl->desc.window_left, kTile, tkv);
+  g.init(len_q, len_kv, pl->desc.bottom_right, pl->desc.causal, clamp_band(pl->desc.window_left, len_q, len_kv),
+         clamp_band(pl->desc.window_right, len_q, len_kv), kTile, tkv);
   if (tile_q) *tile_q = kTile;
   if (tile_kv) *tile_kv = tkv;
   if (n_q) *n_q = g.n_q_tiles;

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
   const int kv0 = jt * kTile;
   if (kv0 >= s.cap_kv) return;
   SeqSched g;
-  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, kTile);
+  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, p.right, kTile, kTile);
   const int qlo = g.q_lo(jt), nit = g.n_iters(jt);
   const int nvisit = nit * p.G;
 
@@ -300,10 +300,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
   for (int e = 0; e < 8; ++e) zero8[e] = Elem<T>::from_float(0.f);
 
   // Mask: with t = row + diag - key, an element is visible iff
-  // tlo <= t <= thi (tlo = 0 if causal, thi = W if windowed; otherwise far
+  // tlo <= t <= thi (tlo = -R if causal, thi = W if windowed; otherwise far
   // out of reach).  A key past the sequence is pushed below tlo through its
   // lane term, and rows past the sequence carry LSE = +inf.
-  const int tlo = p.causal ? 0 : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
+  const int tlo = p.causal ? -p.right : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
   const unsigned trange = (unsigned)(thi - tlo);
   const int key = kv0 + 16 * w + c;
   const int tkey = key < s.len_kv ? g.diag - key - tlo : -(1 << 30);  // t - tlo = row + tkey
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int q0 = i * kTile;
   if (q0 >= s.cap_q) return;
   SeqSched g;
-  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, kTile);
+  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, p.right, kTile, kTile);
   const int nv = g.n_visitors(i), jf = g.kv_first(i);  // nv > 0 implies len_q, len_kv > 0
 
   const int row = q0 + 16 * w + c;  // this lane's query row
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // Mask as in bwd_main: with t = row + diag - key, visible iff
   // 0 <= t - tlo <= trange, and the key lies inside the sequence.
-  const int tlo = p.causal ? 0 : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
+  const int tlo = p.causal ? -p.right : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
   const unsigned trange = (unsigned)(thi - tlo);
 
   f32x4 dQt[NDB];

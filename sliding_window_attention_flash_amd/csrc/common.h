@@ -29,6 +29,7 @@ struct Problem {
   int layout;
   int64_t total_q, total_kv;  // packed rows (THD)
   int causal, bottom_right, window;
+  int right;                  // causal only: inclusive right band (0: plain causal)
   float scale;                // softmax scale
   float scale_log2;           // scale * log2(e)
   int has_sink;
@@ -98,11 +99,12 @@ __device__ __forceinline__ int64_t elem_off(const Problem& p, const int64_t* st,
 }
 
 // Mask of the pages: anchor a = row (+ diag for bottom-right); key visible
-// when inside both valid lengths, key <= a if causal, a - key <= W if W >= 0.
+// when inside both valid lengths, key <= a + R if causal (R: right band,
+// 0 for plain causal), a - key <= W if W >= 0.
 __device__ __forceinline__ bool visible(const SeqSched& g, int row, int key) {
   const int a = row + g.diag;
   bool v = (row < g.len_q) & (key < g.len_kv);
-  if (g.causal) v &= key <= a;
+  if (g.causal) v &= key <= a + g.right;
   if (g.window >= 0) v &= (a - key) <= g.window;
   return v;
 }
@@ -136,7 +138,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // The schedule the main kernel runs: kv-tiles of kTile keys (per-tile
 // kernel) or kv-steps of step_kv keys (streaming kernel); q-tiles of kTile.
 __device__ __forceinline__ void main_sched(const Problem& p, const Seq& s, SeqSched& g) {
-  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, p.stream ? p.step_kv : kTile);
+  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, p.right, kTile,
+         p.stream ? p.step_kv : kTile);
 }
 
 // Streaming kernel: number of chunks (blocks) that visit q-tile i.  A q-tile

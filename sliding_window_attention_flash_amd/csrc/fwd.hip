@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int q0 = i * kTile;
   if (q0 >= s.cap_q) return;
   SeqSched g;
-  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, kTile, kTile);
+  g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, p.right, kTile, kTile);
   const int hk = h / p.G;
   const int qrow = q0 + 16 * w + c;
   const T* qp = static_cast<const T*>(a.q);

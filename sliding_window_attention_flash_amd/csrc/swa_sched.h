@@ -16,6 +16,10 @@
 //   * the ordered dQ relay counts a visitor's turn from the q-tile's first
 //     visitor kv_first = max((q_row0 + diag - W) // tile_kv, 0).
 // The window is inclusive: row i keeps keys with anchor(i) - j <= W.
+// Right-band widening (cudnn-frontend PR #557, Summary, named there without
+// a formula) is read as an inclusive right bound R on the causal mask: row i
+// keeps keys j <= anchor(i) + R, so R = 0 is plain causal; it moves the
+// causal skip q_lo and its inverse kv_last by R keys.
 #pragma once
 
 #if defined(__HIPCC__)
@@ -41,12 +45,13 @@ struct SeqSched {
   int len_q, len_kv;  // valid rows
   int diag;           // anchor offset: s_kv - s_q (bottom-right) or 0
   int tile_q, tile_kv;
-  int causal;         // 1: keys after the anchor are masked
+  int causal;         // 1: keys after anchor + right are masked
   int window;         // < 0: no window; else inclusive left window W
+  int right;          // causal only: inclusive right band R >= 0
   int n_q_tiles, n_kv_tiles;
 
-  SWA_HD void init(int lq, int lkv, int bottom_right, int causal_, int window_, int tq,
-                   int tkv) {
+  SWA_HD void init(int lq, int lkv, int bottom_right, int causal_, int window_, int right_,
+                   int tq, int tkv) {
     len_q = lq;
     len_kv = lkv;
     diag = bottom_right ? lkv - lq : 0;
@@ -54,14 +59,16 @@ struct SeqSched {
     tile_kv = tkv;
     causal = causal_;
     window = window_;
+    right = causal_ ? right_ : 0;
     n_q_tiles = lq > 0 ? ceil_div(lq, tq) : 0;
     n_kv_tiles = lkv > 0 ? ceil_div(lkv, tkv) : 0;
   }
 
-  // First q-tile that kv-tile j can feed: causal skip.
+  // First q-tile that kv-tile j can feed: causal skip (the first row whose
+  // anchor + R reaches kv-tile j's first key).
   SWA_HD int q_lo(int j) const {
     if (!causal) return 0;
-    return imax(floor_div(j * tile_kv - diag, tile_q), 0);
+    return imax(floor_div(j * tile_kv - diag - right, tile_q), 0);
   }
   // One past the last q-tile that kv-tile j can feed: window bound.
   SWA_HD int q_hi(int j) const {
@@ -80,7 +87,7 @@ struct SeqSched {
   // Last kv-tile that visits q-tile i (inverse of the q_lo clamp).
   SWA_HD int kv_last(int i) const {
     if (!causal) return n_kv_tiles - 1;
-    return imin(ceil_div((i + 1) * tile_q + diag, tile_kv) - 1, n_kv_tiles - 1);
+    return imin(ceil_div((i + 1) * tile_q + diag + right, tile_kv) - 1, n_kv_tiles - 1);
   }
   // Visitors of q-tile i form the contiguous range [kv_first, kv_last];
   // empty when i is past the valid rows or the range is inverted.

@@ -42,6 +42,7 @@ class Workload:
     causal: bool = True
     bottom_right: bool = False
     window_left: int = -1
+    window_right: int = 0  # causal only: inclusive right band (0: plain causal)
     scale: Optional[float] = None
     deterministic: bool = False
     sink: bool = False
@@ -169,15 +170,16 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0) -> dict:
 def attended_pairs_per_head(w: Workload) -> int:
     """Attended (query, key) pairs of one query head, summed over sequences,
     counted in closed form per row: the key interval of row i is
-    [max(0, a - W), min(a, s_kv - 1)] with a = i (+ s_kv - s_q if
-    bottom-right); this is workload bookkeeping for the FLOP count."""
+    [max(0, a - W), min(a + R, s_kv - 1)] with a = i (+ s_kv - s_q if
+    bottom-right) and R the right band; this is workload bookkeeping for
+    the FLOP count."""
     total = 0
     for lq, lk in zip(w.valid_len_q(), w.valid_len_kv()):
         diag = (lk - lq) if w.bottom_right else 0
         for i in range(lq):
             a = i + diag
             lo = max(0, a - w.window_left) if w.window_left >= 0 else 0
-            hi = min(a, lk - 1) if w.causal else lk - 1
+            hi = min(a + w.window_right, lk - 1) if w.causal else lk - 1
             if hi >= lo:
                 total += hi - lo + 1
     return total

@@ -26,7 +26,7 @@ def say(msg: str) -> None:
 
 def mask_kw(w: Workload) -> dict:
     return dict(causal=w.causal, bottom_right=w.bottom_right, window_left=w.window_left,
-                scale=w.softmax_scale)
+                window_right=w.window_right, scale=w.softmax_scale)
 
 
 def seq_kw(w: Workload, inp: dict) -> dict:
@@ -56,7 +56,7 @@ def gpu_backward(w: Workload, inp: dict, o, lse, deterministic=None, nan_fill=Tr
 
 def oracle_problem(w: Workload) -> oracle.Problem:
     kw = dict(causal=w.causal, bottom_right=w.bottom_right, window_left=w.window_left,
-              scale=w.softmax_scale, has_sink=w.sink)
+              window_right=w.window_right, scale=w.softmax_scale, has_sink=w.sink)
     if w.layout == "thd":
         cu_q = [0]
         for c in w.cap_q:

@@ -12,10 +12,12 @@ What pins what:
   ``scaled_dot_product_attention(is_causal=True)``: the forward softmax
   arithmetic and the causal mask;
 * closed forms: window 0 keeps only the diagonal key, constant V gives zero
-  dQ / dK, zero Q gives a uniform average;
+  dQ / dK, zero Q gives a uniform average (also over a right band);
 * invariants: dS rows sum to zero (dQ unchanged by shifting every key by one
   vector; dK sums to zero over keys), window >= S equals plain causal,
-  bottom-right equals the matching rows of a square top-left problem, GQA
+  bottom-right equals the matching rows of a square top-left problem, a
+  top-left right band R equals the bottom-right mask with s_kv - s_q = R,
+  a right band wider than the keys equals the window-only mask, GQA
   equals the group sum of the head-expanded MHA problem, keys outside every
   window get zero dK / dV, padding and packed sequences equal independent
   dense problems.
@@ -76,6 +78,11 @@ FD_CASES = [
     dict(B=1, Hq=2, Hkv=1, Sq=7, Skv=19, D=8, causal=False, bottom_right=True, window_left=3, has_sink=True),
     dict(B=2, Hq=2, Hkv=1, Sq=9, Skv=9, D=8, causal=True, bottom_right=False, window_left=2, has_sink=False,
          len_q=[9, 5], len_kv=[9, 6]),
+    # right-band widening: keys up to anchor + R
+    dict(B=1, Hq=4, Hkv=2, Sq=9, Skv=13, D=8, causal=True, bottom_right=True, window_left=3, window_right=2,
+         has_sink=True),
+    dict(B=1, Hq=2, Hkv=2, Sq=11, Skv=8, D=8, causal=True, bottom_right=False, window_left=-1, window_right=3,
+         has_sink=False),
 ]
 
 
@@ -135,13 +142,13 @@ def check_finite_differences(lib=None, cases=None):
             _close(fd_grad(p, q, k, v, dO, sink, "sink", lib), r["dsink"], 1e-7, f"case {n} dsink")
 
 
-def explicit_mask(lq, lk, causal, bottom_right, window_left):
+def explicit_mask(lq, lk, causal, bottom_right, window_left, window_right=0):
     i = torch.arange(lq)[:, None]
     j = torch.arange(lk)[None, :]
     a = i + (lk - lq if bottom_right else 0)
     m = torch.ones(lq, lk, dtype=torch.bool)
     if causal:
-        m &= j <= a
+        m &= j <= a + window_right
     if window_left >= 0:
         m &= (a - j) <= window_left
     return m
@@ -159,7 +166,7 @@ def torch_reference(p: Problem, q, k, v, dO, sink, layout="dense"):
     loss = 0.0
     for b in range(p.batch):
         lq, lk = int(p.len_q[b]), int(p.len_kv[b])
-        m = explicit_mask(lq, lk, p.causal, p.bottom_right, p.window_left)
+        m = explicit_mask(lq, lk, p.causal, p.bottom_right, p.window_left, p.window_right)
         for h in range(p.heads_q):
             if layout == "dense":
                 qb, kb, vb, dob = q[b, h, :lq], k[b, h // G, :lk], v[b, h // G, :lk], dO[b, h, :lq]
@@ -222,6 +229,21 @@ def check_torch_sdpa_causal(lib=None):
     rw = oracle.backward(pw, q, k, v, dO, None, lib=lib)
     for key in ("o", "dq", "dk", "dv"):
         assert torch.equal(rw[key], r[key]), f"window >= S differs from causal in {key}"
+    # a right band reaching past every key is the window-only (non-causal) mask
+    for wl in (-1, 5):
+        pn = Problem.dense(2, 3, 3, 29, 29, 16, scale=0.4, causal=False, window_left=wl)
+        pr = Problem.dense(2, 3, 3, 29, 29, 16, scale=0.4, causal=True, window_left=wl, window_right=28)
+        rn = oracle.backward(pn, q, k, v, dO, None, lib=lib)
+        rr = oracle.backward(pr, q, k, v, dO, None, lib=lib)
+        for key in ("o", "dq", "dk", "dv"):
+            assert torch.equal(rr[key], rn[key]), f"right band >= S differs from window-only in {key}"
+        if wl < 0:  # no window, no causal bound: torch's unmasked SDPA
+            qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+            o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=0.4)
+            (o * dO).sum().backward()
+            _close(rr["o"], o.detach(), 1e-12, "unmasked sdpa O")
+            _close(rr["dq"], qq.grad, 1e-12, "unmasked sdpa dQ")
+            _close(rr["dk"], kk.grad, 1e-12, "unmasked sdpa dK")
 
 
 def check_closed_forms(lib=None):
@@ -257,6 +279,17 @@ def check_closed_forms(lib=None):
         lo = max(0, i - 3)
         _close(o[0, 0, i], v[0, 0, lo:i + 1].mean(0), 1e-14, f"Q=0 row {i}")
         assert abs(float(lse[0, 0, i]) - math.log(i + 1 - lo)) < 1e-14, f"Q=0 LSE row {i}"
+    # Q = 0 with a right band R and left window W: row i averages keys
+    # [i - W, i + R] clipped to the sequence (R + W + 1 keys inside it).
+    for W, R in ((0, 2), (1, 3)):
+        p, q, k, v, dO, _ = dense_case(1, 1, 1, 10, 12, 8, 44, scale=0.5, causal=True, window_left=W,
+                                       window_right=R)
+        q = torch.zeros_like(q)
+        o, lse = oracle.forward(p, q, k, v, None, lib=lib)
+        for i in range(10):
+            lo, hi = max(0, i - W), min(11, i + R)
+            _close(o[0, 0, i], v[0, 0, lo:hi + 1].mean(0), 1e-14, f"Q=0 band W={W} R={R} row {i}")
+            assert abs(float(lse[0, 0, i]) - math.log(hi + 1 - lo)) < 1e-14, f"Q=0 band LSE row {i}"
 
 
 def check_invariants(lib=None):
@@ -302,6 +335,16 @@ def check_invariants(lib=None):
     ot, lset = oracle.forward(pt, qt, k, v, None, lib=lib)
     _close(ro, ot[:, :, 9:], 1e-14, "BR vs shifted TL: O")
     _close(lse, lset[:, :, 9:], 1e-14, "BR vs shifted TL: LSE")
+    # a top-left right band R is the bottom-right mask of a problem with
+    # s_kv - s_q = R (anchor i + R), its left window moved by R as well.
+    p, q, k, v, dO, sink = dense_case(2, 4, 2, 9, 14, 8, 59, scale=0.6, causal=True, window_left=2,
+                                      window_right=5, has_sink=True)
+    r = oracle.backward(p, q, k, v, dO, sink, lib=lib)
+    pb = Problem.dense(2, 4, 2, 9, 14, 8, scale=0.6, causal=True, bottom_right=True, window_left=7,
+                       has_sink=True)
+    rb = oracle.backward(pb, q, k, v, dO, sink, lib=lib)
+    for key in ("o", "lse", "dq", "dk", "dv", "dsink"):
+        _close(r[key], rb[key], 1e-14, f"TL right band vs BR: {key}")
     # keys outside every window (BR, s_q < s_kv - W): exact zero dK / dV.
     p, q, k, v, dO, _ = dense_case(1, 2, 1, 5, 20, 8, 56, scale=0.6, causal=True,
                                    bottom_right=True, window_left=3)

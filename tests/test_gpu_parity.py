@@ -39,6 +39,13 @@ SMALL = [
     _wl("stream_padded_w61", F16, 2, 2, 2, 64, 640, 700, bottom_right=True, window_left=61,
         pad_len_q=(640, 333), pad_len_kv=(700, 500)),
     _wl("stream_sink_w96_s1500", BF16, 1, 2, 2, 64, 1500, 1500, window_left=96, sink=True),
+    # right-band widening: keys up to anchor + R
+    _wl("rband_tl_w40_r24_d64", BF16, 2, 4, 4, 64, 300, 300, window_left=40, window_right=24),
+    _wl("rband_gqa_br_w100_r70_d128_sink", BF16, 2, 8, 2, 128, 200, 333, bottom_right=True, window_left=100,
+        window_right=70, sink=True),
+    _wl("rband_nowin_r64_sq_gt_skv_f16", F16, 1, 4, 2, 64, 260, 190, window_right=64),
+    _wl("rband_mha_s2048_w128_r64", BF16, 1, 4, 4, 64, 2048, 2048, window_left=128, window_right=64,
+        scale=0.125),
 ]
 
 
@@ -51,21 +58,21 @@ def test_small_full_oracle(w, det):
     compare_full(w, inp, out)
 
 
-def _thd_small(sink=True, dtype=F16, D=64, hkv=2):
+def _thd_small(sink=True, dtype=F16, D=64, hkv=2, wr=0):
     # one sequence with no query rows and one with no keys, slots padded
     lq = (70, 0, 130, 5, 64, 600)
     lk = (300, 40, 130, 0, 200, 900)
     cq = (128, 64, 192, 64, 64, 640)
     ck = (300, 64, 150, 16, 200, 901)
-    return Workload(f"thd_small_sink{int(sink)}_d{D}_hkv{hkv}", dtype, 6, 8, hkv, D, max(cq), max(ck),
-                    bottom_right=True, window_left=90, sink=sink, layout="thd",
+    return Workload(f"thd_small_sink{int(sink)}_d{D}_hkv{hkv}_r{wr}", dtype, 6, 8, hkv, D, max(cq), max(ck),
+                    bottom_right=True, window_left=90, window_right=wr, sink=sink, layout="thd",
                     len_q=lq, len_kv=lk, cap_q=cq, cap_kv=ck)
 
 
 @pytest.mark.parametrize("det", [False, True], ids=["atomic", "relay"])
-@pytest.mark.parametrize("D,hkv", [(64, 2), (128, 2), (64, 8)])
-def test_thd_padded_with_sinks(det, D, hkv):
-    w = _thd_small(D=D, hkv=hkv)
+@pytest.mark.parametrize("D,hkv,wr", [(64, 2, 0), (128, 2, 0), (64, 8, 0), (64, 2, 50)])
+def test_thd_padded_with_sinks(det, D, hkv, wr):
+    w = _thd_small(D=D, hkv=hkv, wr=wr)
     say(f"case {w.name} det={det}")
     inp, out, _ = run_gpu(w, seed=5, deterministic=det)
     compare_full(w, inp, out)

@@ -36,7 +36,8 @@ def _desc(**kw):
     q = torch.empty(g.batch, g.heads_q, g.seq_q, g.head_dim, dtype=torch.bfloat16)
     k = torch.empty(g.batch, g.heads_kv, g.seq_kv, g.head_dim, dtype=torch.bfloat16)
     d = api.make_desc(g, torch.bfloat16, q=q, k=k, v=k, o=q, dO=q, dq=q, dk=k, dv=k,
-                      window_left=kw.pop("window_left", 64), bottom_right=kw.pop("bottom_right", False))
+                      window_left=kw.pop("window_left", 64), window_right=kw.pop("window_right", 0),
+                      bottom_right=kw.pop("bottom_right", False))
     for key, val in kw.items():
         setattr(d, key, val)
     return d
@@ -50,12 +51,20 @@ def _desc(**kw):
     ("scale", 0.0, _lib.SDPA_ERR_INVALID_ARG, "scale"),
     ("batch", 0, _lib.SDPA_ERR_INVALID_ARG, "batch"),
     ("deterministic", 2, _lib.SDPA_ERR_INVALID_ARG, "deterministic"),
+    ("window_right", -1, _lib.SDPA_ERR_INVALID_ARG, "window_right"),
 ])
 def test_plan_rejects_bad_descriptors(lib, field, value, status, needle):
     d = _desc(**{field: value})
     with pytest.raises(_lib.SdpaError) as e:
         api.sdpa_bwd_plan(d)
     assert e.value.status == status and needle in str(e.value)
+
+
+def test_plan_rejects_right_band_without_causal(lib):
+    d = _desc(window_right=8)
+    d.causal = 0
+    with pytest.raises(_lib.SdpaError, match="needs causal"):
+        api.sdpa_bwd_plan(d)
 
 
 def test_plan_rejects_bottom_right_with_more_queries_than_keys(lib):
@@ -105,29 +114,33 @@ def test_workspace_size_formula(lib, det):
 
 def _schedule_cases():
     g = torch.Generator().manual_seed(17)
-    cases = [(256, 256, 64, False, True), (32768 // 64, 32768 // 64, 128, False, True),
-             (100, 1000, 50, True, True), (260, 130, 40, False, True), (190, 190, -1, False, True),
-             (100, 250, 50, True, False), (150, 170, -1, False, False), (16484 % 997, 16484 % 997, 96, True, True),
-             (1, 1, 0, False, True), (0, 5, 3, False, True), (5, 0, 3, True, True)]
+    cases = [(256, 256, 64, False, True, 0), (32768 // 64, 32768 // 64, 128, False, True, 0),
+             (100, 1000, 50, True, True, 0), (260, 130, 40, False, True, 0), (190, 190, -1, False, True, 0),
+             (100, 250, 50, True, False, 0), (150, 170, -1, False, False, 0),
+             (16484 % 997, 16484 % 997, 96, True, True, 0), (1, 1, 0, False, True, 0), (0, 5, 3, False, True, 0),
+             (5, 0, 3, True, True, 0), (300, 300, 64, False, True, 70), (200, 333, 100, True, True, 1),
+             (190, 190, -1, False, True, 64), (128, 128, 0, False, True, 1000)]
     for _ in range(60):
         lq, lk = (int(x) for x in torch.randint(0, 400, (2,), generator=g))
         w = int(torch.randint(-1, 300, (1,), generator=g))
         br = bool(torch.randint(0, 2, (1,), generator=g))
         causal = bool(torch.randint(0, 3, (1,), generator=g))  # mostly causal
-        cases.append((lq, lk, w, br, causal))
+        wr = int(torch.randint(0, 150, (1,), generator=g)) if causal and torch.rand(1, generator=g) < 0.3 else 0
+        cases.append((lq, lk, w, br, causal, wr))
     return cases
 
 
 @pytest.mark.parametrize("mha", [False, True], ids=["gqa_tiles", "mha"])
-@pytest.mark.parametrize("lq,lk,w,br,causal", _schedule_cases())
-def test_schedule_covers_the_mask_exactly(lib, lq, lk, w, br, causal, mha):
-    # multi-head causal plans with a window <= 128 schedule 128-key kv-steps
-    d = _desc(window_left=w, bottom_right=br, Hkv=4 if mha else 2)
+@pytest.mark.parametrize("lq,lk,w,br,causal,wr", _schedule_cases())
+def test_schedule_covers_the_mask_exactly(lib, lq, lk, w, br, causal, wr, mha):
+    # multi-head causal plans with a window <= 128 (and no right band)
+    # schedule 128-key kv-steps
+    d = _desc(window_left=w, window_right=wr, bottom_right=br, Hkv=4 if mha else 2)
     d.causal = int(causal)
     plan = api.sdpa_bwd_plan(d)
     s = api.sdpa_bwd_schedule(plan, lq, lk)
     Tq, Tk = s["tile_q"], s["tile_kv"]
-    m = oc.explicit_mask(lq, lk, causal, br, w) if lq and lk else torch.zeros(lq, lk, dtype=torch.bool)
+    m = oc.explicit_mask(lq, lk, causal, br, w, wr) if lq and lk else torch.zeros(lq, lk, dtype=torch.bool)
     nq, nk = s["n_q"], s["n_kv"]
     assert nq == -(-lq // Tq) and nk == -(-lk // Tk)
     # tile-level visibility from brute force
@@ -153,7 +166,7 @@ def test_schedule_covers_the_mask_exactly(lib, lq, lk, w, br, causal, mha):
         if hi > lo and vis[:, j].any():
             first = int(torch.nonzero(vis[:, j])[0])
             last = int(torch.nonzero(vis[:, j])[-1])
-            r_lo = j * Tk - diag
+            r_lo = j * Tk - diag - wr
             if causal and 0 <= r_lo < lq:
                 assert lo == first
             r_hi = j * Tk + Tk - 1 + w - diag
@@ -209,9 +222,11 @@ def simulate_relay(s, kv_first=None, timeout_s=2.0):
 
 
 @pytest.mark.parametrize("mha", [False, True])
-@pytest.mark.parametrize("lq,lk,w,br", [(640, 640, 128, False), (300, 700, 100, True), (500, 500, 0, False)])
-def test_relay_simulation_orders_every_q_tile(lib, lq, lk, w, br, mha):
-    plan = api.sdpa_bwd_plan(_desc(window_left=w, bottom_right=br, Hkv=4 if mha else 2))
+@pytest.mark.parametrize("lq,lk,w,br,wr", [(640, 640, 128, False, 0), (300, 700, 100, True, 0),
+                                           (500, 500, 0, False, 0), (500, 500, 40, False, 90),
+                                           (300, 700, 100, True, 33)])
+def test_relay_simulation_orders_every_q_tile(lib, lq, lk, w, br, wr, mha):
+    plan = api.sdpa_bwd_plan(_desc(window_left=w, window_right=wr, bottom_right=br, Hkv=4 if mha else 2))
     s = api.sdpa_bwd_schedule(plan, lq, lk)
     log, expired = simulate_relay(s)
     assert not expired

@@ -54,8 +54,10 @@ def test_attended_pairs_brute_force(oracle_lib):
         w = int(torch.randint(-1, 12, (1,), generator=g))
         causal = bool(torch.randint(0, 2, (1,), generator=g))
         br = bool(torch.randint(0, 2, (1,), generator=g))
-        m = oc.explicit_mask(sq, skv, causal, br, w)
-        p = Problem.dense(1, 1, 1, sq, skv, 8, causal=causal, bottom_right=br, window_left=w)
+        wr = int(torch.randint(0, 6, (1,), generator=g)) if causal else 0
+        m = oc.explicit_mask(sq, skv, causal, br, w, wr)
+        p = Problem.dense(1, 1, 1, sq, skv, 8, causal=causal, bottom_right=br, window_left=w,
+                          window_right=wr)
         assert oracle.attended_pairs(p) == int(m.sum())
 
 
@@ -68,6 +70,7 @@ MUTANTS = {
     6: "bottom-right anchor shifted the wrong way",
     7: "dSink sign flipped",
     8: "GQA head map h % H_kv instead of h / G",
+    9: "exclusive right band (j - anchor < R)",
 }
 
 
