@@ -160,6 +160,15 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   // The per-tile kernel in unordered mode leaves dQ to a q-major pass (no
   // fp32 accumulator); in deterministic mode dQ goes through the relay.
   p.split_dq = !p.stream && !d->deterministic;
+  // A block of the dQ pass walks several q-tiles when each has few visiting
+  // kv-tiles (a narrow window), so its start-up latency is paid once per
+  // run; with many visitors one q-tile per block keeps the grid large.
+  {
+    const int64_t band = (d->window_left >= 0 ? (int64_t)d->window_left : (int64_t)d->seq_kv) +
+                         (d->causal ? (int64_t)d->window_right : (int64_t)d->seq_kv);
+    const int64_t visitors = (band + 2 * kTile - 1) / kTile;
+    p.dq_tiles = visitors <= 8 ? 4 : 1;
+  }
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one
     // block per MI355X CU, never shorter than 2 steps (so a q-tile has at

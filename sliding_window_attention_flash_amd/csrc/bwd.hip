@@ -519,23 +519,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // bwd_dq: q-tile-stationary dQ pass of the unordered mode, one block (4
-// waves) per (q-tile i of 64 rows, query head, sequence); two blocks per CU.
+// waves) per (run of p.dq_tiles consecutive q-tiles, query head, sequence);
+// two blocks per CU.
 //
-// Each wave owns 16 query rows; a lane keeps its row's Q and dO slices (the
-// B operands below), LSE and delta in registers.  For every kv-tile j in
-// [kv_first(i), kv_last(i)] (K and V staged in LDS, double-buffered, the
-// next tile loaded into registers while the current one computes):
+// Each wave owns 16 query rows of the current q-tile i; a lane keeps its
+// row's Q and dO slices (the B operands below), LSE and delta in registers.
+// For every kv-tile j in [kv_first(i), kv_last(i)]:
 //   S^T = K Q^T,  dP^T = V dO^T       A: K / V rows (LDS), B: Q / dO
 //   P^T = exp2(S^T c - LSE),  dS^T = P^T (dP^T - delta)        (fp32, masked)
 //   dQ^T += K^T dS^T                   A: transposed reads of the K tile,
 //                                      B: dS^T straight from the accumulator
+// The block walks the (q-tile, kv-tile) pairs of its run as one pipeline:
+// K and V are double-buffered in LDS and the next pair's tiles load into
+// registers while the current pair computes, also across a q-tile boundary,
+// where the next q-tile's Q / dO rows are prefetched the same way.  Short
+// visitor ranges (a narrow window) then pay no per-q-tile start-up latency.
 // Every dQ row is produced by one wave and leaves as 16-bit values once, so
 // no fp32 accumulator or conversion pass exists.  The transposed orientation
 // leaves each lane with 4 consecutive head-dim values of one row: one 8-byte
 // store per 16 columns.  A wave skips the 16-key blocks its rows cannot see.
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+// Occupancy: two blocks per CU, four for single-tile blocks at D = 64, whose
+// registers fit in 128 per lane.
+template <typename T, int D, bool RUN>
+__global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_kernel(BwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
   constexpr int NS = D / 32;   // k-steps over the head dim
   constexpr int NDB = D / 16;  // 16-column blocks of the head dim
@@ -550,43 +557,79 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // block -> (sequence, kv head, q-tile, head within the group): the heads
-  // that share a kv head, and neighbouring q-tiles, read the same K / V
+  // block -> (sequence, kv head, run of q-tiles, head within the group): the
+  // heads that share a kv head, and neighbouring runs, read the same K / V
   // tiles and run next to each other on one XCD
+  const int nruns = (p.n_q_tiles + p.dq_tiles - 1) / p.dq_tiles;
   int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = L % p.G;
   L /= p.G;
-  const int i = L % p.n_q_tiles;
-  L /= p.n_q_tiles;
+  const int run = L % nruns;
+  L /= nruns;
   const int hk = L % p.Hkv, b = L / p.Hkv, h = hk * p.G + hg;
   const Seq s = load_seq(p, b);
-  const int q0 = i * kTile;
-  if (q0 >= s.cap_q) return;
+  const int ia = run * p.dq_tiles;
+  const int ib = min(ia + p.dq_tiles, (s.cap_q + kTile - 1) / kTile);  // q-tiles holding slot rows
+  if (ia >= ib) return;
   SeqSched g;
   g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, p.right, kTile, kTile);
-  const int nv = g.n_visitors(i), jf = g.kv_first(i);  // nv > 0 implies len_q, len_kv > 0
 
-  const int row = q0 + 16 * w + c;  // this lane's query row
-  V8 qB[NS], oB[NS];
-  float lse2 = INFINITY, del = 0.f;  // padding rows: P = exp2(-inf) = 0
-  if (nv > 0) {
+  T* dqp = static_cast<T*>(a.dq);
+  // dQ = scale * dS K; lane holds d = 16 db + 4 gq + r of row 16 w + c of
+  // q-tile i.  Rows past the slot are not stored.
+  auto store_dq = [&](int i, const f32x4* v) {
+    const int row = i * kTile + 16 * w + c;
+    if (row >= s.cap_q) return;
+    T* dqr = dqp + elem_off(p, p.sdq, b, s.row0_q, h, row) + 4 * gq;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      T x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = Elem<T>::from_float(p.scale * v[db][r]);
+      *reinterpret_cast<u32x2*>(dqr + 16 * db) = __builtin_bit_cast(u32x2, x);
+    }
+  };
+  f32x4 dQt[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dQt[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // q-tiles no kv-tile visits (rows past the sequence, or out of every
+  // window) get zeros
+  for (int i = ia; i < ib; ++i)
+    if (g.n_visitors(i) == 0) store_dq(i, dQt);
+  auto next_visited = [&](int i) {
+    while (i < ib && g.n_visitors(i) == 0) ++i;
+    return i;
+  };
+  int ci = next_visited(ia);  // current pair (ci, cj)
+  if (ci >= ib) return;
+  int cj = g.kv_first(ci);
+
+  // Q / dO rows and row statistics of a visited q-tile (len_q > 0); rows
+  // past the sequence repeat its last row and carry LSE = +inf, so that
+  // P = exp2(-inf) = 0
+  V8 qB[NS], oB[NS], nqB[NS], noB[NS];
+  float lse2, del, nlse2 = 0.f, ndel = 0.f;
+  auto load_q = [&](int i, V8* qv, V8* ov, float& l2, float& dl) {
+    const int row = i * kTile + 16 * w + c;
     const int qr = min(row, s.len_q - 1);
     const T* qrow = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, qr) + 8 * gq;
     const T* orow = static_cast<const T*>(a.dO) + elem_off(p, p.sdo, b, s.row0_q, h, qr) + 8 * gq;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      qB[st] = ld8(qrow + 32 * st);
-      oB[st] = ld8(orow + 32 * st);
+      qv[st] = ld8(qrow + 32 * st);
+      ov[st] = ld8(orow + 32 * st);
     }
+    l2 = INFINITY;
+    dl = 0.f;
     if (row < s.len_q) {
       const int64_t si = s.stat0 + h * s.stat_hs + row;
-      lse2 = a.lse[si] * kLog2e;
-      del = a.delta[si];
+      l2 = a.lse[si] * kLog2e;
+      dl = a.delta[si];
     }
-  }
+  };
 
-  // K / V staging; rows past the sequence repeat its last key (finite
-  // values; the mask gives them zero weight)
+  // K / V staging (a visited kv-tile: len_kv > 0); rows past the sequence
+  // repeat its last key (finite values; the mask gives them zero weight)
   const T* kp = static_cast<const T*>(a.k);
   const T* vp = static_cast<const T*>(a.v);
   V8 rk[NPASS], rv[NPASS];
@@ -619,23 +662,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int tlo = p.causal ? -p.right : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
   const unsigned trange = (unsigned)(thi - tlo);
 
-  f32x4 dQt[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) dQt[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (nv > 0) {
-    load_kv(jf);
-    store_kv(0);
-  }
+  load_q(ci, qB, oB, lse2, del);
+  load_kv(cj);
+  store_kv(0);
   __syncthreads();
-  for (int n = 0; n < nv; ++n) {
-    const int kv0 = (jf + n) * kTile, buf = n & 1;
-    if (n + 1 < nv) load_kv(jf + n + 1);
+  for (int n = 0;; ++n) {
+    // the pair after (ci, cj): the next kv-tile of ci, else the first of
+    // the next visited q-tile of the run
+    int ni = ci, nj = cj + 1;
+    if (nj > g.kv_last(ci)) {
+      ni = RUN ? next_visited(ci + 1) : ib;
+      nj = ni < ib ? g.kv_first(ni) : 0;
+    }
+    const bool more = ni < ib;
+    if (more) {
+      load_kv(nj);
+      if (RUN && ni != ci) load_q(ni, nqB, noB, nlse2, ndel);
+    }
+    const int buf = n & 1;
     const T* cK = sK[buf];
     const T* cV = sV[buf];
-    const int kvn = s.len_kv - kv0;                      // keys of this tile inside the sequence
-    const int u0 = q0 + 16 * w + g.diag - tlo - kv0;     // t - tlo at (row q0 + 16 w, key kv0)
-    const int tq = u0 + c - 4 * gq;                      // t - tlo at (row, key kv0 + 4 gq), minus 16 nb + r
+    const int kv0 = cj * kTile;
+    const int kvn = s.len_kv - kv0;                               // keys of this tile inside the sequence
+    const int u0 = ci * kTile + 16 * w + g.diag - tlo - kv0;      // t - tlo at (row 16 w, key kv0)
+    const int tq = u0 + c - 4 * gq;                               // t - tlo at (row, key kv0 + 4 gq), minus 16 nb + r
 
     f32x4 St[4], dPt[4];
     bool live[4];
@@ -651,8 +701,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[st]]), oB[st], dPt[nb]);
       }
     }
-    // dS^T of key 16 nb + 4 gq + r, row `row`; blocks 2 ks and 2 ks + 1
-    // form the 32-key B operand of step ks
+    // dS^T of key 16 nb + 4 gq + r; blocks 2 ks and 2 ks + 1 form the
+    // 32-key B operand of step ks
     V8 bS[2];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
@@ -677,21 +727,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         dQt[db] = mfma16(trpair(&cK[32 * ks * D + tr_off[db]], &cK[(32 * ks + 16) * D + tr_off[db]]), bS[ks],
                          dQt[db]);
     }
-    if (n + 1 < nv) store_kv(buf ^ 1);
-    __syncthreads();  // buffer buf is free; the next one is staged
-  }
-
-  // dQ = scale * dS K; lane holds d = 16 db + 4 gq + r of row `row`.  Rows
-  // past the sequence and q-tiles no kv-tile visits store zeros.
-  if (row < s.cap_q) {
-    T* dqr = static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, h, row) + 4 * gq;
+    if (ni != ci) {  // q-tile ci is complete
+      store_dq(ci, dQt);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      T x[4];
+      for (int db = 0; db < NDB; ++db) dQt[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (RUN && more) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = Elem<T>::from_float(p.scale * dQt[db][r]);
-      *reinterpret_cast<u32x2*>(dqr + 16 * db) = __builtin_bit_cast(u32x2, x);
+        for (int st = 0; st < NS; ++st) {
+          qB[st] = nqB[st];
+          oB[st] = noB[st];
+        }
+        lse2 = nlse2;
+        del = ndel;
+      }
     }
+    if (!more) break;
+    store_kv(buf ^ 1);
+    __syncthreads();  // buffer buf is free; the next one is staged
+    ci = ni;
+    cj = nj;
   }
 }
 
@@ -782,11 +836,19 @@ hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t st) {
 
 template <typename T>
 static hipError_t dq_t(const BwdArgs& a, hipStream_t st) {
-  const int n = a.p.B * a.p.Hq * a.p.n_q_tiles;
-  if (a.p.D == 64)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, 64>), dim3(n), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, 128>), dim3(n), dim3(kThreads), 0, st, a);
+  const int n = a.p.B * a.p.Hq * ((a.p.n_q_tiles + a.p.dq_tiles - 1) / a.p.dq_tiles);
+  const bool run = a.p.dq_tiles > 1;
+  if (a.p.D == 64) {
+    if (run)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 64, true>), dim3(n), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 64, false>), dim3(n), dim3(kThreads), 0, st, a);
+  } else {
+    if (run)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 128, true>), dim3(n), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 128, false>), dim3(n), dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -43,6 +43,7 @@ struct Problem {
   // streaming main kernel (see bwd_stream): kv-step width, kv-steps per
   // chunk and chunks per sequence; stream == 0 selects the per-tile kernel
   int split_dq;  // general path, unordered mode: dQ by its own q-major pass
+  int dq_tiles;  // consecutive q-tiles one block of that pass walks
   int stream;
   int step_kv;
   int chunk;
