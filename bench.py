@@ -1,25 +1,30 @@
 """Benchmark of the sliding-window attention backward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c3|c3_atomic|c2_4k|c2_8k]
+    python bench.py [--steps K] [--warmup W] [--workload c3|c3_atomic|c1|c2_4k|c2_8k|c4|c4_f16|c5]
     python bench.py --copy-calibration ...      (appends a copy of known size)
     python bench.py --summarize-stats DIR --out FILE --command CMD
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --out FILE --command CMD
 
 A step is one full backward, sdpa_bwd_run: the dot preprocess, the main
-window-bounded kernel with its dQ accumulation (ordered relay or fp32
-atomics), the dQ conversion (atomic mode) and dSink (with sinks), on inputs
-already resident in HBM.  The default workload is the long-sequence one the
-target names: batch 2, 16 heads, head_dim 64, S = 32768, causal top-left with
-a left window of 128, bf16, deterministic relay.  Prints one JSON line.
+window-bounded kernel with its dQ accumulation (ordered relay, fp32 atomics
+at the streaming kernel's chunk boundaries, or the separate q-major dQ
+pass), the dQ conversion where an accumulator is used, and dSink (with
+sinks), on inputs already resident in HBM.  The default workload is the
+long-sequence shape of the pages' measurements: batch 2, 16 heads,
+head_dim 64, S = 32768, causal top-left with a left window of 128, bf16,
+deterministic relay.  Prints one JSON line; ``extra`` carries the other
+workloads and the forward's time per call for each.
 
 FLOPs count attended (query, key) pairs only: 10 * head_dim per pair per
-query head.  The roofline entry is for the dominant kernel (bwd_main), timed
-with HIP events recorded on its launch stream around every launch.  Its
-``traffic`` is the HBM bytes per launch that rocprofv3's FETCH_SIZE and
-WRITE_SIZE counters read for it, each divided by what the same counter reads
-per byte for an elementwise copy of known size; the figures are kept in a
-text summary under profiles/ together with a hash of the kernel's sources,
-and ``traffic`` is null when the sources no longer match.
+query head for the backward, 4 * head_dim for the forward.  The roofline
+entry is for the dominant kernel (the streaming main kernel at the default
+workload), timed with HIP events recorded on its launch stream around every
+launch.  Its ``traffic`` is the HBM bytes per launch that rocprofv3's
+FETCH_SIZE and WRITE_SIZE counters read for it, each divided by what the
+same counter reads per byte for an elementwise copy of known size; the
+figures are kept in a text summary under profiles/ together with a hash of
+the kernel's sources, and ``traffic`` is null when the sources no longer
+match.
 """
 from __future__ import annotations
 
@@ -87,18 +92,23 @@ def main_kernel_bytes(w) -> int:
     return rows_q * (3 * w.head_dim * 2 + 8) + rows_kv * (4 * w.head_dim * 2)
 
 
-def time_backward(w, steps, warmup, seed=0):
+def time_backward(w, steps, warmup, seed=0, forward=False):
+    """Per-step wall time of the backward (ms), the average of the main
+    kernel's HIP-event times (ms), the relay expiries, and with forward=True
+    also the forward's wall time per call (ms)."""
     import torch
     from sliding_window_attention_flash_amd import api
     from sliding_window_attention_flash_amd.synth import make_inputs
 
     inp = make_inputs(w, device="cuda", seed=seed)
     mk = dict(causal=w.causal, bottom_right=w.bottom_right, window_left=w.window_left,
-              scale=w.softmax_scale, cu_seqlens_q=inp["cu_seqlens_q"], cu_seqlens_kv=inp["cu_seqlens_kv"],
+              window_right=w.window_right, scale=w.softmax_scale, cu_seqlens_q=inp["cu_seqlens_q"],
+              cu_seqlens_kv=inp["cu_seqlens_kv"],
               seq_lens_q=inp["seq_lens_q"], seq_lens_kv=inp["seq_lens_kv"])
     if w.layout == "thd":
         mk.update(max_seqlen_q=w.seq_q, max_seqlen_kv=w.seq_kv)
-    o, lse = api.forward(inp["q"], inp["k"], inp["v"], sink=inp["sink"], **mk)
+    fw = api.Forward(inp["q"], inp["k"], inp["v"], sink=inp["sink"], **mk)
+    o, lse = fw.run()
     bw = api.Backward(inp["q"], inp["k"], inp["v"], o, inp["dO"], lse, deterministic=w.deterministic,
                       sink=inp["sink"], **mk)
     hip = _hip()
@@ -123,7 +133,17 @@ def time_backward(w, steps, warmup, seed=0):
     for e in ev:
         hip.hipEventDestroy(e)
     expiries = bw.relay_expiries() if w.deterministic else 0
-    return wall * 1e3, sum(main_ms) / len(main_ms), expiries
+    if not forward:
+        return wall * 1e3, sum(main_ms) / len(main_ms), expiries
+    for _ in range(max(3, warmup // 5)):
+        fw.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fw.run()
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t0) / steps * 1e3
+    return wall * 1e3, sum(main_ms) / len(main_ms), expiries, fwd_ms
 
 
 def kernel_source_hash() -> str:
@@ -308,7 +328,7 @@ def main():
         sys.exit(1)
     wl = workloads()
     w = wl[args.workload]
-    ms, main_ms, exp = time_backward(w, args.steps, args.warmup)
+    ms, main_ms, exp, fwd_ms = time_backward(w, args.steps, args.warmup, forward=True)
     fl = flops(w)
     tflops = fl / (ms * 1e-3) / 1e12
     nbytes = main_kernel_bytes(w)
@@ -317,7 +337,8 @@ def main():
              "main_kernel_algorithmic_bytes": nbytes,
              "main_kernel_attended_tflops": fl / (main_ms * 1e-3) / 1e12,
              "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS, "relay_expiries": exp,
-             "attended_flops": fl}
+             "attended_flops": fl, "forward_ms": fwd_ms,
+             "forward_tflops": 0.4 * fl / (fwd_ms * 1e-3) / 1e12}
     if not args.no_extra:
         # every other workload, timed the same way (the large GQA one with
         # fewer steps); each entry names its workload's shape
@@ -327,9 +348,10 @@ def main():
             wx = wl[name]
             big = wx.batch * wx.heads_q * wx.seq_q * wx.head_dim > (1 << 30)
             st, wu = (max(3, args.steps // 4), max(3, args.warmup // 10)) if big else (max(5, args.steps // 2), args.warmup)
-            m2, mm2, _ = time_backward(wx, st, wu)
+            m2, mm2, _, fm2 = time_backward(wx, st, wu, forward=True)
             extra[name] = {"workload": wx.name, "ms": m2, "tflops": flops(wx) / (m2 * 1e-3) / 1e12, "main_ms": mm2,
-                           "frac_bf16_mfma_peak": flops(wx) / (m2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+                           "frac_bf16_mfma_peak": flops(wx) / (m2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                           "forward_ms": fm2, "forward_tflops": 0.4 * flops(wx) / (fm2 * 1e-3) / 1e12}
     line = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",

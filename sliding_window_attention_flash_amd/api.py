@@ -186,25 +186,34 @@ def lse_shape(g: Geometry):
     return (g.batch, g.heads_q, g.seq_q)
 
 
-def forward(q, k, v, *, causal=True, bottom_right=False, window_left=-1, window_right=0, scale=None,
-            sink=None,
-            cu_seqlens_q=None, cu_seqlens_kv=None, seq_lens_q=None, seq_lens_kv=None,
-            max_seqlen_q=None, max_seqlen_kv=None, stream=None):
-    """Window-trimmed forward: returns (O like q, LSE fp32)."""
-    g = geometry(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_kv)
-    o = torch.empty_like(q)
-    lse = torch.empty(lse_shape(g), dtype=torch.float32, device=q.device)
-    has_lens = seq_lens_q is not None
-    desc = make_desc(g, q.dtype, causal=causal, bottom_right=bottom_right, window_left=window_left,
-                     window_right=window_right, scale=scale, has_sink=sink is not None,
-                     has_seq_lens=has_lens,
-                     q=q, k=k, v=v, o=o)
-    plan = sdpa_fwd_plan(desc)
-    t = FwdTensors(q=_p(q), k=_p(k), v=_p(v), sink=_p(sink), cu_seqlens_q=_p(cu_seqlens_q),
-                   cu_seqlens_kv=_p(cu_seqlens_kv), seq_lens_q=_p(seq_lens_q),
-                   seq_lens_kv=_p(seq_lens_kv), o=_p(o), lse=_p(lse))
-    sdpa_fwd_run(plan, t, None, stream)
-    return o, lse
+class Forward:
+    """A planned forward bound to fixed tensors (O and LSE are allocated
+    here unless given)."""
+
+    def __init__(self, q, k, v, *, causal=True, bottom_right=False, window_left=-1, window_right=0,
+                 scale=None, sink=None, cu_seqlens_q=None, cu_seqlens_kv=None, seq_lens_q=None,
+                 seq_lens_kv=None, max_seqlen_q=None, max_seqlen_kv=None, o=None, lse=None):
+        g = geometry(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_kv)
+        self.o = torch.empty_like(q) if o is None else o
+        self.lse = torch.empty(lse_shape(g), dtype=torch.float32, device=q.device) if lse is None else lse
+        desc = make_desc(g, q.dtype, causal=causal, bottom_right=bottom_right, window_left=window_left,
+                         window_right=window_right, scale=scale, has_sink=sink is not None,
+                         has_seq_lens=seq_lens_q is not None, q=q, k=k, v=v, o=self.o)
+        self.plan = sdpa_fwd_plan(desc)
+        self._keep = (q, k, v, sink, cu_seqlens_q, cu_seqlens_kv, seq_lens_q, seq_lens_kv)
+        self.tensors = FwdTensors(q=_p(q), k=_p(k), v=_p(v), sink=_p(sink), cu_seqlens_q=_p(cu_seqlens_q),
+                                  cu_seqlens_kv=_p(cu_seqlens_kv), seq_lens_q=_p(seq_lens_q),
+                                  seq_lens_kv=_p(seq_lens_kv), o=_p(self.o), lse=_p(self.lse))
+
+    def run(self, stream=None):
+        sdpa_fwd_run(self.plan, self.tensors, None, stream)
+        return self.o, self.lse
+
+
+def forward(q, k, v, *, stream=None, **kw):
+    """Window-trimmed forward: returns (O like q, LSE fp32).  Keywords as
+    for ``Forward``."""
+    return Forward(q, k, v, **kw).run(stream)
 
 
 class Backward:

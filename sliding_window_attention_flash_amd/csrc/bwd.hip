@@ -17,34 +17,9 @@
 // per-sequence lengths and dSink.  The kernel design itself is written for
 // CDNA4 and is not taken from those pages.
 #include "kernels.h"
+#include "tiles.h"
 
 namespace swa {
-
-// ---------------------------------------------------------------------------
-// helpers
-
-// Loads 8 contiguous 16-bit elements (16 bytes) from global memory.
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::vec8 ld8(const T* p) {
-  return *reinterpret_cast<const typename Elem<T>::vec8*>(p);
-}
-template <typename T>
-__device__ __forceinline__ void st8(T* p, const typename Elem<T>::vec8& v) {
-  *reinterpret_cast<typename Elem<T>::vec8*>(p) = v;
-}
-
-// Two 4-element runs (8 bytes each) from LDS at p and p + 16 elements,
-// as one 8-element MFMA operand.  This is the operand layout that pairs with
-// an accumulator tile used as the other operand (rows 4g..4g+3 of two
-// stacked 16-row blocks).
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::vec8 lds_pair4(const T* p) {
-  typedef typename Elem<T>::vec8 V8;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
-  u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(V8, r);
-}
 
 // ---- ordered dQ relay ------------------------------------------------------
 // One q-tile's fp32 partial is touched only through agent-scope atomics: the
@@ -83,15 +58,6 @@ __device__ __forceinline__ void relay_release(int* semp, int turn, int nv, int t
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0 && nv > 1) __hip_atomic_store(semp, turn + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Blocks are dealt to the 8 XCDs round-robin; renumber them so that each XCD
-// runs one contiguous range of logical tiles (neighbouring kv-tiles of one
-// head then share that XCD's L2).
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int base = n >> 3, extra = n & 7;
-  return xcd * base + (xcd < extra ? xcd : extra) + slot;
 }
 
 // ---------------------------------------------------------------------------
@@ -210,38 +176,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
 // next visit's Q / dO tile is loaded into registers while the current one
 // computes.  All products are 16x16x32 MFMAs with fp32 accumulation.
 //
-// Tiles are row-major with the 16-byte chunks of row r permuted by XOR with
-// (r mod 8) (64-wide rows) or 2 (r mod 8) (128-wide rows, moving whole
-// 32-byte pairs): the 8 rows a half-wave's transposed read touches then
-// fall on disjoint banks.
-
-namespace {
-
-template <int D>
-__device__ __forceinline__ int tsw(int r) { return D == 64 ? (r & 7) : ((r & 7) << 1); }
-// element offset of (row r, 16-byte chunk ch) in a D-wide swizzled tile
-template <int D>
-__device__ __forceinline__ int toff(int r, int ch) { return r * D + ((ch ^ tsw<D>(r)) << 3); }
-// lane offset of a transposed read: row 4 g + c / 4, column 16 cb + 4 (c % 4)
-template <int D>
-__device__ __forceinline__ int troff(int c, int g, int cb) {
-  const int r = 4 * g + (c >> 2);
-  return r * D + (((2 * cb + ((c & 3) >> 1)) ^ tsw<D>(r)) << 3) + 4 * (c & 1);
-}
-typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
-template <typename T>
-__device__ __forceinline__ u32x2 ldtr(const T* p) {
-  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
-// 8 contraction values for lane (c, g): e < 4 from the read at p0, e >= 4 from p1
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::vec8 trpair(const T* p0, const T* p1) {
-  const u32x2 lo = ldtr(p0), hi = ldtr(p1);
-  return __builtin_bit_cast(typename Elem<T>::vec8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
-}  // namespace
+// Q / dO / K tiles use the swizzled layout of tiles.h.
 
 template <typename T, int D, bool RELAY>
 __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {

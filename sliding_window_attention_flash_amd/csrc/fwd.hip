@@ -8,171 +8,247 @@
 // Sinks: cudnn-frontend PR #557 "... sink-token gradients ...", Summary: the
 // per-head sink logit joins each row's softmax denominator.
 //
-// One block (4 waves) per (q-tile of 64 rows, query head, sequence); each
-// wave owns 16 query rows, kept in registers as the B operand of
-// S^T = K Q^T (keys on the MFMA rows, queries on the columns).  The online
-// softmax runs per column; O^T += V^T P^T takes P^T straight from the
-// accumulator.  Accumulation in fp32, exp2 with log2(e) folded into the
-// scale.
+// One block (4 waves) per (run of p.dq_tiles consecutive q-tiles, query
+// head, sequence); each wave owns 16 query rows of the current q-tile, kept
+// in registers as the B operand of S^T = K Q^T (keys on the MFMA rows,
+// queries on the columns).  The online softmax runs per column (one query
+// row per lane column, its 16 keys spread over 4 lanes x 4 registers).
+// O^T += V^T P^T takes V^T from transposed reads of the V tile and P^T
+// straight from the accumulator, so each lane ends with 4 consecutive
+// head-dim values of one row and O leaves as 8-byte stores.  K and V are
+// double-buffered in swizzled LDS and the next pair's tiles (and, across a
+// q-tile boundary, the next q-tile's rows) load while the current pair
+// computes.  Accumulation in fp32, exp2 with log2(e) folded into the scale;
+// a wave skips the 16-key blocks its rows cannot see.
 #include "kernels.h"
+#include "tiles.h"
 
 namespace swa {
 
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::vec8 fld8(const T* p) {
-  return *reinterpret_cast<const typename Elem<T>::vec8*>(p);
-}
-
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::vec8 flds_pair4(const T* p) {
-  typedef typename Elem<T>::vec8 V8;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
-  u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(V8, r);
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+template <typename T, int D, bool RUN>
+__global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kernel(FwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
   constexpr int NS = D / 32, NDB = D / 16;
-  constexpr int LDR = D + 8, LDT = kTile + 8;
   constexpr int CH = D / 8, RPP = kThreads / CH, NPASS = kTile / RPP;
-  __shared__ __align__(16) T sK[kTile * LDR];
-  __shared__ __align__(16) T sVt[D * LDT];
+  __shared__ __align__(16) T sK[2][kTile * D];
+  __shared__ __align__(16) T sV[2][kTile * D];
 
   const Problem& p = a.p;
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, c = l & 15, gq = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // block -> (sequence, kv head, run of q-tiles, head within the group)
+  const int nruns = (p.n_q_tiles + p.dq_tiles - 1) / p.dq_tiles;
+  int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int hg = L % p.G;
+  L /= p.G;
+  const int run = L % nruns;
+  L /= nruns;
+  const int hk = L % p.Hkv, b = L / p.Hkv, h = hk * p.G + hg;
   const Seq s = load_seq(p, b);
-  const int q0 = i * kTile;
-  if (q0 >= s.cap_q) return;
+  const int ia = run * p.dq_tiles;
+  const int ib = min(ia + p.dq_tiles, (s.cap_q + kTile - 1) / kTile);  // q-tiles holding slot rows
+  if (ia >= ib) return;
   SeqSched g;
   g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, p.right, kTile, kTile);
-  const int hk = h / p.G;
-  const int qrow = q0 + 16 * w + c;
-  const T* qp = static_cast<const T*>(a.q);
-  const T* kp = static_cast<const T*>(a.k);
-  const T* vp = static_cast<const T*>(a.v);
 
-  V8 zero8;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) zero8[e] = Elem<T>::from_float(0.f);
-  V8 qB[NS];
-  {
-    const bool ok = qrow < s.len_q;
-    const int64_t qo = elem_off(p, p.sq, b, s.row0_q, h, ok ? qrow : 0);
-#pragma unroll
-    for (int st = 0; st < NS; ++st) qB[st] = ok ? fld8(qp + qo + 32 * st + 8 * gq) : zero8;
-  }
-
-  float m = -INFINITY, lsum = 0.f;  // running max (log2 units) and sum
-  if (p.has_sink) {
-    m = a.sink[h] * kLog2e;
-    lsum = 1.f;
-  }
+  // running max (log2 units) and denominator of this lane's row; the sink
+  // starts them at exp2(sink - m) = 1
+  const float m0 = p.has_sink ? a.sink[h] * kLog2e : -INFINITY;
+  const float l0 = p.has_sink ? 1.f : 0.f;
+  float m = m0, lsum = l0;
   f32x4 O[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int jlo = g.kv_first(i), nv = g.n_visitors(i);
-  for (int jt = jlo; jt < jlo + nv; ++jt) {
-    const int kv0 = jt * kTile;
-    __syncthreads();
+  // O = O^T / denominator and LSE of row 16 w + c of q-tile i; a row past
+  // the sequence, or with neither a visible key nor a sink, gets O = 0 and
+  // LSE = -inf.  Rows past the slot are not stored.
+  T* op = static_cast<T*>(a.o);
+  auto finish = [&](int i) {
+    const int row = i * kTile + 16 * w + c;
+    if (row >= s.cap_q) return;
+    const bool live = row < s.len_q && lsum > 0.f;
+    const float inv = live ? 1.f / lsum : 0.f;
+    T* orow = op + elem_off(p, p.so, b, s.row0_q, h, row) + 4 * gq;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      T ox[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ox[r] = Elem<T>::from_float(O[db][r] * inv);
+      *reinterpret_cast<u32x2*>(orow + 16 * db) = __builtin_bit_cast(u32x2, ox);
+    }
+    if (gq == 0) a.lse[s.stat0 + h * s.stat_hs + row] = live ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+  };
+  // q-tiles no kv-tile visits
+  for (int i = ia; i < ib; ++i)
+    if (g.n_visitors(i) == 0) finish(i);
+  auto next_visited = [&](int i) {
+    while (i < ib && g.n_visitors(i) == 0) ++i;
+    return i;
+  };
+  int ci = next_visited(ia);  // current pair (ci, cj)
+  if (ci >= ib) return;
+  int cj = g.kv_first(ci);
+
+  // Q rows of a visited q-tile (len_q > 0); rows past the sequence repeat
+  // its last row and are dropped at the end
+  V8 qB[NS], nqB[NS];
+  auto load_q = [&](int i, V8* qv) {
+    const int qr = min(i * kTile + 16 * w + c, s.len_q - 1);
+    const T* qrow = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, qr) + 8 * gq;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) qv[st] = ld8(qrow + 32 * st);
+  };
+  // K / V staging (a visited kv-tile: len_kv > 0); rows past the sequence
+  // repeat its last key (finite values; the mask gives them zero weight)
+  const T* kp = static_cast<const T*>(a.k);
+  const T* vp = static_cast<const T*>(a.v);
+  V8 rk[NPASS], rv[NPASS];
+  auto load_kv = [&](int j) {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = tid / CH + ps * RPP, ch = tid % CH, kk = kv0 + r;
-      V8 kx = zero8, vx = zero8;
-      if (kk < s.len_kv) {
-        kx = fld8(kp + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch);
-        vx = fld8(vp + elem_off(p, p.sv, b, s.row0_kv, hk, kk) + 8 * ch);
-      }
-      *reinterpret_cast<V8*>(&sK[r * LDR + 8 * ch]) = kx;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sVt[(8 * ch + e) * LDT + r] = vx[e];
+      const int kk = min(j * kTile + tid / CH + ps * RPP, s.len_kv - 1), ch = tid % CH;
+      rk[ps] = ld8(kp + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch);
+      rv[ps] = ld8(vp + elem_off(p, p.sv, b, s.row0_kv, hk, kk) + 8 * ch);
     }
-    __syncthreads();
+  };
+  auto store_kv = [&](int buf) {
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int r = tid / CH + ps * RPP, ch = tid % CH;
+      *reinterpret_cast<V8*>(&sK[buf][toff<D>(r, ch)]) = rk[ps];
+      *reinterpret_cast<V8*>(&sV[buf][toff<D>(r, ch)]) = rv[ps];
+    }
+  };
+
+  int rd_off[NS], tr_off[NDB];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) rd_off[st] = toff<D>(c, 4 * st + gq);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) tr_off[db] = troff<D>(c, gq, db);
+
+  // Mask: with t = row + diag - key, visible iff 0 <= t - tlo <= trange
+  // (tlo = -R if causal, thi = W if windowed), and the key lies inside the
+  // sequence.
+  const int tlo = p.causal ? -p.right : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
+  const unsigned trange = (unsigned)(thi - tlo);
+
+  load_q(ci, qB);
+  load_kv(cj);
+  store_kv(0);
+  __syncthreads();
+  for (int n = 0;; ++n) {
+    int ni = ci, nj = cj + 1;
+    if (nj > g.kv_last(ci)) {
+      ni = RUN ? next_visited(ci + 1) : ib;
+      nj = ni < ib ? g.kv_first(ni) : 0;
+    }
+    const bool more = ni < ib;
+    if (more) {
+      load_kv(nj);
+      if (RUN && ni != ci) load_q(ni, nqB);
+    }
+    const int buf = n & 1;
+    const T* cK = sK[buf];
+    const T* cV = sV[buf];
+    const int kv0 = cj * kTile;
+    const int kvn = s.len_kv - kv0;                           // keys of this tile inside the sequence
+    const int u0 = ci * kTile + 16 * w + g.diag - tlo - kv0;  // t - tlo at (row 16 w, key kv0)
+    const int tq = u0 + c - 4 * gq;                           // t - tlo at (row, key kv0 + 4 gq), minus 16 nb + r
 
     f32x4 St[4];
+    bool live[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      St[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 4; ++nb) {
+      St[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int um = u0 - 16 * nb;  // the block spans t - tlo in [um - 15, um + 15]
+      live[nb] = um + 15 >= 0 && um - 15 <= (int)trange && 16 * nb < kvn;
+      if (!live[nb]) continue;
 #pragma unroll
       for (int st = 0; st < NS; ++st)
-        St[mb] = mfma16(*reinterpret_cast<const V8*>(&sK[(16 * mb + c) * LDR + 32 * st + 8 * gq]),
-                        qB[st], St[mb]);
+        St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[st]]), qB[st], St[nb]);
     }
-    float x[16];
+    // masked logits (log2 units) and the tile's row max over the 4 lanes
+    // sharing a column
+    float x[4][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kv0 + 16 * mb + 4 * gq + r;
-        const float t = visible(g, qrow, key) ? St[mb][r] * p.scale_log2 : -INFINITY;
-        x[4 * mb + r] = t;
-        mx = fmaxf(mx, t);
+        float v = St[nb][r] * p.scale_log2;
+        asm("" : "+v"(v));
+        const bool vis = live[nb] && (unsigned)(tq - 16 * nb - r) <= trange && 16 * nb + 4 * gq + r < kvn;
+        x[nb][r] = vis ? v : -INFINITY;
+        mx = fmaxf(mx, x[nb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx);
-    V8 pB[2];
+    const float mref = mnew == -INFINITY ? 0.f : mnew;  // a row with nothing yet keeps zeros
+    const float alpha = fast_exp2(m - mref);
+    V8 bP[2];
     float rs = 0.f;
-    if (mnew == -INFINITY) {
-      pB[0] = zero8;
-      pB[1] = zero8;
-    } else {
-      const float alpha = fast_exp2(m - mnew);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = fast_exp2(x[4 * mb + r] - mnew);
-          rs += pv;
-          pB[mb >> 1][(mb & 1) * 4 + r] = Elem<T>::from_float(pv);
-        }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      lsum = lsum * alpha + rs;
+      for (int r = 0; r < 4; ++r) {
+        const float pv = fast_exp2(x[nb][r] - mref);
+        rs += pv;
+        bP[nb >> 1][(nb & 1) * 4 + r] = Elem<T>::from_float(pv);
+      }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    lsum = lsum * alpha + rs;
+    m = mnew;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) O[db] *= alpha;
-      m = mnew;
+    for (int db = 0; db < NDB; ++db) O[db] *= alpha;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (!live[2 * ks] && !live[2 * ks + 1]) continue;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        O[db] = mfma16(trpair(&cV[32 * ks * D + tr_off[db]], &cV[(32 * ks + 16) * D + tr_off[db]]), bP[ks], O[db]);
     }
+    if (ni != ci) {  // q-tile ci is complete
+      finish(ci);
+      m = m0;
+      lsum = l0;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (RUN && more) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        O[db] = mfma16(flds_pair4(&sVt[(16 * db + c) * LDT + 32 * s2 + 4 * gq]), pB[s2], O[db]);
+        for (int st = 0; st < NS; ++st) qB[st] = nqB[st];
+      }
+    }
+    if (!more) break;
+    store_kv(buf ^ 1);
+    __syncthreads();  // buffer buf is free; the next one is staged
+    ci = ni;
+    cj = nj;
   }
-
-  if (qrow >= s.cap_q) return;
-  const bool live = qrow < s.len_q && lsum > 0.f;
-  const float inv = live ? 1.f / lsum : 0.f;
-  T* op = static_cast<T*>(a.o) + elem_off(p, p.so, b, s.row0_q, h, qrow);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    T ox[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ox[r] = Elem<T>::from_float(O[db][r] * inv);
-    *reinterpret_cast<u32x2*>(op + 16 * db + 4 * gq) = __builtin_bit_cast(u32x2, ox);
-  }
-  if (gq == 0)
-    a.lse[s.stat0 + h * s.stat_hs + qrow] = live ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-template <typename T>
-static hipError_t fwd_t(const FwdArgs& a, hipStream_t st) {
-  dim3 grid(a.p.n_q_tiles, a.p.Hq, a.p.B);
-  if (a.p.D == 64)
-    hipLaunchKernelGGL((fwd_kernel<T, 64>), grid, dim3(kThreads), 0, st, a);
+template <typename T, int D>
+static void fwd_td(const FwdArgs& a, hipStream_t st) {
+  const int n = a.p.B * a.p.Hq * ((a.p.n_q_tiles + a.p.dq_tiles - 1) / a.p.dq_tiles);
+  if (a.p.dq_tiles > 1)
+    hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3(n), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, 128>), grid, dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+    hipLaunchKernelGGL((fwd_kernel<T, D, false>), dim3(n), dim3(kThreads), 0, st, a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   if (a.p.n_q_tiles == 0) return hipSuccess;
-  return a.dtype == 0 ? fwd_t<__bf16>(a, st) : fwd_t<_Float16>(a, st);
+  if (a.dtype == 0) {
+    if (a.p.D == 64) fwd_td<__bf16, 64>(a, st);
+    else fwd_td<__bf16, 128>(a, st);
+  } else {
+    if (a.p.D == 64) fwd_td<_Float16, 64>(a, st);
+    else fwd_td<_Float16, 128>(a, st);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace swa

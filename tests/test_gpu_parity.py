@@ -46,6 +46,10 @@ SMALL = [
     _wl("rband_nowin_r64_sq_gt_skv_f16", F16, 1, 4, 2, 64, 260, 190, window_right=64),
     _wl("rband_mha_s2048_w128_r64", BF16, 1, 4, 4, 64, 2048, 2048, window_left=128, window_right=64,
         scale=0.125),
+    # narrow window, GQA: the dQ pass walks runs of q-tiles; rows past
+    # s_kv + W see no key, so a run ends in q-tiles no kv-tile visits
+    _wl("gqa_tl_sq_gt_skv_w40_runs", BF16, 2, 4, 2, 64, 520, 130, window_left=40),
+    _wl("gqa_br_w60_d128_runs_f16", F16, 1, 6, 2, 128, 700, 900, bottom_right=True, window_left=60),
 ]
 
 
