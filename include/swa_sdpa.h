@@ -91,6 +91,10 @@ typedef struct sdpa_attn_desc {
                             0 unordered fp32 atomics                         */
   int32_t has_sink;     /* 1: sink logits given (fp32 [heads_q])             */
   int32_t has_seq_lens; /* 1: seq_lens_q / seq_lens_kv given (THD requires)  */
+  int32_t q_run_tiles;  /* 0: the measured default; 1..16: consecutive 64-row
+                           q-tiles one block of the q-major passes (forward,
+                           unordered dQ of the per-tile path) walks; for
+                           tuning studies                                     */
   /* Element strides (batch, head, row) of each tensor; the head_dim axis is
    * contiguous.  THD ignores the batch entry (rows are tokens).  Rows and
    * base pointers must be 16-byte aligned. */

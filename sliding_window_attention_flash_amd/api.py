@@ -162,7 +162,7 @@ def geometry(q, k, cu_seqlens_q=None, max_seqlen_q=None, max_seqlen_kv=None) -> 
 
 
 def make_desc(g: Geometry, dtype, *, causal=True, bottom_right=False, window_left=-1,
-              window_right=0, scale=None, deterministic=False, has_sink=False, has_seq_lens=False,
+              window_right=0, q_run_tiles=0, scale=None, deterministic=False, has_sink=False, has_seq_lens=False,
               q=None, k=None, v=None, o=None, dO=None, dq=None, dk=None, dv=None) -> AttnDesc:
     if dtype not in _DT:
         raise ValueError(f"dtype {dtype} not supported (bf16 / f16)")
@@ -172,7 +172,7 @@ def make_desc(g: Geometry, dtype, *, causal=True, bottom_right=False, window_lef
     d.heads_q, d.heads_kv, d.head_dim = g.heads_q, g.heads_kv, g.head_dim
     d.seq_q, d.seq_kv, d.total_q, d.total_kv = g.seq_q, g.seq_kv, g.total_q, g.total_kv
     d.causal, d.bottom_right, d.window_left = int(causal), int(bottom_right), int(window_left)
-    d.window_right = int(window_right)
+    d.window_right, d.q_run_tiles = int(window_right), int(q_run_tiles)
     d.scale = float(scale) if scale is not None else g.head_dim ** -0.5
     d.deterministic, d.has_sink, d.has_seq_lens = int(deterministic), int(has_sink), int(has_seq_lens)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dO), ("dq", dq), ("dk", dk), ("dv", dv)):
@@ -191,14 +191,16 @@ class Forward:
     here unless given)."""
 
     def __init__(self, q, k, v, *, causal=True, bottom_right=False, window_left=-1, window_right=0,
-                 scale=None, sink=None, cu_seqlens_q=None, cu_seqlens_kv=None, seq_lens_q=None,
-                 seq_lens_kv=None, max_seqlen_q=None, max_seqlen_kv=None, o=None, lse=None):
+                 q_run_tiles=0, scale=None, sink=None, cu_seqlens_q=None, cu_seqlens_kv=None,
+                 seq_lens_q=None, seq_lens_kv=None, max_seqlen_q=None, max_seqlen_kv=None, o=None,
+                 lse=None):
         g = geometry(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_kv)
         self.o = torch.empty_like(q) if o is None else o
         self.lse = torch.empty(lse_shape(g), dtype=torch.float32, device=q.device) if lse is None else lse
         desc = make_desc(g, q.dtype, causal=causal, bottom_right=bottom_right, window_left=window_left,
-                         window_right=window_right, scale=scale, has_sink=sink is not None,
-                         has_seq_lens=seq_lens_q is not None, q=q, k=k, v=v, o=self.o)
+                         window_right=window_right, q_run_tiles=q_run_tiles, scale=scale,
+                         has_sink=sink is not None, has_seq_lens=seq_lens_q is not None,
+                         q=q, k=k, v=v, o=self.o)
         self.plan = sdpa_fwd_plan(desc)
         self._keep = (q, k, v, sink, cu_seqlens_q, cu_seqlens_kv, seq_lens_q, seq_lens_kv)
         self.tensors = FwdTensors(q=_p(q), k=_p(k), v=_p(v), sink=_p(sink), cu_seqlens_q=_p(cu_seqlens_q),
@@ -221,7 +223,7 @@ class Backward:
     the tests to rerun the same launch)."""
 
     def __init__(self, q, k, v, o, dO, lse, *, causal=True, bottom_right=False, window_left=-1,
-                 window_right=0, scale=None, deterministic=False, sink=None, cu_seqlens_q=None,
+                 window_right=0, q_run_tiles=0, scale=None, deterministic=False, sink=None, cu_seqlens_q=None,
                  cu_seqlens_kv=None, seq_lens_q=None, seq_lens_kv=None, max_seqlen_q=None,
                  max_seqlen_kv=None, dq=None, dk=None, dv=None, dsink=None, workspace=None):
         g = geometry(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_kv)
@@ -232,8 +234,8 @@ class Backward:
         if sink is not None:
             self.dsink = torch.empty(g.heads_q, dtype=torch.float32, device=q.device) if dsink is None else dsink
         desc = make_desc(g, q.dtype, causal=causal, bottom_right=bottom_right,
-                         window_left=window_left, window_right=window_right, scale=scale,
-                         deterministic=deterministic,
+                         window_left=window_left, window_right=window_right,
+                         q_run_tiles=q_run_tiles, scale=scale, deterministic=deterministic,
                          has_sink=sink is not None, has_seq_lens=seq_lens_q is not None,
                          q=q, k=k, v=v, o=o, dO=dO, dq=self.dq, dk=self.dk, dv=self.dv)
         self.plan = sdpa_bwd_plan(desc)

@@ -90,6 +90,8 @@ sdpa_status check_desc(const sdpa_attn_desc* d, bool backward) {
   if (d->has_sink != 0 && d->has_sink != 1) return fail(SDPA_ERR_INVALID_ARG, "has_sink %d is not 0/1", d->has_sink);
   if (d->has_seq_lens != 0 && d->has_seq_lens != 1)
     return fail(SDPA_ERR_INVALID_ARG, "has_seq_lens %d is not 0/1", d->has_seq_lens);
+  if (d->q_run_tiles < 0 || d->q_run_tiles > 16)
+    return fail(SDPA_ERR_INVALID_ARG, "q_run_tiles %d is not in 0..16", d->q_run_tiles);
   if (d->layout == SDPA_LAYOUT_THD) {
     if (!d->has_seq_lens) return fail(SDPA_ERR_INVALID_ARG, "THD layout needs seq_lens_q / seq_lens_kv (has_seq_lens = 1)");
     if (d->total_q < 0 || d->total_kv < 0)
@@ -160,14 +162,21 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   // The per-tile kernel in unordered mode leaves dQ to a q-major pass (no
   // fp32 accumulator); in deterministic mode dQ goes through the relay.
   p.split_dq = !p.stream && !d->deterministic;
-  // A block of the dQ pass walks several q-tiles when each has few visiting
-  // kv-tiles (a narrow window), so its start-up latency is paid once per
-  // run; with many visitors one q-tile per block keeps the grid large.
+  // Consecutive q-tiles one block of the q-major passes walks.  A run
+  // pays the block's start-up latency once, but needs registers for the
+  // next q-tile's rows; a measured study over head_dim and band width on
+  // MI355X (bwd_dq and the forward, runs of 1 / 2 / 4 / 8, GQA and the
+  // workloads of the pages) picked these classes:
+  //   head_dim 128, band <= 256 keys: runs of 8 (both passes);
+  //   head_dim 64, band <= 64 keys: runs of 4 for the forward;
+  //   otherwise one q-tile per block (at head_dim 64 that keeps four blocks
+  //   per CU).
   {
-    const int64_t band = (d->window_left >= 0 ? (int64_t)d->window_left : (int64_t)d->seq_kv) +
-                         (d->causal ? (int64_t)d->window_right : (int64_t)d->seq_kv);
-    const int64_t visitors = (band + 2 * kTile - 1) / kTile;
-    p.dq_tiles = visitors <= 8 ? 4 : 1;
+    const int64_t band = (d->window_left >= 0 ? (int64_t)d->window_left : (int64_t)d->seq_kv + d->seq_q) +
+                         (d->causal ? (int64_t)d->window_right : (int64_t)d->seq_kv + d->seq_q);
+    p.dq_tiles = d->head_dim == 128 && band <= 256 ? 8 : 1;
+    p.fwd_tiles = d->head_dim == 128 && band <= 256 ? 8 : (band <= 64 ? 4 : 1);
+    if (d->q_run_tiles > 0) p.dq_tiles = p.fwd_tiles = d->q_run_tiles;
   }
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one

@@ -8,7 +8,7 @@
 // Sinks: cudnn-frontend PR #557 "... sink-token gradients ...", Summary: the
 // per-head sink logit joins each row's softmax denominator.
 //
-// One block (4 waves) per (run of p.dq_tiles consecutive q-tiles, query
+// One block (4 waves) per (run of p.fwd_tiles consecutive q-tiles, query
 // head, sequence); each wave owns 16 query rows of the current q-tile, kept
 // in registers as the B operand of S^T = K Q^T (keys on the MFMA rows,
 // queries on the columns).  The online softmax runs per column (one query
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // block -> (sequence, kv head, run of q-tiles, head within the group)
-  const int nruns = (p.n_q_tiles + p.dq_tiles - 1) / p.dq_tiles;
+  const int nruns = (p.n_q_tiles + p.fwd_tiles - 1) / p.fwd_tiles;
   int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = L % p.G;
   L /= p.G;
@@ -46,8 +46,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
   L /= nruns;
   const int hk = L % p.Hkv, b = L / p.Hkv, h = hk * p.G + hg;
   const Seq s = load_seq(p, b);
-  const int ia = run * p.dq_tiles;
-  const int ib = min(ia + p.dq_tiles, (s.cap_q + kTile - 1) / kTile);  // q-tiles holding slot rows
+  const int ia = run * p.fwd_tiles;
+  const int ib = min(ia + p.fwd_tiles, (s.cap_q + kTile - 1) / kTile);  // q-tiles holding slot rows
   if (ia >= ib) return;
   SeqSched g;
   g.init(s.len_q, s.len_kv, p.bottom_right, p.causal, p.window, p.right, kTile, kTile);
@@ -232,8 +232,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
 
 template <typename T, int D>
 static void fwd_td(const FwdArgs& a, hipStream_t st) {
-  const int n = a.p.B * a.p.Hq * ((a.p.n_q_tiles + a.p.dq_tiles - 1) / a.p.dq_tiles);
-  if (a.p.dq_tiles > 1)
+  const int n = a.p.B * a.p.Hq * ((a.p.n_q_tiles + a.p.fwd_tiles - 1) / a.p.fwd_tiles);
+  if (a.p.fwd_tiles > 1)
     hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3(n), dim3(kThreads), 0, st, a);
   else
     hipLaunchKernelGGL((fwd_kernel<T, D, false>), dim3(n), dim3(kThreads), 0, st, a);

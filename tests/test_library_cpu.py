@@ -52,6 +52,7 @@ def _desc(**kw):
     ("batch", 0, _lib.SDPA_ERR_INVALID_ARG, "batch"),
     ("deterministic", 2, _lib.SDPA_ERR_INVALID_ARG, "deterministic"),
     ("window_right", -1, _lib.SDPA_ERR_INVALID_ARG, "window_right"),
+    ("q_run_tiles", 17, _lib.SDPA_ERR_INVALID_ARG, "q_run_tiles"),
 ])
 def test_plan_rejects_bad_descriptors(lib, field, value, status, needle):
     d = _desc(**{field: value})
