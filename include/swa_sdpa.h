@@ -158,10 +158,13 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan,
  *   2. main : per kv-tile, the window-bounded q-tile loop ([PR866] Change):
  *             recompute P, dS = P (dP - delta), accumulate dK / dV over the
  *             kv head's query-head group ([PR557] Summary), add dS K into
- *             dQ through fp32 atomics or the ordered relay whose turns
- *             count from kv_first ([PR866] commit message); a kv-tile with
- *             no q-tile stores dK = dV = 0;
- *   3. cvt  : (atomic mode) fp32 dQ accumulator -> dtype;
+ *             dQ through the ordered relay whose turns count from kv_first
+ *             ([PR866] commit message) or, unordered, through fp32 atomics
+ *             (multi-head windows up to 128 keys: only at the boundaries of
+ *             the streaming kernel's chunks, converted by the last chunk);
+ *             a kv-tile with no q-tile stores dK = dV = 0;
+ *   3. dq   : (unordered mode, other shapes) a q-major pass that writes
+ *             dQ = scale * sum_j dS_ij K_j once per row;
  *   4. dsink: fixed-order reduction dSink[h] = -sum exp(sink_h - LSE) delta
  *             over valid rows ([PR557] Summary and review).
  * `workspace` is a device buffer of at least the planned size.

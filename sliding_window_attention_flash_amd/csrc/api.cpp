@@ -342,8 +342,6 @@ sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensor
     return fail(SDPA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   if (a.p.split_dq && (e = swa::launch_bwd_dq(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dq launch: %s", hipGetErrorString(e));
-  if (!d.deterministic && !a.p.split_dq && (e = swa::launch_bwd_cvt(a, stream)) != hipSuccess)
-    return fail(SDPA_ERR_HIP, "bwd_cvt launch: %s", hipGetErrorString(e));
   if (d.has_sink && (e = swa::launch_bwd_dsink(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dsink launch: %s", hipGetErrorString(e));
   g_err[0] = 0;

@@ -1,11 +1,11 @@
 // Backward kernels of the sliding-window attention (gfx950).
 //
 //   bwd_dot   delta_i = <dO_i, O_i>, per-q-tile dSink partials, clearing of
-//             the relay counters and of the dQ accumulator
+//             the relay counters, of the dQ accumulator and of unvisited
+//             dQ rows
 //   bwd_main  kv-tile-stationary backward with the window-bounded q-loop
 //             (dK, dV; dQ too in deterministic mode, through the relay)
 //   bwd_dq    q-tile-stationary dQ pass (unordered mode)
-//   bwd_cvt   fp32 dQ accumulator -> 16-bit dQ (streaming kernel, atomic mode)
 //   bwd_dsink fixed-order dSink reduction
 //
 // Method sources (web pages): cudnn-frontend PR #866 "frost(sdpa): bound the
@@ -13,7 +13,7 @@
 // relay" (commit message, Change) for the q-loop bounds, the zero store and
 // the relay turn; cudnn-frontend PR #557 "frost(sdpa): GQA/MQA, padding mask,
 // right-band widening, and sink-token gradients for the SM120 f16 backward"
-// (Summary, review comments) for the dot / main / reduce / cvt split, GQA,
+// (Summary, review comments) for the dot / main / reduce split, GQA,
 // per-sequence lengths and dSink.  The kernel design itself is written for
 // CDNA4 and is not taken from those pages.
 #include "kernels.h"
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
   const int tile0 = blockIdx.x * DOT_TILES, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const Seq s = load_seq(p, b);
   if (tile0 == 0 && h == 0 && b == 0 && tid < 2) a.ctl[tid] = 0;
-  if (a.deterministic && tid < DOT_TILES && tile0 + tid < p.n_q_tiles)
+  if ((a.deterministic || p.stream) && tid < DOT_TILES && tile0 + tid < p.n_q_tiles)
     a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile0 + tid] = 0;
 
   constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -130,29 +130,31 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
     }
   }
 
-  // Clearing for the main kernel.  Atomic mode (streaming kernel only; the
-  // per-tile kernel's dQ pass keeps no accumulator): the fp32 accumulator
-  // rows of q-tiles visited by several chunks, or none.  Relay mode: dQ rows
-  // of a q-tile that no kv-tile visits (the relay's last visitor writes
-  // every other q-tile).
+  // Clearing for the main kernel: dQ rows of a q-tile that no kv-tile (no
+  // chunk of the streaming kernel) visits, where no other kernel writes them
+  // (the relay, and the streaming kernel in either mode; the unordered dQ
+  // pass of the per-tile path writes its own zeros); and in the streaming
+  // kernel's atomic mode the fp32 accumulator rows of q-tiles several
+  // chunks visit.
   SeqSched g;
   main_sched(p, s, g);
   for (int t = 0; t < DOT_TILES; ++t) {
     const int tile = tile0 + t, row_base = tile * kTile;
     const int rows = min(kTile, s.cap_q - row_base);
     if (tile >= p.n_q_tiles || rows <= 0) break;
-    if (!a.deterministic) {
-      if (p.split_dq || chunk_visitors(p, g, tile) == 1) continue;
-      float4* acc = reinterpret_cast<float4*>(a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D);
-      const float4 z = {0.f, 0.f, 0.f, 0.f};
-      for (int e = tid; e < rows * (D / 4); e += kThreads) acc[e] = z;
-    } else if (g.n_visitors(tile) == 0) {
+    if (p.split_dq) break;
+    const int nv = p.stream ? chunk_visitors(p, g, tile) : g.n_visitors(tile);
+    if (nv == 0) {
       T* dqp = static_cast<T*>(a.dq);
       V8 z;
 #pragma unroll
       for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
       for (int e = tid; e < rows * CH; e += kThreads)
         st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
+    } else if (!a.deterministic && nv > 1) {
+      float4* acc = reinterpret_cast<float4*>(a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D);
+      const float4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int e = tid; e < rows * (D / 4); e += kThreads) acc[e] = z;
     }
   }
 }
@@ -685,42 +687,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
 }
 
 // ---------------------------------------------------------------------------
-// bwd_cvt: dQ = scale * accumulator, one block per (q-tile, head, sequence).
-
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_cvt_kernel(BwdArgs a) {
-  const Problem& p = a.p;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const Seq s = load_seq(p, b);
-  const int row_base = tile * kTile;
-  const int rows = min(kTile, s.cap_q - row_base);
-  if (p.stream) {
-    // interior q-tiles were written by the streaming kernel itself
-    SeqSched g;
-    main_sched(p, s, g);
-    if (chunk_visitors(p, g, tile) == 1) return;
-  }
-  constexpr int CH = D / 8;
-  T* dqp = static_cast<T*>(a.dq);
-  const float* acc = a.dq_acc + (s.stat0 + h * s.stat_hs + row_base) * D;
-  for (int e = tid; e < rows * CH; e += kThreads) {
-    const int r = e / CH, ch = e % CH;
-    const float4 x0 = *reinterpret_cast<const float4*>(acc + r * D + 8 * ch);
-    const float4 x1 = *reinterpret_cast<const float4*>(acc + r * D + 8 * ch + 4);
-    typename Elem<T>::vec8 y;
-    y[0] = Elem<T>::from_float(p.scale * x0.x);
-    y[1] = Elem<T>::from_float(p.scale * x0.y);
-    y[2] = Elem<T>::from_float(p.scale * x0.z);
-    y[3] = Elem<T>::from_float(p.scale * x0.w);
-    y[4] = Elem<T>::from_float(p.scale * x1.x);
-    y[5] = Elem<T>::from_float(p.scale * x1.y);
-    y[6] = Elem<T>::from_float(p.scale * x1.z);
-    y[7] = Elem<T>::from_float(p.scale * x1.w);
-    st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + r) + 8 * ch, y);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // bwd_dsink: dSink[h] = -sum of the per-q-tile partials, in a fixed order.
 
 __global__ __launch_bounds__(64) void bwd_dsink_kernel(BwdArgs a) {
@@ -790,21 +756,6 @@ static hipError_t dq_t(const BwdArgs& a, hipStream_t st) {
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   if (a.p.n_q_tiles == 0) return hipSuccess;
   return a.dtype == 0 ? dq_t<__bf16>(a, st) : dq_t<_Float16>(a, st);
-}
-
-template <typename T>
-static hipError_t cvt_t(const BwdArgs& a, hipStream_t st) {
-  dim3 grid(a.p.n_q_tiles, a.p.Hq, a.p.B);
-  if (a.p.D == 64)
-    hipLaunchKernelGGL((bwd_cvt_kernel<T, 64>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_cvt_kernel<T, 128>), grid, dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_cvt(const BwdArgs& a, hipStream_t st) {
-  if (a.p.n_q_tiles == 0) return hipSuccess;
-  return a.dtype == 0 ? cvt_t<__bf16>(a, st) : cvt_t<_Float16>(a, st);
 }
 
 hipError_t launch_bwd_dsink(const BwdArgs& a, hipStream_t st) {

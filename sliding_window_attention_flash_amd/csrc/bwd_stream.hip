@@ -306,6 +306,26 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         for (int e = 0; e < 2; ++e)
 #pragma unroll
           for (int r = 0; r < 4; ++r) unsafeAtomicAdd(accb + acc_off(i, e) + r, acc[e][r]);
+      // The visiting chunk whose adds complete last converts the tile: every
+      // thread waits for its agent-scope atomics, then one thread counts the
+      // chunk in; the chunk that completes the count reads the sums back
+      // with agent-scope loads (coherent across XCDs).
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) sTicket = __hip_atomic_fetch_add(semb + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const int nv = kv_last(i) / p.chunk - kv_first(i) / p.chunk + 1;
+      if (sTicket == nv - 1 && qi < s.cap_q) {
+        T* row = dqb + (int64_t)qi * rs_dq + 32 * wd + 4 * gq;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            v[r] = p.scale * __hip_atomic_load(accb + acc_off(i, e) + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          *reinterpret_cast<u32x2*>(row + 16 * e) = pack4<T>(v[0], v[1], v[2], v[3]);
+        }
+      }
     } else if (!earlier) {
       // first visiting chunk of a boundary tile: turn 0, no wait
       if (qi < s.cap_q)
