@@ -197,9 +197,19 @@ def _find(d, suffix):
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
-def summarize_stats(d, out, command, bench_json=None):
+def _timed_launch_avg_us(d, steps):
+    """Average duration (us) of the main kernel over its last ``steps``
+    dispatches in the kernel trace (the timed ones; warm-up precedes them)."""
+    rows = [r for r in _rows(_find(d, "kernel_trace.csv")) if MAIN_KERNEL in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    last = rows[-steps:]
+    return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in last) / len(last) / 1e3, len(last)
+
+
+def summarize_stats(d, out, command, bench_json=None, steps=None, workload="c3"):
     rows = _rows(_find(d, "kernel_stats.csv"))
-    lines = [f"# rocprofv3 kernel statistics, {MAIN_KERNEL} workload", "", "command:", f"    {command}", "",
+    lines = [f"# rocprofv3 kernel statistics, workload {workloads()[workload].name}", "", "command:",
+             f"    {command}", "",
              f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
     for r in rows:
         name = r["Name"]
@@ -211,6 +221,10 @@ def summarize_stats(d, out, command, bench_json=None):
             b = json.loads([x for x in fh if x.startswith("{")][-1])
         lines += ["", "bench line of the same run (HIP events on the launch stream, profiler attached):",
                   f"    main_kernel_ms = {b['extra']['main_kernel_ms']:.4f}, ms_per_step = {b['ms_per_step']:.4f}"]
+    if steps and any(MAIN_KERNEL in r["Name"] for r in rows):
+        avg, n = _timed_launch_avg_us(d, steps)
+        lines += ["", f"{MAIN_KERNEL} over the timed launches (last {n} dispatches of the kernel trace): "
+                      f"avg {avg:.2f} us"]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -310,7 +324,8 @@ def main():
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.out, " ".join(args.command), args.bench_json)
+        summarize_stats(args.summarize_stats, args.out, " ".join(args.command), args.bench_json, args.steps,
+                        args.workload)
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.out, args.command, args.workload)
