@@ -87,8 +87,13 @@ typedef struct sdpa_attn_desc {
   int32_t window_right; /* >= 0, causal only: keys up to a(i) + window_right
                            are visible (0: plain causal)                      */
   float scale;          /* softmax scale on Q.K (> 0), e.g. 1/sqrt(D)        */
-  int32_t deterministic; /* backward dQ: 1 ordered relay (bitwise repeatable),
-                            0 unordered fp32 atomics                         */
+  int32_t deterministic; /* backward: 0 unordered (fp32 atomics where
+                            blocks share a dQ tile); 1 bitwise repeatable,
+                            by the fastest ordered method (the streaming
+                            kernel's chunk relay, or the relay-free q-major
+                            dQ pass of the per-tile path); 2 the per-kv-tile
+                            ordered relay of [PR866] on the per-tile path,
+                            for every shape                                 */
   int32_t has_sink;     /* 1: sink logits given (fp32 [heads_q])             */
   int32_t has_seq_lens; /* 1: seq_lens_q / seq_lens_kv given (THD requires)  */
   int32_t q_run_tiles;  /* 0: the measured default; 1..16: consecutive 64-row

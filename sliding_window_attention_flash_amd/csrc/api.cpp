@@ -85,8 +85,8 @@ sdpa_status check_desc(const sdpa_attn_desc* d, bool backward) {
     return fail(SDPA_ERR_INVALID_ARG, "window_right %d widens the causal band and needs causal = 1", d->window_right);
   if (!(d->scale > 0.f) || !std::isfinite(d->scale))
     return fail(SDPA_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)d->scale);
-  if (d->deterministic != 0 && d->deterministic != 1)
-    return fail(SDPA_ERR_INVALID_ARG, "deterministic %d is not 0/1", d->deterministic);
+  if (d->deterministic < 0 || d->deterministic > 2)
+    return fail(SDPA_ERR_INVALID_ARG, "deterministic %d is not 0/1/2", d->deterministic);
   if (d->has_sink != 0 && d->has_sink != 1) return fail(SDPA_ERR_INVALID_ARG, "has_sink %d is not 0/1", d->has_sink);
   if (d->has_seq_lens != 0 && d->has_seq_lens != 1)
     return fail(SDPA_ERR_INVALID_ARG, "has_seq_lens %d is not 0/1", d->has_seq_lens);
@@ -156,12 +156,16 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   bool small_rows = true;
   for (const int64_t rs : {p.sq[2], p.sk[2], p.sv[2], p.sdo[2], p.sdq[2], p.sdk[2], p.sdv[2]})
     small_rows &= rs > 0 && rs <= INT32_MAX;
+  // deterministic = 2 asks for the per-kv-tile relay, which only the
+  // per-tile kernel has.
   p.stream = p.G == 1 && d->causal && p.right == 0 && d->window_left >= 0 && d->window_left <= 128 &&
-             d->head_dim == 64 && small_rows;
+             d->head_dim == 64 && small_rows && d->deterministic != 2;
   p.step_kv = p.stream ? 128 : kTile;
-  // The per-tile kernel in unordered mode leaves dQ to a q-major pass (no
-  // fp32 accumulator); in deterministic mode dQ goes through the relay.
-  p.split_dq = !p.stream && !d->deterministic;
+  // The per-tile kernel leaves dQ to a q-major pass (no fp32 accumulator).
+  // Each dQ row is summed inside one block in a fixed order and each dK / dV
+  // row likewise, so this path is bitwise repeatable and serves both the
+  // unordered and the repeatable mode; deterministic = 2 runs the relay.
+  p.split_dq = !p.stream && d->deterministic != 2;
   // Consecutive q-tiles one block of the q-major passes walks.  A run
   // pays the block's start-up latency once, but needs registers for the
   // next q-tile's rows; a measured study over head_dim and band width on

@@ -4,8 +4,8 @@
 //             the relay counters, of the dQ accumulator and of unvisited
 //             dQ rows
 //   bwd_main  kv-tile-stationary backward with the window-bounded q-loop
-//             (dK, dV; dQ too in deterministic mode, through the relay)
-//   bwd_dq    q-tile-stationary dQ pass (unordered mode)
+//             (dK, dV; dQ too in relay mode, deterministic = 2)
+//   bwd_dq    q-tile-stationary dQ pass (per-tile path, modes 0 and 1)
 //   bwd_dsink fixed-order dSink reduction
 //
 // Method sources (web pages): cudnn-frontend PR #866 "frost(sdpa): bound the
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
 
   // Clearing for the main kernel: dQ rows of a q-tile that no kv-tile (no
   // chunk of the streaming kernel) visits, where no other kernel writes them
-  // (the relay, and the streaming kernel in either mode; the unordered dQ
+  // (the relay, and the streaming kernel in either mode; the q-major dQ
   // pass of the per-tile path writes its own zeros); and in the streaming
   // kernel's atomic mode the fp32 accumulator rows of q-tiles several
   // chunks visit.
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
 //   dQ_i = dS K                           A: transposed reads of dS^T,
 //                                         B: transposed reads of the K tile
 // and dQ_i is added into q-tile i's fp32 partial through the ordered relay
-// (deterministic mode); in unordered mode dQ is left to bwd_dq and the two
+// (deterministic = 2); otherwise dQ is left to bwd_dq and the two
 // dS^T / dQ steps drop out.  A wave skips the 16-row blocks its keys cannot see.  The
 // next visit's Q / dO tile is loaded into registers while the current one
 // computes.  All products are 16x16x32 MFMAs with fp32 accumulation.
@@ -455,7 +455,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dq: q-tile-stationary dQ pass of the unordered mode, one block (4
+// bwd_dq: q-tile-stationary dQ pass of the per-tile path (deterministic 0
+// and 1: it sums each row's kv-tiles in a fixed order), one block (4
 // waves) per (run of p.dq_tiles consecutive q-tiles, query head, sequence);
 // two blocks per CU.
 //
@@ -721,7 +722,7 @@ hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t st) {
 template <typename T, int D>
 static hipError_t main_td(const BwdArgs& a, hipStream_t st) {
   const int n = a.p.B * a.p.Hkv * a.p.n_kv_tiles;
-  if (a.deterministic)
+  if (!a.p.split_dq)
     hipLaunchKernelGGL((bwd_main_kernel<T, D, true>), dim3(n), dim3(kThreads), 0, st, a);
   else
     hipLaunchKernelGGL((bwd_main_kernel<T, D, false>), dim3(n), dim3(kThreads), 0, st, a);

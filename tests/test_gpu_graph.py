@@ -25,9 +25,9 @@ CASES = [
     (Workload("graph_stream_w128_s1000", BF16, 1, 4, 4, 64, 1000, 1000, window_left=128), False),
     # GQA, bottom-right, sinks: the per-tile kernel (relay) or the split dQ pass
     (Workload("graph_gqa_br_w70_sink", BF16, 2, 8, 2, 64, 190, 230, bottom_right=True, window_left=70,
-              sink=True), True),
+              sink=True), 2),
     (Workload("graph_gqa_br_w70_sink", BF16, 2, 8, 2, 64, 190, 230, bottom_right=True, window_left=70,
-              sink=True), False),
+              sink=True), 0),
 ]
 
 
@@ -45,7 +45,7 @@ def _capture(fn):
     return g
 
 
-@pytest.mark.parametrize("w,det", CASES, ids=[f"{w.name}-{'relay' if d else 'unordered'}" for w, d in CASES])
+@pytest.mark.parametrize("w,det", CASES, ids=[f"{w.name}-det{int(d)}" for w, d in CASES])
 def test_backward_graph_replays_match_eager(w, det):
     say(f"case {w.name} det={det}: eager, capture, 4 replays")
     inp = make_inputs(w, device="cuda", seed=31)

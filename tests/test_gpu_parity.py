@@ -53,7 +53,12 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("det", [False, True], ids=["atomic", "relay"])
+# deterministic: 0 unordered, 1 bitwise repeatable (chunk relay in the
+# streaming kernel, q-major dQ pass elsewhere), 2 the per-kv-tile relay
+DET = dict(argvalues=[0, 1, 2], ids=["unordered", "ordered", "tile_relay"])
+
+
+@pytest.mark.parametrize("det", **DET)
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_small_full_oracle(w, det):
     say(f"case {w.name} det={det}")
@@ -73,7 +78,7 @@ def _thd_small(sink=True, dtype=F16, D=64, hkv=2, wr=0):
                     len_q=lq, len_kv=lk, cap_q=cq, cap_kv=ck)
 
 
-@pytest.mark.parametrize("det", [False, True], ids=["atomic", "relay"])
+@pytest.mark.parametrize("det", **DET)
 @pytest.mark.parametrize("D,hkv,wr", [(64, 2, 0), (128, 2, 0), (64, 8, 0), (64, 2, 50)])
 def test_thd_padded_with_sinks(det, D, hkv, wr):
     w = _thd_small(D=D, hkv=hkv, wr=wr)
@@ -84,7 +89,7 @@ def test_thd_padded_with_sinks(det, D, hkv, wr):
 
 def test_c1_tiny_full_oracle():
     w = CONFIGS["c1"]
-    for det in (False, True):
+    for det in (0, 1, 2):
         say(f"case {w.name} det={det}")
         inp, out, _ = run_gpu(w, seed=1, deterministic=det)
         compare_full(w, inp, out)
@@ -102,6 +107,24 @@ def test_relay_bitwise_repeatable_and_matches_atomic():
     _, at, _ = run_gpu(w, seed=9, deterministic=False)
     for key in ("dq", "dk", "dv"):
         assert_close(f"{key} det/at", outs[0][key].cpu(), at[key].cpu().double())
+    compare_full(w, inp, outs[0], check_fwd=False)
+
+
+@pytest.mark.parametrize("det", [1, 2], ids=["ordered", "tile_relay"])
+def test_general_path_bitwise_repeatable(det):
+    # GQA, bottom-right, sinks, head_dim 128: the per-tile kernel with the
+    # q-major dQ pass (1) or the per-kv-tile relay (2)
+    w = _wl("det_gqa_br_w100_d128_s777", BF16, 2, 8, 2, 128, 777, 900, bottom_right=True, window_left=100,
+            sink=True)
+    say(f"case {w.name} det={det}: 3 runs + 1 unordered run")
+    inp, outs, _ = run_gpu(w, seed=19, deterministic=det, runs=3)
+    for o in outs:
+        assert o["expiries"] == 0
+    for key in ("dq", "dk", "dv", "dsink"):
+        assert torch.equal(outs[0][key], outs[1][key]) and torch.equal(outs[0][key], outs[2][key]), key
+    _, un, _ = run_gpu(w, seed=19, deterministic=0)
+    for key in ("dq", "dk", "dv", "dsink"):
+        assert_close(f"{key} det/un", outs[0][key].float().cpu(), un[key].double().cpu())
     compare_full(w, inp, outs[0], check_fwd=False)
 
 

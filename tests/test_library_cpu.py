@@ -50,7 +50,7 @@ def _desc(**kw):
     ("window_left", -2, _lib.SDPA_ERR_INVALID_ARG, "window_left"),
     ("scale", 0.0, _lib.SDPA_ERR_INVALID_ARG, "scale"),
     ("batch", 0, _lib.SDPA_ERR_INVALID_ARG, "batch"),
-    ("deterministic", 2, _lib.SDPA_ERR_INVALID_ARG, "deterministic"),
+    ("deterministic", 3, _lib.SDPA_ERR_INVALID_ARG, "deterministic"),
     ("window_right", -1, _lib.SDPA_ERR_INVALID_ARG, "window_right"),
     ("q_run_tiles", 17, _lib.SDPA_ERR_INVALID_ARG, "q_run_tiles"),
 ])
@@ -97,15 +97,16 @@ def test_run_validates_workspace_and_tensors_before_touching_a_device(lib):
     assert b"256-byte" in lib.sdpa_last_error()
 
 
-@pytest.mark.parametrize("det", [False, True])
+@pytest.mark.parametrize("det", [0, 1, 2])
 def test_workspace_size_formula(lib, det):
-    # delta, fp32 dQ partials (relay only: the unordered general path computes
-    # dQ in its own q-major pass), relay counters, control words, dSink partials
-    plan = api.sdpa_bwd_plan(_desc(B=2, Hq=4, Hkv=2, D=64, Sq=300, Skv=300, deterministic=int(det)))
+    # delta, fp32 dQ partials (the per-kv-tile relay only: otherwise this
+    # GQA shape computes dQ in the q-major pass), relay counters, control
+    # words, dSink partials
+    plan = api.sdpa_bwd_plan(_desc(B=2, Hq=4, Hkv=2, D=64, Sq=300, Skv=300, deterministic=det))
     rows = 2 * 4 * 300
     ntq = 5
     expect = 0
-    for nbytes in (4 * rows, 4 * rows * 64 if det else 0, 4 * 2 * 4 * ntq, 16, 4 * 4 * 2 * ntq):
+    for nbytes in (4 * rows, 4 * rows * 64 if det == 2 else 0, 4 * 2 * 4 * ntq, 16, 4 * 4 * 2 * ntq):
         expect = (expect + nbytes + 255) // 256 * 256
     assert plan.workspace_bytes == expect
 
