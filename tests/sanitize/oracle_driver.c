@@ -1,6 +1,6 @@
 /* Drives every entry point of the fp64 oracle on small problems whose
  * buffers are allocated at exactly their required sizes, for a build with
- * AddressSanitizer and UndefinedBehaviorSanitizer (tests/test_oracle_sanitizers.py).
+ * AddressSanitizer and UndefinedBehaviorSanitizer (tests/test_host_sanitizers.py).
  * Cases: dense GQA with a sink, a left window and a right band (bf16 and
  * fp64 storage), and a packed batch with padded slots, an empty query
  * sequence and an empty key sequence.  Exit status 0 when every call
