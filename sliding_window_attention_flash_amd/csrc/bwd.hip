@@ -352,13 +352,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
         dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[st]]), vB[st], dP[mb]);
       }
     }
+    // Where the wave's 16 keys see all 64 rows (t - tlo in [u0 - 15,
+    // u0 + 63] inside [0, trange], every key in the sequence) the mask drops
+    // out; rows past the sequence still get P = 0 from LSE = +inf.
+    const bool full = u0 >= 15 && u0 + 63 <= (int)trange && kv0 + 16 * w + 15 < s.len_kv;
     V8 pP[2], pS[2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int um = u0 + 16 * mb;
       const bool any = um + 15 >= 0 && um - 15 <= (int)trange;
       float pv[4] = {0.f, 0.f, 0.f, 0.f}, dsv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (any) {
+      if (full) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&sLse[16 * mb + 4 * gq]);
+        const f32x4 del4 = *reinterpret_cast<const f32x4*>(&sDelta[16 * mb + 4 * gq]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[r] = fast_exp2(S[mb][r] * p.scale_log2 - lse4[r]);
+          dsv[r] = pv[r] * (dP[mb][r] - del4[r]);
+        }
+      } else if (any) {
         const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&sLse[16 * mb + 4 * gq]);
         const f32x4 del4 = *reinterpret_cast<const f32x4*>(&sDelta[16 * mb + 4 * gq]);
         const int tb = q0 + 16 * mb + 4 * gq + tkey;
@@ -640,12 +652,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
       }
     }
     // dS^T of key 16 nb + 4 gq + r; blocks 2 ks and 2 ks + 1 form the
-    // 32-key B operand of step ks
+    // 32-key B operand of step ks.  Where the wave's 16 rows see all 64 keys
+    // (t - tlo in [u0 - 63, u0 + 15] inside [0, trange], every key in the
+    // sequence) the mask drops out.
+    const bool full = u0 >= 63 && u0 + 15 <= (int)trange && kvn >= kTile;
     V8 bS[2];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       float dsv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (live[nb]) {
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dsv[r] = fast_exp2(St[nb][r] * p.scale_log2 - lse2) * (dPt[nb][r] - del);
+      } else if (live[nb]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float x = St[nb][r] * p.scale_log2 - lse2;

@@ -170,19 +170,31 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
         St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[st]]), qB[st], St[nb]);
     }
     // masked logits (log2 units) and the tile's row max over the 4 lanes
-    // sharing a column
+    // sharing a column.  Where the wave's 16 rows see all 64 keys the mask
+    // drops out.
+    const bool full = u0 >= 63 && u0 + 15 <= (int)trange && kvn >= kTile;
     float x[4][4];
     float mx = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = St[nb][r] * p.scale_log2;
-        asm("" : "+v"(v));
-        const bool vis = live[nb] && (unsigned)(tq - 16 * nb - r) <= trange && 16 * nb + 4 * gq + r < kvn;
-        x[nb][r] = vis ? v : -INFINITY;
-        mx = fmaxf(mx, x[nb][r]);
-      }
+        for (int r = 0; r < 4; ++r) {
+          x[nb][r] = St[nb][r] * p.scale_log2;
+          mx = fmaxf(mx, x[nb][r]);
+        }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = St[nb][r] * p.scale_log2;
+          asm("" : "+v"(v));
+          const bool vis = live[nb] && (unsigned)(tq - 16 * nb - r) <= trange && 16 * nb + 4 * gq + r < kvn;
+          x[nb][r] = vis ? v : -INFINITY;
+          mx = fmaxf(mx, x[nb][r]);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx);
