@@ -102,7 +102,8 @@ typedef struct sdpa_attn_desc {
                            tuning studies                                     */
   /* Element strides (batch, head, row) of each tensor; the head_dim axis is
    * contiguous.  THD ignores the batch entry (rows are tokens).  Rows and
-   * base pointers must be 16-byte aligned. */
+   * base pointers must be 16-byte aligned; row strides below 2^32 elements
+   * (SDPA_ERR_UNSUPPORTED otherwise). */
   int64_t stride_q[3], stride_k[3], stride_v[3], stride_o[3], stride_do[3];
   int64_t stride_dq[3], stride_dk[3], stride_dv[3];
 } sdpa_attn_desc;

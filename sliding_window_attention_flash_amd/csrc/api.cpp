@@ -58,6 +58,9 @@ sdpa_status check_strides(const char* name, const int64_t* st, const sdpa_attn_d
   if (st[2] < d->head_dim)
     return fail(SDPA_ERR_INVALID_ARG, "stride_%s row stride %lld is smaller than head_dim %d", name,
                 (long long)st[2], d->head_dim);
+  if (st[2] > (int64_t)UINT32_MAX)  // the kernels form row offsets with 32 x 32-bit products
+    return fail(SDPA_ERR_UNSUPPORTED, "stride_%s row stride %lld exceeds 2^32 - 1 elements", name,
+                (long long)st[2]);
   return SDPA_OK;
 }
 

@@ -282,16 +282,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
     h = hk * p.G + v / nit;
     i = qlo + (nit - 1 - v % nit);  // descending q-tiles within a head
   };
+  // this thread's 16-byte chunk of row 0, head 0; a row r of head h is
+  // r * (row stride) + h * (head stride) further in either layout
+  const T* q00 = qp + elem_off(p, p.sq, b, s.row0_q, 0, 0) + 8 * (tid % CH);
+  const T* o00 = dop + elem_off(p, p.sdo, b, s.row0_q, 0, 0) + 8 * (tid % CH);
   auto stage_load = [&](int v) {  // a visited q-tile: the sequence has rows
     int h, i;
     visit_hi(v, h, i);
     st_i = i;
     const int row0 = i * kTile;
+    const T* qh = q00 + h * p.sq[1];
+    const T* oh = o00 + h * p.sdo[1];
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const int qi = min(row0 + tid / CH + ps * RPP, s.len_q - 1), ch = tid % CH;
-      rq[ps] = ld8(qp + elem_off(p, p.sq, b, s.row0_q, h, qi) + 8 * ch);
-      rdo[ps] = ld8(dop + elem_off(p, p.sdo, b, s.row0_q, h, qi) + 8 * ch);
+      const int qi = min(row0 + tid / CH + ps * RPP, s.len_q - 1);
+      rq[ps] = ld8(row_at(qh, qi, p.sq[2]));
+      rdo[ps] = ld8(row_at(oh, qi, p.sdo[2]));
     }
     if (tid < kTile) {
       const int64_t si = s.stat0 + h * s.stat_hs + min(row0 + tid, s.len_q - 1);
@@ -559,11 +565,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
   // P = exp2(-inf) = 0
   V8 qB[NS], oB[NS], nqB[NS], noB[NS];
   float lse2, del, nlse2 = 0.f, ndel = 0.f;
+  const T* q0h = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, 0) + 8 * gq;
+  const T* o0h = static_cast<const T*>(a.dO) + elem_off(p, p.sdo, b, s.row0_q, h, 0) + 8 * gq;
   auto load_q = [&](int i, V8* qv, V8* ov, float& l2, float& dl) {
     const int row = i * kTile + 16 * w + c;
     const int qr = min(row, s.len_q - 1);
-    const T* qrow = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, qr) + 8 * gq;
-    const T* orow = static_cast<const T*>(a.dO) + elem_off(p, p.sdo, b, s.row0_q, h, qr) + 8 * gq;
+    const T* qrow = row_at(q0h, qr, p.sq[2]);
+    const T* orow = row_at(o0h, qr, p.sdo[2]);
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       qv[st] = ld8(qrow + 32 * st);
@@ -580,15 +588,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
 
   // K / V staging (a visited kv-tile: len_kv > 0); rows past the sequence
   // repeat its last key (finite values; the mask gives them zero weight)
-  const T* kp = static_cast<const T*>(a.k);
-  const T* vp = static_cast<const T*>(a.v);
+  const T* k0 = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, 0) + 8 * (tid % CH);
+  const T* v0 = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, 0) + 8 * (tid % CH);
   V8 rk[NPASS], rv[NPASS];
   auto load_kv = [&](int j) {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const int kk = min(j * kTile + tid / CH + ps * RPP, s.len_kv - 1), ch = tid % CH;
-      rk[ps] = ld8(kp + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch);
-      rv[ps] = ld8(vp + elem_off(p, p.sv, b, s.row0_kv, hk, kk) + 8 * ch);
+      const int kk = min(j * kTile + tid / CH + ps * RPP, s.len_kv - 1);
+      rk[ps] = ld8(row_at(k0, kk, p.sk[2]));
+      rv[ps] = ld8(row_at(v0, kk, p.sv[2]));
     }
   };
   auto store_kv = [&](int buf) {

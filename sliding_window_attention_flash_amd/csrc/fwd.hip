@@ -94,23 +94,24 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
   // Q rows of a visited q-tile (len_q > 0); rows past the sequence repeat
   // its last row and are dropped at the end
   V8 qB[NS], nqB[NS];
+  const T* q0h = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, 0) + 8 * gq;
   auto load_q = [&](int i, V8* qv) {
     const int qr = min(i * kTile + 16 * w + c, s.len_q - 1);
-    const T* qrow = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, qr) + 8 * gq;
+    const T* qrow = row_at(q0h, qr, p.sq[2]);
 #pragma unroll
     for (int st = 0; st < NS; ++st) qv[st] = ld8(qrow + 32 * st);
   };
   // K / V staging (a visited kv-tile: len_kv > 0); rows past the sequence
   // repeat its last key (finite values; the mask gives them zero weight)
-  const T* kp = static_cast<const T*>(a.k);
-  const T* vp = static_cast<const T*>(a.v);
+  const T* k0 = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, 0) + 8 * (tid % CH);
+  const T* v0 = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, 0) + 8 * (tid % CH);
   V8 rk[NPASS], rv[NPASS];
   auto load_kv = [&](int j) {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const int kk = min(j * kTile + tid / CH + ps * RPP, s.len_kv - 1), ch = tid % CH;
-      rk[ps] = ld8(kp + elem_off(p, p.sk, b, s.row0_kv, hk, kk) + 8 * ch);
-      rv[ps] = ld8(vp + elem_off(p, p.sv, b, s.row0_kv, hk, kk) + 8 * ch);
+      const int kk = min(j * kTile + tid / CH + ps * RPP, s.len_kv - 1);
+      rk[ps] = ld8(row_at(k0, kk, p.sk[2]));
+      rv[ps] = ld8(row_at(v0, kk, p.sv[2]));
     }
   };
   auto store_kv = [&](int buf) {

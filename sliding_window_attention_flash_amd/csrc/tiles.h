@@ -16,6 +16,13 @@ __device__ __forceinline__ void st8(T* p, const typename Elem<T>::vec8& v) {
   *reinterpret_cast<typename Elem<T>::vec8*>(p) = v;
 }
 
+// Row `row` (>= 0) of a tensor whose row stride fits in 32 bits (checked
+// when a plan is made): one 32 x 32 -> 64-bit multiply-add.
+template <typename T>
+__device__ __forceinline__ const T* row_at(const T* base, int row, int64_t stride) {
+  return base + (uint64_t)(uint32_t)row * (uint32_t)stride;
+}
+
 // Blocks are dealt to the 8 XCDs round-robin; renumber them so that each XCD
 // runs one contiguous range of logical tiles (neighbouring tiles of one head
 // then share that XCD's L2).

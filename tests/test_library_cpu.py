@@ -86,6 +86,14 @@ def test_plan_rejects_unaligned_strides_and_thd_without_lengths(lib):
         api.sdpa_bwd_plan(d)
 
 
+def test_plan_rejects_row_strides_beyond_32_bits(lib):
+    d = _desc()
+    d.stride_k[2] = 1 << 32
+    with pytest.raises(_lib.SdpaError) as e:
+        api.sdpa_bwd_plan(d)
+    assert e.value.status == _lib.SDPA_ERR_UNSUPPORTED and "stride_k" in str(e.value)
+
+
 def test_run_validates_workspace_and_tensors_before_touching_a_device(lib):
     plan = api.sdpa_bwd_plan(_desc())
     t = _lib.BwdTensors()
