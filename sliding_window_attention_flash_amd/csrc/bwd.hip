@@ -347,13 +347,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
     const int u0 = q0 + g.diag - (kv0 + 16 * w) - tlo;
 
     f32x4 S[4], dP[4];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      S[mb] = dP[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int um = u0 + 16 * mb;
-      if (um + 15 < 0 || um - 15 > (int)trange) continue;
+      if (um + 15 < 0 || um - 15 > (int)trange) {
+        S[mb] = dP[mb] = zero4;
+        continue;
+      }
+      // the first product starts from a literal zero accumulator
+      S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[0]]), kB[0], zero4);
+      dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[0]]), vB[0], zero4);
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
+      for (int st = 1; st < NS; ++st) {
         S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[st]]), kB[st], S[mb]);
         dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[st]]), vB[st], dP[mb]);
       }
@@ -647,14 +653,20 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
 
     f32x4 St[4], dPt[4];
     bool live[4];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      St[nb] = dPt[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int um = u0 - 16 * nb;  // the block spans t - tlo in [um - 15, um + 15]
       live[nb] = um + 15 >= 0 && um - 15 <= (int)trange && 16 * nb < kvn;
-      if (!live[nb]) continue;
+      if (!live[nb]) {
+        St[nb] = dPt[nb] = zero4;
+        continue;
+      }
+      // the first product starts from a literal zero accumulator
+      St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[0]]), qB[0], zero4);
+      dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[0]]), oB[0], zero4);
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
+      for (int st = 1; st < NS; ++st) {
         St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[st]]), qB[st], St[nb]);
         dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[st]]), oB[st], dPt[nb]);
       }

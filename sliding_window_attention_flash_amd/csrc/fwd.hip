@@ -160,14 +160,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
 
     f32x4 St[4];
     bool live[4];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      St[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int um = u0 - 16 * nb;  // the block spans t - tlo in [um - 15, um + 15]
       live[nb] = um + 15 >= 0 && um - 15 <= (int)trange && 16 * nb < kvn;
-      if (!live[nb]) continue;
+      if (!live[nb]) {
+        St[nb] = zero4;
+        continue;
+      }
+      // the first product starts from a literal zero accumulator
+      St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[0]]), qB[0], zero4);
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
+      for (int st = 1; st < NS; ++st)
         St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[st]]), qB[st], St[nb]);
     }
     // masked logits (log2 units) and the tile's row max over the 4 lanes
