@@ -1,6 +1,6 @@
 """Benchmark of the sliding-window attention backward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c3|c3_atomic|c1|c2_4k|c2_8k|c4|c4_f16|c5]
+    python bench.py [--steps K] [--warmup W] [--workload c3|c3_atomic|c1|c2_4k|c2_8k|c2_4k_det|c2_8k_det|c4|c4_f16|c5]
     python bench.py --copy-calibration ...      (appends a copy of known size)
     python bench.py --summarize-stats DIR --out FILE --command CMD
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --out FILE --command CMD
@@ -76,6 +76,8 @@ def workloads():
         "c1": CONFIGS["c1"],
         "c2_4k": CONFIGS["c2_4k"],
         "c2_8k": CONFIGS["c2_8k"],
+        "c2_4k_det": CONFIGS["c2_4k"].with_(name=CONFIGS["c2_4k"].name + "_det", deterministic=True),
+        "c2_8k_det": CONFIGS["c2_8k"].with_(name=CONFIGS["c2_8k"].name + "_det", deterministic=True),
         "c4": CONFIGS["c4"],
         "c4_f16": CONFIGS["c4_f16"],
         "c5": CONFIGS["c5"],
@@ -357,7 +359,7 @@ def main():
     if not args.no_extra:
         # every other workload, timed the same way (the large GQA one with
         # fewer steps); each entry names its workload's shape
-        for name in ("c3_atomic", "c1", "c2_4k", "c2_8k", "c4", "c4_f16", "c5"):
+        for name in ("c3_atomic", "c1", "c2_4k", "c2_8k", "c2_4k_det", "c2_8k_det", "c4", "c4_f16", "c5"):
             if name == args.workload:
                 continue
             wx = wl[name]
