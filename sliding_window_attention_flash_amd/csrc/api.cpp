@@ -155,8 +155,9 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   // The streaming kernel covers multi-head attention with a causal mask and
   // a left window of at most 128 keys at head_dim 64 (its ring of q-tile
   // slots is sized for that); everything else runs the per-tile kernel.
-  // It addresses rows with 32-bit row strides.
-  bool small_rows = true;
+  // It addresses rows with 32-bit row strides, and one (batch, head)'s fp32
+  // dQ partial rows with 32-bit byte offsets.
+  bool small_rows = (int64_t)d->seq_q * d->head_dim * (int64_t)sizeof(float) <= INT32_MAX;
   for (const int64_t rs : {p.sq[2], p.sk[2], p.sv[2], p.sdo[2], p.sdq[2], p.sdk[2], p.sdv[2]})
     small_rows &= rs > 0 && rs <= INT32_MAX;
   // deterministic = 2 asks for the per-kv-tile relay, which only the

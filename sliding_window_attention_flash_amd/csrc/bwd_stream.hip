@@ -124,6 +124,24 @@ __device__ __forceinline__ u32x2 lds_tr4(uint32_t a) {
   v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(uintptr_t)a);
   return __builtin_bit_cast(u32x2, v);
 }
+// Agent-coherent 16-byte store and load of fp32 partial sums through a raw
+// buffer resource with cache policy sc1: for each of the four words, the
+// same visibility across the XCDs' L2 caches as a relaxed agent-scope
+// atomic store or load (which compile to single-word sc1 stores and loads),
+// in one instruction per lane.  Offsets are bytes from the resource base;
+// the buffer unit drops stores at or past its size and reads zeros there.
+constexpr int kAgentCoherent = 16;  // CPol::SC1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(float* base, int64_t bytes) {
+  const int n = (int)min<int64_t>(bytes, INT32_MAX);
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, n, 0x00020000);
+}
+__device__ __forceinline__ void st_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kAgentCoherent);
+}
+__device__ __forceinline__ f32x4 ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAgentCoherent));
+}
+
 // a value the compiler must keep in a register as computed (no re-derivation)
 __device__ __forceinline__ uint32_t pin(uint32_t x) {
   asm("" : "+v"(x));
@@ -189,6 +207,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   const float* lseb = a.lse + s.stat0 + h * s.stat_hs;
   const float* deltab = a.delta + s.stat0 + h * s.stat_hs;
   float* accb = a.dq_acc + (s.stat0 + h * s.stat_hs) * SD;
+  // this (b, h)'s rows of the accumulator, for the relay's coherent accesses
+  const __amdgpu_buffer_rsrc_t accr = coherent_rsrc(accb, (int64_t)s.cap_q * SD * sizeof(float));
   float* stashb = a.dq_stash + (s.stat0 + h * s.stat_hs) * SD;
   int* semb = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles;
   V8 zero8;
@@ -327,13 +347,12 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         }
       }
     } else if (!earlier) {
-      // first visiting chunk of a boundary tile: turn 0, no wait
+      // first visiting chunk of a boundary tile: turn 0, no wait; the
+      // partial leaves with agent-coherent stores, whose completion the
+      // wait below observes before the turn is released
       if (qi < s.cap_q)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            __hip_atomic_exchange(accb + acc_off(i, e) + r, acc[e][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int e = 0; e < 2; ++e) st_coherent(accr, (uint32_t)acc_off(i, e) * sizeof(float), acc[e]);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) __hip_atomic_store(semb + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -359,8 +378,21 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 
   // ---- prologue -------------------------------------------------------------
   load_kv(j0, kBn, vBn);
-  take_kv(j0, kBn, vBn);
   int loaded_hi = q_lo(j0);  // the ring holds q-tiles [.., loaded_hi)
+  {
+    // the first kv-step's q-tiles: all loads (K / V's too) issued before
+    // the first store
+    const int n0 = min(n_iters(j0), NACT);
+    QRegs t0[NACT];
+#pragma unroll
+    for (int k = 0; k < NACT; ++k)
+      if (k < n0) load_q_tile(loaded_hi + k, t0[k]);
+#pragma unroll
+    for (int k = 0; k < NACT; ++k)
+      if (k < n0) store_q_tile(t0[k]);
+    loaded_hi += n0;
+  }
+  take_kv(j0, kBn, vBn);
   int acc_lo = q_lo(j0);     // q-tile held in dQa[0]
   QRegs pf[2];
 
@@ -615,17 +647,16 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       if (qi < s.cap_q) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float* ap = accb + acc_off(i, e);
+          // the turn holds the tile alone: a coherent read of the running
+          // sum, this chunk's add, and a coherent write for the next turn
+          const uint32_t off = (uint32_t)acc_off(i, e) * sizeof(float);
           const f32x4 mine = *reinterpret_cast<const f32x4*>(stashb + acc_off(i, e));
-          float out[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float old = __hip_atomic_fetch_add(ap + r, mine[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            out[r] = p.scale * (old + mine[r]);
-          }
-          if (turn == nv - 1)
+          const f32x4 sum = ld_coherent(accr, off) + mine;
+          if (turn < nv - 1)
+            st_coherent(accr, off, sum);
+          else
             *reinterpret_cast<u32x2*>(dqb + (int64_t)qi * rs_dq + 16 * (2 * wd + e) + 4 * gq) =
-                pack4<T>(out[0], out[1], out[2], out[3]);
+                pack4<T>(p.scale * sum[0], p.scale * sum[1], p.scale * sum[2], p.scale * sum[3]);
         }
       }
       __builtin_amdgcn_s_waitcnt(0);
