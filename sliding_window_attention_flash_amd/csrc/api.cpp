@@ -256,7 +256,14 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   pl->off_delta = off;
   off = align256(off + sizeof(float) * (size_t)pl->stat_rows);
   pl->off_acc = off;
-  if (!p.split_dq) off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
+  if (!p.split_dq) {
+    size_t acc_floats = (size_t)pl->stat_rows * p.D;
+    // the streaming kernel's unordered mode keeps each q-tile's partial sum
+    // in a 64-row slot of its own, indexed like the semaphores
+    if (p.stream && !desc->deterministic)
+      acc_floats = std::max(acc_floats, (size_t)p.B * p.Hq * p.n_q_tiles * swa::kTile * p.D);
+    off = align256(off + sizeof(float) * acc_floats);
+  }
   pl->off_stash = off;
   if (p.stream && desc->deterministic) off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
   pl->off_sem = off;

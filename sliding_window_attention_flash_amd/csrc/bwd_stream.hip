@@ -210,6 +210,12 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   // this (b, h)'s rows of the accumulator, for the relay's coherent accesses
   const __amdgpu_buffer_rsrc_t accr = coherent_rsrc(accb, (int64_t)s.cap_q * SD * sizeof(float));
   float* stashb = a.dq_stash + (s.stat0 + h * s.stat_hs) * SD;
+  // unordered mode: q-tile i's fp32 partial sum sits in a slot of its own
+  // (indexed like the semaphores), lane-contiguous: element (wave w, e, r) of
+  // lane l at ((2 w + e) 4 + r) 64 + l, so one atomic instruction adds into
+  // 256 contiguous bytes (measured 3.5x cheaper than 16 rows x 4 words)
+  float* slotb = a.dq_acc + ((int64_t)b * p.Hq + h) * p.n_q_tiles * (kTile * SD);
+  const int slot_lane = 4 * 64 * 2 * w + l;
   int* semb = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles;
   V8 zero8;
 #pragma unroll
@@ -321,11 +327,12 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
               pack4<T>(p.scale * acc[e][0], p.scale * acc[e][1], p.scale * acc[e][2], p.scale * acc[e][3]);
       }
     } else if (!RELAY) {
+      float* slot = slotb + (int64_t)i * (kTile * SD) + slot_lane;
       if (qi < s.len_q)
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(accb + acc_off(i, e) + r, acc[e][r]);
+          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(slot + (4 * e + r) * 64, acc[e][r]);
       // The visiting chunk whose adds complete last converts the tile: every
       // thread waits for its agent-scope atomics, then one thread counts the
       // chunk in; the chunk that completes the count reads the sums back
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            v[r] = p.scale * __hip_atomic_load(accb + acc_off(i, e) + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v[r] = p.scale * __hip_atomic_load(slot + (4 * e + r) * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           *reinterpret_cast<u32x2*>(row + 16 * e) = pack4<T>(v[0], v[1], v[2], v[3]);
         }
       }
