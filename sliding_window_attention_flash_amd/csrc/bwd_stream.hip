@@ -221,9 +221,6 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) zero8[e] = Elem<T>::from_float(0.f);
 
-  // bands start (and their guard positions stay) zero
-  for (int e = tid; e < NWAVE * 16 * BP / 8; e += NTHR) reinterpret_cast<V8*>(&sBand[0][0])[e] = zero8;
-
   // ---- per-lane LDS offsets (elements) --------------------------------------
   int rd_off[2];  // row read of a 16-row block: row c, chunk 4 ks + gq
 #pragma unroll
@@ -394,6 +391,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < NACT; ++k)
       if (k < n0) load_q_tile(loaded_hi + k, t0[k]);
+    // While they are in flight: the bands start (and their guard positions
+    // stay) zero, and so does the ring, so that a ring slot read before any
+    // tile was staged in it holds finite values (see the pair geometry).
+    for (int e = tid; e < NWAVE * 16 * BP / 8; e += NTHR) reinterpret_cast<V8*>(&sBand[0][0])[e] = zero8;
+    for (int e = tid; e < 2 * NRB * 16 * TROW / 8; e += NTHR) reinterpret_cast<V8*>(&sRing[0][0][0])[e] = zero8;
+    for (int e = tid; e < 2 * NRB * 16 / 4; e += NTHR)
+      reinterpret_cast<f32x4*>(&sLD[0][0][0])[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < NACT; ++k)
       if (k < n0) store_q_tile(t0[k]);
@@ -460,20 +465,15 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     struct PairSD {
       f32x4 S0, D0, S1, D1;
     };
-    // Pair pr holds the band's blocks b0 = blo + 2 pr and b0 + 1, at ring
-    // positions m0, m1 (consecutive modulo NRB).  A block before row 0 (only
-    // at a sequence start, where q-tile 0 is in the ring) reads block 0, and a
-    // block past the band reads its partner; both are masked out entirely.
+    // Pair pr holds the band's blocks blo + 2 pr and blo + 2 pr + 1; block
+    // blo + n sits at ring position (mlo + n) mod NRB.  A block before row 0
+    // (only at a sequence start) or past bhi is masked out entirely; the
+    // ring slot it reads holds finite values -- zeros from the kernel start
+    // or rows staged earlier -- so its masked products add exact zeros.
     const int mlo = ((blo % NRB) + NRB) % NRB;
-    auto pair_rows = [&](int pr, int& b0, int& m0, int& m1, bool& has0, bool& has1) {
-      b0 = blo + 2 * pr;
-      has0 = b0 >= 0;
-      has1 = b0 + 1 >= 0 && b0 + 1 <= bhi;
-      int mm = mlo + 2 * pr;
-      mm = mm >= NRB ? mm - NRB : mm;
-      const int mn = mm + 1 == NRB ? 0 : mm + 1;
-      m0 = has0 ? mm : 0;
-      m1 = has1 ? mn : (b0 + 1 < 0 ? 0 : m0);
+    auto ring_pos = [&](int n) {  // n < 2 NPAIR <= NRB
+      const int m = mlo + n;
+      return m >= NRB ? m - NRB : m;
     };
     // LDS byte addresses of ring block m (Q; the dO rows are QO_DO bytes
     // further) and of its LSE values (delta: LD_DL bytes further)
@@ -482,10 +482,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     auto ld_addr = [&](int m) { return ring_ld + (uint32_t)m * (16 * sizeof(float)); };
     // S = Q K^T and dP = dO V^T of both blocks
     auto stage_sdp = [&](int pr) {
-      int b0, m0, m1;
-      bool has0, has1;
-      pair_rows(pr, b0, m0, m1, has0, has1);
-      const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
+      const uint32_t a0 = blk_addr(ring_pos(2 * pr)), a1 = blk_addr(ring_pos(2 * pr + 1));
       PairSD r;
       r.S0 = r.D0 = r.S1 = r.D1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -500,9 +497,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     };
     // P, dS, the band write and dV^T += dO^T P, dK^T += Q^T dS
     auto stage_grad = [&](int pr, const PairSD& r) {
-      int b0, m0, m1;
-      bool has0, has1;
-      pair_rows(pr, b0, m0, m1, has0, has1);
+      const int b0 = blo + 2 * pr, m0 = ring_pos(2 * pr), m1 = ring_pos(2 * pr + 1);
+      const bool has0 = b0 >= 0, has1 = b0 + 1 >= 0 && b0 + 1 <= bhi;
       const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
       const uint32_t l0 = pin(ld_addr(m0) + ld_off_b), l1 = pin(ld_addr(m1) + ld_off_b);
       const f32x4 lse0 = lds_ld<f32x4>(l0), del0 = lds_ld<f32x4>(l0 + LD_DL);
@@ -603,17 +599,17 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         store_dkdv(ks);
-        bool any = false;
-#pragma unroll
-        for (int k = 0; k < NACT; ++k) any |= k < nit && (unsigned)(4 * k - 2 * ks + c0 - 1) <= (unsigned)nb;
-        if (!any) continue;
+        // the active k, klo <= k <= khi: 0 <= 4 k - 2 ks + c0 - 1 <= nb and
+        // k < nit, as a bit mask
+        const int klo = max((2 * ks - c0 + 4) >> 2, 0), khi = min((nb + 1 + 2 * ks - c0) >> 2, nit - 1);
+        const unsigned act = khi < klo ? 0u : ((2u << khi) - 1u) & ~((1u << klo) - 1u);
+        if (act == 0u) continue;
         const T* kr = sK + 32 * ks * TROW;
         const V8 kt0 = tr_two(kr + tr_off_k0, kr + 16 * TROW + tr_off_k0);
         const V8 kt1 = tr_two(kr + tr_off_k1, kr + 16 * TROW + tr_off_k1);
 #pragma unroll
         for (int k = 0; k < NACT; ++k) {
-          if (k >= nit) break;
-          if ((unsigned)(4 * k - 2 * ks + c0 - 1) > (unsigned)nb) continue;
+          if (!((act >> k) & 1u)) continue;
           const uint32_t ya = bbase + (uint32_t)(2 * ks * 16 * BP * sizeof(T)) + 32 * (4 * k - 2 * ks);
           const u32x2 lo = lds_tr4(ya), hi = lds_tr4(ya + 16 * BP * sizeof(T) - 32);
           const V8 st = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
