@@ -53,6 +53,8 @@
 // lane i receives element (i % 4) of lanes i / 4 + 4e (e = 0..3), so a lane
 // pointing at row r0 + i / 4, column c0 + 4 (i % 4) receives rows
 // r0 .. r0 + 3 of column c0 + i.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace swa {
@@ -419,21 +421,25 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     __syncthreads();  // T: ring ready; sK and the bands are free
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<V8*>(&sK[tile_off(16 * w + c, 4 * ks + gq)]) = kB[ks];
-    // realign dQa[0] with q_lo(j); q_lo advances by two q-tiles per step
-    // except where it is clamped at the sequence start
-    while (acc_lo < qlo) {
-      const int sh = min(qlo - acc_lo, 2);
+    // realign dQa[0] with q_lo(j): q_lo advances by two q-tiles per step
+    // except where it is clamped at the sequence start, so the shift is a
+    // block-uniform 2 (plain register moves) or, once per sequence, 1
+    auto shift_acc = [&](auto by) {
+      constexpr int SH = decltype(by)::value;
 #pragma unroll
-      for (int k = 0; k < NACT; ++k) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 a0 = k + 2 < NACT ? dQa[min(k + 2, NACT - 1)][0] : z;
-        const f32x4 a1 = k + 2 < NACT ? dQa[min(k + 2, NACT - 1)][1] : z;
-        const f32x4 b0 = k + 1 < NACT ? dQa[min(k + 1, NACT - 1)][0] : z;
-        const f32x4 b1 = k + 1 < NACT ? dQa[min(k + 1, NACT - 1)][1] : z;
-        dQa[k][0] = sh == 2 ? a0 : b0;
-        dQa[k][1] = sh == 2 ? a1 : b1;
+      for (int k = 0; k < NACT; ++k)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          dQa[k][e] = k + SH < NACT ? dQa[min(k + SH, NACT - 1)][e] : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    while (acc_lo < qlo) {
+      if (qlo - acc_lo >= 2) {
+        shift_acc(std::integral_constant<int, 2>());
+        acc_lo += 2;
+      } else {
+        shift_acc(std::integral_constant<int, 1>());
+        acc_lo += 1;
       }
-      acc_lo += sh;
     }
 
     // Prefetch of the next kv-step -- its K / V rows and new q-tiles -- is
@@ -526,9 +532,6 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const u32x2 s1 = pack4<T>(dsv[4], dsv[5], dsv[6], dsv[7]);
       const V8 pP = __builtin_bit_cast(V8, u32x4{p0[0], p0[1], p1[0], p1[1]});
       const V8 pS = __builtin_bit_cast(V8, u32x4{s0[0], s0[1], s1[0], s1[1]});
-      // dS^T of blocks b0, b1 at band positions 2 pr + 1, 2 pr + 2
-      *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 1)) = s0;
-      *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 2)) = s1;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const uint32_t y0 = pin(a0 + tr_off_b[db]), y1 = pin(a1 + tr_off_b[db]);
@@ -537,6 +540,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         dVa[db] = mfma16(__builtin_bit_cast(V8, u32x4{o_lo[0], o_lo[1], o_hi[0], o_hi[1]}), pP, dVa[db]);
         dKa[db] = mfma16(__builtin_bit_cast(V8, u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}), pS, dKa[db]);
       }
+      // dS^T of blocks b0, b1 at band positions 2 pr + 1, 2 pr + 2 (after the
+      // pair's ring reads, which the stores would otherwise hold back)
+      *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 1)) = s0;
+      *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 2)) = s1;
     };
     // Software pipeline: the products of pair pr + 1 are issued in the same
     // straight-line block as the softmax and gradients of pair pr.
