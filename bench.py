@@ -19,7 +19,8 @@ FLOPs count attended (query, key) pairs only: 10 * head_dim per pair per
 query head for the backward, 4 * head_dim for the forward.  The roofline
 entry is for the dominant kernel (the streaming main kernel at the default
 workload), timed with HIP events recorded on its launch stream around every
-launch.  Its ``traffic`` is the HBM bytes per launch that rocprofv3's
+launch of a second run of as many steps (the timed steps themselves run
+uninstrumented, since the event packets lengthen a step).  Its ``traffic`` is the HBM bytes per launch that rocprofv3's
 FETCH_SIZE and WRITE_SIZE counters read for it, each divided by what the
 same counter reads per byte for an elementwise copy of known size; the
 figures are kept in a text summary under profiles/ together with a hash of
@@ -121,12 +122,19 @@ def time_backward(w, steps, warmup, seed=0, forward=False):
         ev.append(e)
     for _ in range(warmup):
         bw.run()
+    # the timed steps, uninstrumented
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        bw.run()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    # the same number of steps again, with HIP events recorded on the launch
+    # stream around the main kernel of each (the events add stream packets,
+    # so these steps are not the timed ones)
     for s in range(steps):
         bw.run_events(ev[2 * s].value, ev[2 * s + 1].value)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
     main_ms = []
     for s in range(steps):
         ms = ctypes.c_float()
@@ -201,7 +209,8 @@ def _find(d, suffix):
 
 def _timed_launch_avg_us(d, steps):
     """Average duration (us) of the main kernel over its last ``steps``
-    dispatches in the kernel trace (the timed ones; warm-up precedes them)."""
+    dispatches in the kernel trace (the event-timed ones, which follow the
+    warm-up and the uninstrumented timed steps)."""
     rows = [r for r in _rows(_find(d, "kernel_trace.csv")) if MAIN_KERNEL in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     last = rows[-steps:]
@@ -225,7 +234,7 @@ def summarize_stats(d, out, command, bench_json=None, steps=None, workload="c3")
                   f"    main_kernel_ms = {b['extra']['main_kernel_ms']:.4f}, ms_per_step = {b['ms_per_step']:.4f}"]
     if steps and any(MAIN_KERNEL in r["Name"] for r in rows):
         avg, n = _timed_launch_avg_us(d, steps)
-        lines += ["", f"{MAIN_KERNEL} over the timed launches (last {n} dispatches of the kernel trace): "
+        lines += ["", f"{MAIN_KERNEL} over the event-timed launches (last {n} dispatches of the kernel trace): "
                       f"avg {avg:.2f} us"]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
