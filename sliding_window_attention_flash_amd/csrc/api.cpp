@@ -259,9 +259,14 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   if (!p.split_dq) {
     size_t acc_floats = (size_t)pl->stat_rows * p.D;
     // the streaming kernel's unordered mode keeps each q-tile's partial sum
-    // in a 64-row slot of its own, indexed like the semaphores
-    if (p.stream && !desc->deterministic)
-      acc_floats = std::max(acc_floats, (size_t)p.B * p.Hq * p.n_q_tiles * swa::kTile * p.D);
+    // in a 64-row slot of its own (stream_slot: dense B x Hq x n_q_tiles
+    // slots, packed Hq x (total_q / 64 + B + 1))
+    if (p.stream && !desc->deterministic) {
+      const size_t slots = p.layout == swa::LAYOUT_THD
+                               ? (size_t)p.Hq * (size_t)((p.total_q >> 6) + p.B + 1)
+                               : (size_t)p.B * p.Hq * p.n_q_tiles;
+      acc_floats = std::max(acc_floats, slots * swa::kTile * p.D);
+    }
     off = align256(off + sizeof(float) * acc_floats);
   }
   pl->off_stash = off;

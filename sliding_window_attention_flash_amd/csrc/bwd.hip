@@ -134,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
   // chunk of the streaming kernel) visits, where no other kernel writes them
   // (the relay, and the streaming kernel in either mode; the q-major dQ
   // pass of the per-tile path writes its own zeros); and in the streaming
-  // kernel's atomic mode the fp32 partial-sum slots (one per q-tile, indexed
-  // like the semaphores) of q-tiles several chunks visit.
+  // kernel's atomic mode the fp32 partial-sum slots (one per q-tile) of
+  // q-tiles several chunks visit.
   SeqSched g;
   main_sched(p, s, g);
   for (int t = 0; t < DOT_TILES; ++t) {
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
       for (int e = tid; e < rows * CH; e += kThreads)
         st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
     } else if (!a.deterministic && nv > 1) {
-      float4* acc = reinterpret_cast<float4*>(a.dq_acc + (((int64_t)b * p.Hq + h) * p.n_q_tiles + tile) * kTile * D);
+      float4* acc = reinterpret_cast<float4*>(a.dq_acc + stream_slot(p, s, b, h, tile) * kTile * D);
       const float4 z = {0.f, 0.f, 0.f, 0.f};
       for (int e = tid; e < kTile * (D / 4); e += kThreads) acc[e] = z;
     }

@@ -212,11 +212,11 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   // this (b, h)'s rows of the accumulator, for the relay's coherent accesses
   const __amdgpu_buffer_rsrc_t accr = coherent_rsrc(accb, (int64_t)s.cap_q * SD * sizeof(float));
   float* stashb = a.dq_stash + (s.stat0 + h * s.stat_hs) * SD;
-  // unordered mode: q-tile i's fp32 partial sum sits in a slot of its own
-  // (indexed like the semaphores), lane-contiguous: element (wave w, e, r) of
-  // lane l at ((2 w + e) 4 + r) 64 + l, so one atomic instruction adds into
-  // 256 contiguous bytes (measured 3.5x cheaper than 16 rows x 4 words)
-  float* slotb = a.dq_acc + ((int64_t)b * p.Hq + h) * p.n_q_tiles * (kTile * SD);
+  // unordered mode: q-tile i's fp32 partial sum sits in a 64-row slot of its
+  // own (stream_slot), lane-contiguous: element (wave w, e, r) of lane l at
+  // ((2 w + e) 4 + r) 64 + l, so one atomic instruction adds into 256
+  // contiguous bytes (measured 3.5x cheaper than 16 rows x 4 words)
+  float* slotb = a.dq_acc + stream_slot(p, s, b, h, 0) * (kTile * SD);
   const int slot_lane = 4 * 64 * 2 * w + l;
   int* semb = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles;
   V8 zero8;

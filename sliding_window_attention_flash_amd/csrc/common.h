@@ -144,6 +144,17 @@ __device__ __forceinline__ void main_sched(const Problem& p, const Seq& s, SeqSc
          p.stream ? p.step_kv : kTile);
 }
 
+// Streaming kernel, unordered mode: index of the 64-row fp32 partial-sum
+// slot of q-tile i of (sequence b, head h).  Dense: b, h, i row-major over
+// n_q_tiles per (b, h).  Packed (THD): per head, sequence b's slots start at
+// floor(q0 / 64) + b, where q0 is its first packed row; consecutive
+// sequences never overlap (floor(x) - floor(y) + 1 >= ceil(x - y)), and a
+// head needs at most total_q / 64 + B + 1 slots.
+__device__ __forceinline__ int64_t stream_slot(const Problem& p, const Seq& s, int b, int h, int i) {
+  if (p.layout == LAYOUT_THD) return (int64_t)h * ((p.total_q >> 6) + p.B + 1) + (s.row0_q >> 6) + b + i;
+  return ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
+}
+
 // Streaming kernel: number of chunks (blocks) that visit q-tile i.  A q-tile
 // with more than one visiting chunk is a boundary tile whose dQ goes through
 // the fp32 accumulator (relay or atomics); the others are written directly.

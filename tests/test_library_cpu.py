@@ -119,6 +119,44 @@ def test_workspace_size_formula(lib, det):
     assert plan.workspace_bytes == expect
 
 
+def _sections(*nbytes):
+    total = 0
+    for n in nbytes:
+        total = (total + n + 255) // 256 * 256
+    return total
+
+
+@pytest.mark.parametrize("det", [0, 1])
+def test_streaming_workspace_size(lib, det):
+    # multi-head, causal, window <= 128, head_dim 64: the streaming kernel.
+    # Unordered: one 64-row fp32 slot per (batch, head, q-tile) for the
+    # boundary partials; ordered: the partial rows plus the relay stash.
+    B, H, S, D = 2, 4, 300, 64
+    plan = api.sdpa_bwd_plan(_desc(B=B, Hq=H, Hkv=H, D=D, Sq=S, Skv=S, window_left=128, deterministic=det))
+    rows, ntq = B * H * S, 5
+    acc = 4 * B * H * ntq * 64 * D if det == 0 else 4 * rows * D
+    stash = 4 * rows * D if det == 1 else 0
+    assert plan.workspace_bytes == _sections(4 * rows, acc, stash, 4 * B * H * ntq, 16, 4 * H * B * ntq)
+
+
+def test_streaming_workspace_packed_scales_with_rows_not_batch_times_longest(lib):
+    # packed layout, 200 short sequences and one long one: the unordered
+    # mode's partial-sum slots follow the packed rows (per head at most
+    # total_q / 64 + B + 1 slots), not batch x the longest sequence's tiles
+    B, H, D, S = 201, 4, 64, 32768
+    T = 200 * 64 + S
+    g = api.Geometry(_lib.SDPA_LAYOUT_THD, B, H, H, D, S, S, T, T)
+    q = torch.empty(T, H, D, dtype=torch.bfloat16)
+    d = api.make_desc(g, torch.bfloat16, q=q, k=q, v=q, o=q, dO=q, dq=q, dk=q, dv=q, window_left=128,
+                      has_seq_lens=True)
+    plan = api.sdpa_bwd_plan(d)
+    rows, ntq = H * T, S // 64
+    slots = H * ((T >> 6) + B + 1)
+    acc = 4 * max(rows * D, slots * 64 * D)
+    assert plan.workspace_bytes == _sections(4 * rows, acc, 4 * B * H * ntq, 16, 4 * H * B * ntq)
+    assert plan.workspace_bytes < 3 * 4 * rows * D
+
+
 # ---- the window-bounded schedule, brute force ------------------------------------
 
 
