@@ -63,9 +63,13 @@ __device__ __forceinline__ void relay_release(int* semp, int turn, int nv, int t
 // ---------------------------------------------------------------------------
 // bwd_dot: one block per (group of DOT_TILES q-tiles, query head, sequence).
 // Every thread issues all of its O / dO loads before the first product, so
-// a block keeps DOT_TILES * 64 rows of loads in flight.
+// a block keeps DOT_TILES * 64 rows of loads in flight.  One q-tile per block
+// (measured on MI355X against 2 and 4): the same speed on long sequences,
+// where the pass runs at the read bandwidth, and more blocks in flight on
+// short ones, where it is latency-bound (batch 2, 16 heads, S = 4096: the
+// whole backward step 66 -> 62 us).
 
-constexpr int DOT_TILES = 4;
+constexpr int DOT_TILES = 1;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
