@@ -4,6 +4,7 @@
     python bench.py --copy-calibration ...      (appends a copy of known size)
     python bench.py --summarize-stats DIR --out FILE --command CMD
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --out FILE --command CMD
+    python bench.py --summarize-counters PMC_DIR... --out FILE --command CMD... --workload W
 
 A step is one full backward, sdpa_bwd_run: the dot preprocess, the main
 window-bounded kernel with its dQ accumulation (ordered relay, fp32 atomics
@@ -293,6 +294,51 @@ def summarize_traffic(fetch_dir, write_dir, out, command, workload):
     print("\n".join(lines))
 
 
+SQ_KERNELS = ("bwd_stream_kernel", "bwd_main_kernel", "bwd_dq_kernel", "bwd_dot_kernel", "bwd_dsink_kernel",
+              "fwd_kernel")
+CLOCK_GHZ = 2.4   # MI355X peak engine clock
+N_SIMD = 256 * 4  # compute units x SIMDs
+
+
+def summarize_counters(dirs, out, commands, workload):
+    """Per-kernel averages (per dispatch) of SQ counters from rocprofv3 --pmc
+    runs, with instructions per wave and the MFMA-busy fraction of the
+    kernel's SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES, summed over SIMDs, over
+    dispatch duration x 2.4 GHz x 1024 SIMDs)."""
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(dict))
+    dur = collections.defaultdict(dict)
+    for d in dirs:
+        for r in _rows(_find(d, "counter_collection.csv")):
+            k = next((n for n in SQ_KERNELS if n in r["Kernel_Name"]), None)
+            if k is None:
+                continue
+            key = (d, r["Dispatch_Id"])
+            vals[k][r["Counter_Name"]][key] = vals[k][r["Counter_Name"]].get(key, 0.0) + float(r["Counter_Value"])
+            dur[k][key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    lines = [f"# SQ counters per kernel, workload {workloads()[workload].name}", "",
+             "commands (one rocprofv3 --pmc pass each):"] + [f"    {c}" for c in commands] + [""]
+    for k in SQ_KERNELS:
+        if k not in vals:
+            continue
+        avg = {c: sum(v.values()) / len(v) for c, v in vals[k].items()}
+        d_ns = sum(dur[k].values()) / len(dur[k])
+        lines.append(f"{k}: {len(dur[k])} dispatches, {d_ns / 1e3:.1f} us per dispatch under the counters")
+        for c in sorted(avg):
+            lines.append(f"    {c:28s} {avg[c]:14.4g}")
+        waves = avg.get("SQ_WAVES")
+        if waves:
+            per = {c[len('SQ_INSTS_'):]: avg[c] / waves for c in avg if c.startswith("SQ_INSTS_")}
+            lines.append("    instructions per wave      " + ", ".join(f"{c} {v:.0f}" for c, v in sorted(per.items())))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            frac = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (d_ns * CLOCK_GHZ * N_SIMD)
+            lines.append(f"    MFMA busy / SIMD cycles    {frac:.3f}")
+        lines.append("")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def cpu_baseline(w):
     """The fp64 oracle's backward timed on the whole workload when it is a
     dense multi-head one (the oracle runs one (sequence, kv head) unit per
@@ -330,6 +376,7 @@ def main():
                     help=f"after timing, copy {COPY_BYTES} bytes three times (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR")
     ap.add_argument("--bench-json")
     ap.add_argument("--out")
     ap.add_argument("--command", action="append", default=[])
@@ -340,6 +387,9 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.out, args.command, args.workload)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.out, args.command, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the timed kernel is "
