@@ -50,6 +50,11 @@ SMALL = [
     # s_kv + W see no key, so a run ends in q-tiles no kv-tile visits
     _wl("gqa_tl_sq_gt_skv_w40_runs", BF16, 2, 4, 2, 64, 520, 130, window_left=40),
     _wl("gqa_br_w60_d128_runs_f16", F16, 1, 6, 2, 128, 700, 900, bottom_right=True, window_left=60),
+    # softmax scales other than 1/sqrt(head_dim) (and not a power of two):
+    # the streaming kernel and the per-tile path
+    _wl("stream_tl_w64_scale0p3", BF16, 1, 2, 2, 64, 500, 500, window_left=64, scale=0.3),
+    _wl("gqa_br_w50_d128_scale0p2_f16", F16, 1, 4, 2, 128, 200, 260, bottom_right=True, window_left=50,
+        scale=0.2),
 ]
 
 
