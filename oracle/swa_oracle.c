@@ -25,19 +25,32 @@
 
 /* ---- element access ---------------------------------------------------- */
 
+/* IEEE binary16: sign, 5 exponent bits (bias 15), 10 fraction bits. */
 static double f16_to_double(uint16_t h) {
   int s = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
   double v;
   if (e == 0)
+#if ORACLE_MUTANT == 11
+    v = ldexp((double)m, -25);
+#else
     v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+#endif
   else if (e == 31)
     v = m ? NAN : INFINITY;
   else
+#if ORACLE_MUTANT == 10
+    v = ldexp((double)(m | 0x400), e - 24);
+#else
     v = ldexp((double)(m | 0x400), e - 25); /* (1024 + m) * 2^(e - 25) */
+#endif
   return s ? -v : v;
 }
 
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
 static double bf16_to_double(uint16_t h) {
+#if ORACLE_MUTANT == 13
+  if (((h >> 7) & 0xff) == 0) h &= 0x8000; /* subnormals flushed to zero */
+#endif
   uint32_t u = (uint32_t)h << 16;
   float f;
   memcpy(&f, &u, sizeof f);
@@ -45,6 +58,9 @@ static double bf16_to_double(uint16_t h) {
 }
 
 static double ld(const void* base, int dtype, int64_t idx) {
+#if ORACLE_MUTANT == 12
+  if (dtype != ORACLE_F64) dtype = dtype == ORACLE_BF16 ? ORACLE_F16 : ORACLE_BF16;
+#endif
   switch (dtype) {
     case ORACLE_BF16: return bf16_to_double(((const uint16_t*)base)[idx]);
     case ORACLE_F16: return f16_to_double(((const uint16_t*)base)[idx]);

@@ -410,5 +410,67 @@ def check_sampled_rows(lib=None):
         _close(dv[s], r["dv"][bk[s], hk[s], js[s]], 1e-14, "dv row")
 
 
+def finite_bit_patterns(dtype):
+    """Every finite value of a 16-bit float type, as a 1-D tensor of that
+    type: all 65536 bit patterns except the all-ones exponent (inf / NaN).
+    Covers both zeros, every subnormal and the largest finite values."""
+    bits = torch.arange(1 << 16, dtype=torch.int32)
+    exp_mask = 0x7F80 if dtype == torch.bfloat16 else 0x7C00
+    keep = (bits & exp_mask) != exp_mask
+    return bits[keep].to(torch.int16).view(dtype)
+
+
+def _as_rows(vals, D, fill=0.0):
+    """Pads a 1-D tensor to a multiple of D and shapes it [1, 1, rows, D]."""
+    n = -(-vals.numel() // D)
+    out = torch.full((n * D,), fill, dtype=vals.dtype)
+    out[:vals.numel()] = vals
+    return out.view(1, 1, n, D)
+
+
+def check_widening(lib=None):
+    """The oracle's exact widening of bf16 / f16 storage to fp64, pinned to
+    torch's own conversion (an independent routine) through closed forms of
+    the window-0 mask, where each row sees only its anchor key, so P = 1:
+      * O_i = V_i and dV_j = dO_j exactly, with V and dO holding every finite
+        bit pattern of the type (both zeros, all subnormals, the extremes);
+      * LSE_i = scale * <Q_i, K_i> = Q_i0 when K_i = e_0 and scale = 1, and
+        K_i0 when Q_i = e_0: every finite pattern through Q and through K.
+    Then the problems of the torch cross-check, stored as 16-bit values, give
+    bitwise the results of the same values stored as fp64."""
+    for dt in (torch.bfloat16, torch.float16):
+        pat = finite_bit_patterns(dt)
+        v = _as_rows(pat, 8)
+        dO = _as_rows(pat.flip(0), 8)
+        n = v.shape[2]
+        p = Problem.dense(1, 1, 1, n, n, 8, causal=True, window_left=0, scale=1.0)
+        zero = torch.zeros_like(v)
+        r = oracle.backward(p, zero, zero, v, dO, None, lib=lib)
+        assert torch.equal(r["o"], v.to(F64)), f"{dt}: O != V widened by torch"
+        assert torch.equal(r["dv"], dO.to(F64)), f"{dt}: dV != dO widened by torch"
+        # every pattern in column 0 of Q (then of K), the other operand e_0
+        col = torch.zeros(pat.numel(), 8, dtype=dt)
+        col[:, 0] = pat
+        e0 = torch.zeros(pat.numel(), 8, dtype=dt)
+        e0[:, 0] = 1.0
+        col, e0 = col.view(1, 1, -1, 8), e0.view(1, 1, -1, 8)
+        m = col.shape[2]
+        pm = Problem.dense(1, 1, 1, m, m, 8, causal=True, window_left=0, scale=1.0)
+        want = pat.to(F64).view(1, 1, m)
+        for name, qq, kk in (("Q", col, e0), ("K", e0, col)):
+            _, lse = oracle.forward(pm, qq, kk, e0, None, lib=lib)
+            assert torch.equal(lse, want), f"{dt}: LSE != {name} widened by torch"
+    # 16-bit storage against fp64 storage of the same values: bitwise equal
+    for n, c in enumerate(FD_CASES[:4]):
+        p, q, k, v, dO, sink = make_fd_case(c, 300 + n)
+        for dt in (torch.bfloat16, torch.float16):
+            q16, k16, v16, dO16 = (t.to(dt) for t in (q, k, v, dO))
+            r16 = oracle.backward(p, q16, k16, v16, dO16, sink, lib=lib)
+            r64 = oracle.backward(p, *(t.to(F64) for t in (q16, k16, v16, dO16)), sink, lib=lib)
+            for key in ("o", "lse", "dq", "dk", "dv"):
+                assert torch.equal(r16[key], r64[key]), f"{dt} storage differs from fp64 in {key} (case {n})"
+
+
 ALL_CHECKS = [check_finite_differences, check_torch_autograd, check_torch_sdpa_causal,
-              check_closed_forms, check_invariants, check_dense_scan, check_sampled_rows]
+              check_closed_forms, check_invariants, check_dense_scan, check_sampled_rows,
+              check_widening]

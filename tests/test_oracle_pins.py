@@ -37,6 +37,10 @@ def test_sampled_rows_match_full(oracle_lib):
     oc.check_sampled_rows()
 
 
+def test_16bit_widening_every_finite_pattern(oracle_lib):
+    oc.check_widening()
+
+
 @pytest.mark.parametrize("S,W,per_seq", [(256, 64, 14560), (4096, 128, 520128), (32768, 128, 4218816)])
 def test_attended_pairs_closed_form(oracle_lib, S, W, per_seq):
     # top-left causal + inclusive window W: row i sees min(i, W) + 1 keys, so
@@ -71,6 +75,10 @@ MUTANTS = {
     7: "dSink sign flipped",
     8: "GQA head map h % H_kv instead of h / G",
     9: "exclusive right band (j - anchor < R)",
+    10: "f16 exponent bias off by one (2^(e - 24))",
+    11: "f16 subnormal scale 2^-25 instead of 2^-24",
+    12: "bf16 and f16 storage codes swapped",
+    13: "bf16 subnormals flushed to zero",
 }
 
 
