@@ -378,25 +378,31 @@ sdpa_status sdpa_bwd_schedule(const sdpa_bwd_plan_t* pl, int32_t len_q, int32_t 
                               int32_t* q_hi, int32_t q_cap, int32_t* kv_first, int32_t* kv_last) {
   if (!pl) return fail(SDPA_ERR_INVALID_ARG, "plan is NULL");
   if (len_q < 0 || len_kv < 0) return fail(SDPA_ERR_INVALID_ARG, "len_q %d / len_kv %d must be >= 0", len_q, len_kv);
-  swa::SeqSched g;
+  // The streaming kernel evaluates its schedule in the shift form of
+  // StreamSched with the plan's window; the per-tile kernels use SeqSched.
+  // Reporting what each kernel itself computes lets host tests check the
+  // form that runs.
   const int tkv = pl->prob.step_kv;
+  swa::SeqSched g;
   g.init(len_q, len_kv, pl->desc.bottom_right, pl->desc.causal, clamp_band(pl->desc.window_left, len_q, len_kv),
          clamp_band(pl->desc.window_right, len_q, len_kv), kTile, tkv);
+  swa::StreamSched gs;
+  gs.init(len_q, len_kv, pl->desc.bottom_right, pl->prob.window);
+  const bool stream = pl->prob.stream;
+  const int nq = stream ? gs.n_q_tiles : g.n_q_tiles, nk = stream ? gs.n_kv_tiles : g.n_kv_tiles;
   if (tile_q) *tile_q = kTile;
   if (tile_kv) *tile_kv = tkv;
-  if (n_q) *n_q = g.n_q_tiles;
-  if (n_kv) *n_kv = g.n_kv_tiles;
-  if ((q_lo || q_hi) && kv_cap < g.n_kv_tiles)
-    return fail(SDPA_ERR_INVALID_ARG, "kv_cap %d < %d kv-tiles", kv_cap, g.n_kv_tiles);
-  if ((kv_first || kv_last) && q_cap < g.n_q_tiles)
-    return fail(SDPA_ERR_INVALID_ARG, "q_cap %d < %d q-tiles", q_cap, g.n_q_tiles);
-  for (int j = 0; j < g.n_kv_tiles; ++j) {
-    if (q_lo) q_lo[j] = g.q_lo(j);
-    if (q_hi) q_hi[j] = g.q_hi(j);
+  if (n_q) *n_q = nq;
+  if (n_kv) *n_kv = nk;
+  if ((q_lo || q_hi) && kv_cap < nk) return fail(SDPA_ERR_INVALID_ARG, "kv_cap %d < %d kv-tiles", kv_cap, nk);
+  if ((kv_first || kv_last) && q_cap < nq) return fail(SDPA_ERR_INVALID_ARG, "q_cap %d < %d q-tiles", q_cap, nq);
+  for (int j = 0; j < nk; ++j) {
+    if (q_lo) q_lo[j] = stream ? gs.q_lo(j) : g.q_lo(j);
+    if (q_hi) q_hi[j] = stream ? gs.q_hi(j) : g.q_hi(j);
   }
-  for (int i = 0; i < g.n_q_tiles; ++i) {
-    if (kv_first) kv_first[i] = g.kv_first(i);
-    if (kv_last) kv_last[i] = g.kv_last(i);
+  for (int i = 0; i < nq; ++i) {
+    if (kv_first) kv_first[i] = stream ? gs.kv_first(i) : g.kv_first(i);
+    if (kv_last) kv_last[i] = stream ? gs.kv_last(i) : g.kv_last(i);
   }
   g_err[0] = 0;
   return SDPA_OK;

@@ -72,6 +72,11 @@ constexpr int NPAIR = 5;      // block pairs a band holds
 constexpr int BPOS = 2 * NPAIR + 2;  // band block positions, guards included
 constexpr int BP = 208;       // band row pitch (elements), >= 16 * BPOS
 
+static_assert(STEP == StreamSched::kStep && kTile == StreamSched::kTileQ,
+              "the kernel's kv-step and q-tile are the shift forms' tiles");
+static_assert(NACT >= (STEP + 128) / 64 + 1, "a kv-step feeds at most ceil((128 + W) / 64) + 1 q-tiles, W <= 128");
+static_assert(2 * NPAIR >= (16 + 128 + 15) / 16 + 1, "a 16-key band spans at most 10 16-row blocks, W <= 128");
+
 typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
 
 __device__ __forceinline__ int swz(int r) { return r & 7; }
@@ -178,23 +183,22 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   const int nbh = p.B * p.Hq;
   const int chunk = L / nbh, bh = L % nbh, b = bh / p.Hq, h = bh % p.Hq;
   const Seq s = load_seq(p, b);
-  SeqSched g;
-  main_sched(p, s, g);
+  // The window-bounded schedule at this kernel's fixed tiles (q-tiles of 64
+  // rows, kv-steps of 128 keys, causal, no right band; the plan selects this
+  // kernel only then), in the shift form of swa_sched.h.
+  StreamSched g;
+  g.init(s.len_q, s.len_kv, p.bottom_right, p.window);
   const int n_cap_steps = (s.cap_kv + STEP - 1) / STEP;
   const int j0 = chunk * p.chunk;
   if (j0 >= n_cap_steps) return;
   const int j1 = min(j0 + p.chunk, n_cap_steps);
   const int W = p.window;
-
-  // The schedule of SeqSched at this kernel's fixed tiles (q-tiles of 64
-  // rows, kv-steps of 128 keys, causal): floor / ceil division by a power
-  // of two is an arithmetic shift.
   const int diag = g.diag, nqt = g.n_q_tiles, nkt = g.n_kv_tiles;
-  auto q_lo = [&](int j) { return max((j * STEP - diag) >> 6, 0); };
-  auto q_hi = [&](int j) { return min(-((diag - j * STEP - STEP - W) >> 6), nqt); };
-  auto n_iters = [&](int j) { return j < nkt ? max(q_hi(j) - q_lo(j), 0) : 0; };
-  auto kv_first = [&](int i) { return max((i * kTile + diag - W) >> 7, 0); };
-  auto kv_last = [&](int i) { return min(-((-(i + 1) * kTile - diag) >> 7) - 1, nkt - 1); };
+  auto q_lo = [&](int j) { return g.q_lo(j); };
+  auto q_hi = [&](int j) { return g.q_hi(j); };
+  auto n_iters = [&](int j) { return g.n_iters(j); };
+  auto kv_first = [&](int i) { return g.kv_first(i); };
+  auto kv_last = [&](int i) { return g.kv_last(i); };
 
   // (b, h) bases; row r of a tensor is at base + r * row stride
   const T* qb = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, 0);
@@ -372,16 +376,6 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // ---- band geometry ----------------------------------------------------------
-  // 16-row blocks that keys kv0 + 16 v .. + 15 see (rows t = row + diag - key
-  // in [0, W]): from (kv0 + 16 v - diag) / 16 -- not clipped, so blocks
-  // before row 0 can start a band -- up to the last one, clipped to the
-  // step's q-tiles; empty past the keys.
-  auto band_hi = [&](int kv0, int v, int qhi) {
-    if (kv0 + 16 * v >= s.len_kv) return INT32_MIN / 2;
-    return min((kv0 + 16 * v + 15 + W - diag) >> 4, 4 * qhi - 1);
-  };
-
   // ---- prologue -------------------------------------------------------------
   load_kv(j0, kBn, vBn);
   int loaded_hi = q_lo(j0);  // the ring holds q-tiles [.., loaded_hi)
@@ -466,7 +460,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     // the sequence is pushed out of every window through its lane base.
     const int keyl = kv0 + 16 * w + c;
     const int tkey = keyl < s.len_kv ? diag - keyl : -(1 << 29);
-    const int blo = (kv0 + 16 * w - diag) >> 4, bhi = band_hi(kv0, w, qhi);
+    // 16-row blocks this wave's keys see (StreamSched::band_lo / band_hi)
+    const int blo = g.band_lo(kv0 + 16 * w), bhi = g.band_hi(kv0 + 16 * w, qhi);
     const int npairs = nit == 0 || bhi < 0 ? 0 : min(max(bhi - blo + 2, 0) >> 1, NPAIR);
     struct PairSD {
       f32x4 S0, D0, S1, D1;
@@ -600,15 +595,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     // 1 <= pa <= nb + 1.  Positions of clipped or missing blocks hold zeros,
     // so the positions are compile-time offsets from one per-wave address.
     {
-      const int Lb = (kv0 - diag) >> 4, nb = ((kv0 + 15 + W - diag) >> 4) - Lb + 1;
-      const int c0 = wr + 1 + 4 * qlo - Lb;
+      const int nb = g.dq_nb(j), c0 = g.dq_c0(j, wr);
       const uint32_t bbase = pin(band0 + band_rd * sizeof(T) + 32 * c0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         store_dkdv(ks);
         // the active k, klo <= k <= khi: 0 <= 4 k - 2 ks + c0 - 1 <= nb and
         // k < nit, as a bit mask
-        const int klo = max((2 * ks - c0 + 4) >> 2, 0), khi = min((nb + 1 + 2 * ks - c0) >> 2, nit - 1);
+        const int klo = g.dq_klo(c0, ks), khi = g.dq_khi(c0, nb, ks, nit);
         const unsigned act = khi < klo ? 0u : ((2u << khi) - 1u) & ~((1u << klo) - 1u);
         if (act == 0u) continue;
         const T* kr = sK + 32 * ks * TROW;
@@ -626,10 +620,9 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       }
     }
 
-    // q-tiles whose last visitor in this chunk was this step: kv_last(i) is
-    // nondecreasing in i, and below the last kv-step of the sequence
-    // kv_last(i) <= j iff i <= (128 (j + 1) - diag) / 64 - 1
-    const int nret = j + 1 == j1 || j + 1 >= nkt ? nit : min(((STEP * (j + 1) - diag) >> 6) - qlo, nit);
+    // q-tiles whose last visitor in this chunk was this step (all of them
+    // at the chunk's or the sequence's last step; StreamSched::n_retire)
+    const int nret = j + 1 == j1 || j + 1 >= nkt ? nit : min(g.n_retire(j), nit);
 #pragma unroll
     for (int k = 0; k < NACT; ++k)
       if (k < nret) retire(qlo + k, dQa[k]);

@@ -290,3 +290,23 @@ def test_relay_simulation_with_wrong_first_visitor_times_out(lib):
     s = api.sdpa_bwd_schedule(plan, 512, 512)
     log, expired = simulate_relay(s, kv_first=[0] * s["n_q"], timeout_s=0.3)
     assert expired
+
+
+# ---- the streaming kernel's shift-form schedule, brute force (C++) --------------
+
+
+def test_stream_schedule_shift_forms_brute_force(tmp_path):
+    """StreamSched (the schedule the streaming kernel evaluates) against the
+    mask's definition and SeqSched: bounds, retirement, bands and dQ rounds
+    (tests/host/stream_sched_check.cpp)."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "stream_sched_check")
+    csrc = os.path.join(ROOT, "sliding_window_attention_flash_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+                    "-I" + csrc, os.path.join(ROOT, "tests", "host", "stream_sched_check.cpp"), "-o", exe],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "stream sched: ok" in r.stdout, r.stdout + r.stderr
