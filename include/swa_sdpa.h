@@ -25,8 +25,9 @@
  *   - Errors are returned as sdpa_status; nothing is thrown across the ABI.
  *     sdpa_last_error() returns a thread-local message naming the field or
  *     tensor at fault.  A failed call leaves outputs unspecified.
- *   - Runs are stream-ordered and asynchronous.  A plan is immutable and may
- *     be used by concurrent runs that use distinct workspaces.
+ *   - Runs are stream-ordered and asynchronous.  A plan is immutable (but
+ *     for the test hook sdpa_bwd_plan_set_relay_watchdog) and may be used by
+ *     concurrent runs that use distinct workspaces.
  */
 #ifndef SWA_SDPA_H
 #define SWA_SDPA_H
@@ -45,7 +46,10 @@ typedef enum sdpa_status {
   SDPA_ERR_INVALID_ARG = 1, /* a descriptor field or a pointer is invalid   */
   SDPA_ERR_UNSUPPORTED = 2, /* valid, but not provided (e.g. head_dim 96)  */
   SDPA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned  */
-  SDPA_ERR_HIP = 4          /* a HIP runtime call (e.g. a launch) failed   */
+  SDPA_ERR_HIP = 4,         /* a HIP runtime call (e.g. a launch) failed   */
+  SDPA_ERR_RELAY_TIMEOUT = 5 /* an ordered-relay wait of a run gave up:
+                               that run's dQ is invalid (see
+                               sdpa_bwd_relay_expiries)                     */
 } sdpa_status;
 
 typedef enum sdpa_dtype { SDPA_BF16 = 0, SDPA_F16 = 1 } sdpa_dtype;
@@ -214,13 +218,33 @@ sdpa_status sdpa_bwd_schedule(const sdpa_bwd_plan_t* plan, int32_t len_q, int32_
                               int32_t* kv_first, int32_t* kv_last);
 
 /*
- * sdpa_bwd_relay_expiries -- debug / test aid: copies to *count (host) the
- * number of ordered-relay waits of the last run on `workspace` that gave up
- * after the watchdog's spin limit (0 when every turn arrived in order).
- * Synchronizes `stream`.
+ * sdpa_bwd_relay_expiries -- outcome of the ordered dQ relay of the last run
+ * on `workspace` (deterministic = 1 or 2).  Each relay wait ([PR866] commit
+ * message: a visitor waits for its turn, counted from the q-tile's first
+ * visitor; its tests note that a wrong first visitor would hang or
+ * mis-order) is bounded by a watchdog of 2^20 spins (~55 ms) so that the
+ * device never hangs.  A wait that gives up counts an expiry and adds NaN
+ * instead of its partial, so the q-tile's dQ rows come out NaN, never
+ * plausible but out of order (a late predecessor may still overwrite a
+ * poisoned partial: treat the whole dQ of such a run as invalid).
+ * Copies to *count (host) the number of waits that gave up, synchronizing
+ * `stream`, and returns SDPA_ERR_RELAY_TIMEOUT when it is > 0, SDPA_OK
+ * when every turn arrived in order.  sdpa_bwd_run cannot report this
+ * itself: it returns before the kernels run.
  */
 sdpa_status sdpa_bwd_relay_expiries(const sdpa_bwd_plan_t* plan, const void* workspace,
                                     hipStream_t stream, int32_t* count);
+
+/*
+ * sdpa_bwd_plan_set_relay_watchdog -- test hook for the watchdog path.
+ * spin_limit > 0 sets the spins before a relay wait gives up (0 restores
+ * the default 2^20).  unreachable = 1 makes every wait target a turn no
+ * visitor ever releases, so each non-first turn gives up after spin_limit
+ * spins and every kernel still runs to its end: a host-forced timeout for
+ * tests.  Host only; changes the plan, so call it before runs that use the
+ * plan, not concurrently with them.
+ */
+sdpa_status sdpa_bwd_plan_set_relay_watchdog(sdpa_bwd_plan_t* plan, int32_t spin_limit, int32_t unreachable);
 
 const char* sdpa_status_string(sdpa_status status);
 const char* sdpa_last_error(void);

@@ -12,7 +12,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libswa_sdpa.so")
 
-SDPA_OK, SDPA_ERR_INVALID_ARG, SDPA_ERR_UNSUPPORTED, SDPA_ERR_WORKSPACE, SDPA_ERR_HIP = range(5)
+(SDPA_OK, SDPA_ERR_INVALID_ARG, SDPA_ERR_UNSUPPORTED, SDPA_ERR_WORKSPACE, SDPA_ERR_HIP,
+ SDPA_ERR_RELAY_TIMEOUT) = range(6)
 SDPA_BF16, SDPA_F16 = 0, 1
 SDPA_LAYOUT_BHSD, SDPA_LAYOUT_THD = 0, 1
 
@@ -49,7 +50,7 @@ class BwdTensors(ctypes.Structure):
 EXPORTS = [
     "sdpa_bwd_plan", "sdpa_bwd_run", "sdpa_bwd_run_events", "sdpa_bwd_plan_destroy",
     "sdpa_fwd_plan", "sdpa_fwd_run", "sdpa_fwd_plan_destroy", "sdpa_bwd_schedule",
-    "sdpa_bwd_relay_expiries", "sdpa_status_string", "sdpa_last_error",
+    "sdpa_bwd_relay_expiries", "sdpa_bwd_plan_set_relay_watchdog", "sdpa_status_string", "sdpa_last_error",
 ]
 
 _lib = None
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_bwd_schedule.argtypes = [_vp, _i32, _i32, ip, ip, ip, ip, _i32, ip, ip, _i32, ip, ip]
     lib.sdpa_bwd_relay_expiries.argtypes = [_vp, _vp, _vp, ip]
     lib.sdpa_bwd_relay_expiries.restype = ctypes.c_int
+    lib.sdpa_bwd_plan_set_relay_watchdog.argtypes = [_vp, _i32, _i32]
+    lib.sdpa_bwd_plan_set_relay_watchdog.restype = ctypes.c_int
     lib.sdpa_status_string.argtypes = [ctypes.c_int]
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_last_error.argtypes = []

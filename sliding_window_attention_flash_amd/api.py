@@ -77,12 +77,23 @@ def sdpa_bwd_run_events(plan: BwdPlan, tensors: BwdTensors, workspace, stream, s
                                           ctypes.c_void_p(stop_event)), "sdpa_bwd_run_events")
 
 
-def sdpa_bwd_relay_expiries(plan: BwdPlan, workspace: torch.Tensor, stream=None) -> int:
-    """Relay waits of the last run that hit the watchdog (synchronizes)."""
+def sdpa_bwd_relay_expiries(plan: BwdPlan, workspace: torch.Tensor, stream=None,
+                            raise_on_timeout: bool = False) -> int:
+    """Relay waits of the last run that hit the watchdog (synchronizes).  The
+    library returns SDPA_ERR_RELAY_TIMEOUT when the count is > 0; that raises
+    here only with ``raise_on_timeout``, otherwise the count says it."""
     n = ctypes.c_int32()
-    check(_lib.load().sdpa_bwd_relay_expiries(plan.handle, _p(workspace), _stream(stream),
-                                              ctypes.byref(n)), "sdpa_bwd_relay_expiries")
+    st = _lib.load().sdpa_bwd_relay_expiries(plan.handle, _p(workspace), _stream(stream), ctypes.byref(n))
+    if st != _lib.SDPA_ERR_RELAY_TIMEOUT or raise_on_timeout:
+        check(st, "sdpa_bwd_relay_expiries")
     return int(n.value)
+
+
+def sdpa_bwd_plan_set_relay_watchdog(plan: BwdPlan, spin_limit: int, unreachable: bool) -> None:
+    """Test hook: spins before a relay wait gives up, and whether every wait
+    targets a turn no visitor releases (a host-forced timeout)."""
+    check(_lib.load().sdpa_bwd_plan_set_relay_watchdog(plan.handle, int(spin_limit), int(bool(unreachable))),
+          "sdpa_bwd_plan_set_relay_watchdog")
 
 
 def sdpa_fwd_plan(desc: AttnDesc) -> FwdPlan:

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <new>
 
+#include "api_internal.h"
 #include "kernels.h"
 #include "swa_sdpa.h"
 
@@ -19,7 +20,8 @@ struct sdpa_bwd_plan {
   swa::Problem prob;
   int64_t stat_rows;  // rows of the delta / dQ-accumulator workspace
   size_t off_delta, off_acc, off_stash, off_sem, off_ctl, off_sink, ws_bytes;
-  int spin_limit;
+  int spin_limit;  // relay watchdog: spins before a wait gives up
+  int relay_bias;  // 0, or (test hook) a wait target no visitor releases
 };
 
 struct sdpa_fwd_plan {
@@ -235,6 +237,7 @@ const char* sdpa_status_string(sdpa_status s) {
     case SDPA_ERR_UNSUPPORTED: return "SDPA_ERR_UNSUPPORTED";
     case SDPA_ERR_WORKSPACE: return "SDPA_ERR_WORKSPACE";
     case SDPA_ERR_HIP: return "SDPA_ERR_HIP";
+    case SDPA_ERR_RELAY_TIMEOUT: return "SDPA_ERR_RELAY_TIMEOUT";
   }
   return "SDPA_ERR_UNKNOWN";
 }
@@ -279,6 +282,7 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   off = align256(off + sizeof(float) * (size_t)p.Hq * p.B * p.n_q_tiles);
   pl->ws_bytes = off;
   pl->spin_limit = 1 << 20;  // ~55 ms of s_sleep per wait; legitimate waits take microseconds
+  pl->relay_bias = 0;
   *plan = pl;
   *workspace_bytes = off;
   g_err[0] = 0;
@@ -287,9 +291,19 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
 
 void sdpa_bwd_plan_destroy(sdpa_bwd_plan_t* plan) { delete plan; }
 
-sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensors* t, void* ws,
-                                size_t ws_bytes, hipStream_t stream, hipEvent_t main_start,
-                                hipEvent_t main_stop) {
+}  // extern "C"
+
+namespace swa {
+
+size_t bwd_plan_workspace_bytes(const sdpa_bwd_plan_t* pl) { return pl->ws_bytes; }
+
+// The backward's launch sequence behind sdpa_bwd_run_events and the
+// no-allocation entry point: validates the plan, the workspace size and
+// alignment and the tensors, then enqueues the kernels.  check_ws_ptr asks
+// the runtime whether the workspace is device memory of the current device
+// (the library's own scratch array is known to be).
+sdpa_status bwd_run(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensors* t, void* ws, size_t ws_bytes,
+                    hipStream_t stream, hipEvent_t main_start, hipEvent_t main_stop, bool check_ws_ptr) {
   if (!pl) return fail(SDPA_ERR_INVALID_ARG, "plan is NULL");
   if (!t) return fail(SDPA_ERR_INVALID_ARG, "tensors is NULL");
   const sdpa_attn_desc& d = pl->desc;
@@ -298,7 +312,8 @@ sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensor
   if (!ws && pl->ws_bytes) return fail(SDPA_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(SDPA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   sdpa_status st;
-  if ((st = check_dev_ptr(ws, "workspace", false, 256))) return st == SDPA_ERR_INVALID_ARG ? SDPA_ERR_WORKSPACE : st;
+  if (check_ws_ptr && (st = check_dev_ptr(ws, "workspace", false, 256)))
+    return st == SDPA_ERR_INVALID_ARG ? SDPA_ERR_WORKSPACE : st;
   if ((st = check_dev_ptr(t->q, "q", false, 16))) return st;
   if ((st = check_dev_ptr(t->k, "k", false, 16))) return st;
   if ((st = check_dev_ptr(t->v, "v", false, 16))) return st;
@@ -350,6 +365,7 @@ sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensor
   a.sink_part = reinterpret_cast<float*>(base + pl->off_sink);
   a.deterministic = d.deterministic;
   a.spin_limit = pl->spin_limit;
+  a.relay_bias = pl->relay_bias;
 
   hipError_t e;
   if ((e = swa::launch_bwd_dot(a, stream)) != hipSuccess)
@@ -368,9 +384,21 @@ sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensor
   return SDPA_OK;
 }
 
+sdpa_status set_error(sdpa_status st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace swa
+
+extern "C" {
+
+sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensors* t, void* ws,
+                                size_t ws_bytes, hipStream_t stream, hipEvent_t main_start,
+                                hipEvent_t main_stop) {
+  return swa::bwd_run(pl, t, ws, ws_bytes, stream, main_start, main_stop, true);
+}
+
 sdpa_status sdpa_bwd_run(const sdpa_bwd_plan_t* plan, const sdpa_bwd_tensors* tensors, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  return sdpa_bwd_run_events(plan, tensors, workspace, workspace_bytes, stream, nullptr, nullptr);
+  return swa::bwd_run(plan, tensors, workspace, workspace_bytes, stream, nullptr, nullptr, true);
 }
 
 sdpa_status sdpa_bwd_schedule(const sdpa_bwd_plan_t* pl, int32_t len_q, int32_t len_kv, int32_t* tile_q,
@@ -416,6 +444,21 @@ sdpa_status sdpa_bwd_relay_expiries(const sdpa_bwd_plan_t* pl, const void* ws, h
                                 hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "reading the relay watchdog counter: %s", hipGetErrorString(e));
+  if (*count > 0)
+    return fail(SDPA_ERR_RELAY_TIMEOUT,
+                "%d ordered-relay wait(s) of the last run gave up after %d spins: that run's dQ is invalid "
+                "(the turns that gave up added NaN)", *count, pl->spin_limit);
+  g_err[0] = 0;
+  return SDPA_OK;
+}
+
+sdpa_status sdpa_bwd_plan_set_relay_watchdog(sdpa_bwd_plan_t* pl, int32_t spin_limit, int32_t unreachable) {
+  if (!pl) return fail(SDPA_ERR_INVALID_ARG, "plan is NULL");
+  if (spin_limit < 0) return fail(SDPA_ERR_INVALID_ARG, "spin_limit %d < 0", spin_limit);
+  if (unreachable != 0 && unreachable != 1) return fail(SDPA_ERR_INVALID_ARG, "unreachable %d is not 0/1", unreachable);
+  pl->spin_limit = spin_limit > 0 ? spin_limit : (1 << 20);
+  // counters only ever hold turns below a q-tile's visitor count (<= 2^31 / 64)
+  pl->relay_bias = unreachable ? (1 << 30) : 0;
   g_err[0] = 0;
   return SDPA_OK;
 }

@@ -27,15 +27,21 @@ namespace swa {
 // visitor's fetch-add returns the sum of all earlier turns, to which it adds
 // its own and writes the 16-bit result.  A single visitor writes directly.
 
-__device__ __forceinline__ void relay_wait(int* semp, int turn, int spin_limit, int* expiries) {
+// Spins until the q-tile's counter reaches `turn` (plus the test bias).  A
+// wait that exceeds the spin limit gives up so that the device never hangs:
+// it counts an expiry (reported by sdpa_bwd_relay_expiries) and returns
+// true, and the caller then adds NaN instead of its partial, so the q-tile's
+// dQ comes out poisoned rather than plausible but out of order.
+__device__ __forceinline__ bool relay_wait(int* semp, int turn, int spin_limit, int* expiries) {
   int spins = 0;
   while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != turn) {
-    if (++spins > spin_limit) {  // watchdog: never hang the device
+    if (++spins > spin_limit) {
       atomicAdd(expiries, 1);
-      break;
+      return true;
     }
     __builtin_amdgcn_s_sleep(1);
   }
+  return false;
 }
 
 template <typename T>
@@ -449,15 +455,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
     float* accr = a.dq_acc + (s.stat0 + h * s.stat_hs + qr0) * D + c;
     const int turn = g.relay_turn(i, jt), nv = g.n_visitors(i);
     int* semp = a.sem + ((int64_t)b * p.Hq + h) * p.n_q_tiles + i;
-    if (tid == 0 && turn > 0) relay_wait(semp, turn, a.spin_limit, a.ctl + 1);
+    if (tid == 0) sTicket = turn > 0 && relay_wait(semp, turn + a.relay_bias, a.spin_limit, a.ctl + 1);
     __syncthreads();
+    const bool expired = sTicket != 0;  // then this turn adds NaN (poison)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (qr0 + r >= s.cap_q) continue;
       T* outr = dqp + elem_off(p, p.sdq, b, s.row0_q, h, qr0 + r) + c;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        relay_add<T>(accr + r * D + 16 * db, dQ[db][r], turn, nv, p.scale, outr + 16 * db);
+        relay_add<T>(accr + r * D + 16 * db, expired ? __builtin_nanf("") : dQ[db][r], turn, nv, p.scale,
+                     outr + 16 * db);
     }
     relay_release(semp, turn, nv, tid);
     __syncthreads();  // next tile staged; dS^T reads done

@@ -636,16 +636,22 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const int turn = chunk - first, nv = kv_last(i) / p.chunk - first + 1;
       int* semp = semb + i;
       if (tid == 0) {
-        int spins = 0;
-        while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != turn) {
-          if (++spins > a.spin_limit) {  // watchdog: never hang the device
+        // a wait past the spin limit gives up so that the device never
+        // hangs: it counts an expiry, and this turn then adds NaN, so the
+        // q-tile's dQ comes out poisoned rather than out of order
+        int spins = 0, expired = 0;
+        while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != turn + a.relay_bias) {
+          if (++spins > a.spin_limit) {
             atomicAdd(&a.ctl[1], 1);
+            expired = 1;
             break;
           }
           __builtin_amdgcn_s_sleep(1);
         }
+        sTicket = expired;
       }
       __syncthreads();
+      const bool expired = sTicket != 0;
       const int qi = q_row(i);
       if (qi < s.cap_q) {
 #pragma unroll
@@ -653,7 +659,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
           // the turn holds the tile alone: a coherent read of the running
           // sum, this chunk's add, and a coherent write for the next turn
           const uint32_t off = (uint32_t)acc_off(i, e) * sizeof(float);
-          const f32x4 mine = *reinterpret_cast<const f32x4*>(stashb + acc_off(i, e));
+          f32x4 mine = *reinterpret_cast<const f32x4*>(stashb + acc_off(i, e));
+          if (expired) mine = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
           const f32x4 sum = ld_coherent(accr, off) + mine;
           if (turn < nv - 1)
             st_coherent(accr, off, sum);

@@ -32,6 +32,8 @@ struct BwdArgs {
   float* sink_part;  // [Hq, B, n_q_tiles] per-q-tile dSink partials
   int deterministic;
   int spin_limit;    // relay watchdog: spins before a wait gives up
+  int relay_bias;    // added to every relay wait's target turn: 0, or (test
+                     // hook) a turn no visitor ever releases
 };
 
 struct FwdArgs {

@@ -235,12 +235,15 @@ def test_schedule_covers_the_mask_exactly(lib, lq, lk, w, br, causal, wr, mha):
 
 def simulate_relay(s, kv_first=None, timeout_s=2.0):
     """One thread per kv-tile visits its q-tiles in descending order; each
-    visit waits for its turn (j - kv_first(i)), logs itself, and passes the
-    turn on.  Returns (log per q-tile, expired waits)."""
+    visit waits for its turn (j - kv_first(i)), logs itself, adds its
+    partial (here the value 2^j) into the q-tile's running sum, and passes
+    the turn on.  A wait past the watchdog gives up and adds NaN instead, as
+    the kernels do.  Returns (log per q-tile, expired waits, sums)."""
     kv_first = kv_first or s["kv_first"]
     nq, nk = s["n_q"], s["n_kv"]
     sem = [0] * nq
     log = [[] for _ in range(nq)]
+    sums = [0.0] * nq
     expired = []
     lock = threading.Lock()
 
@@ -248,6 +251,7 @@ def simulate_relay(s, kv_first=None, timeout_s=2.0):
         for i in range(s["q_hi"][j] - 1, s["q_lo"][j] - 1, -1):
             turn = j - kv_first[i]
             t0 = time.time()
+            gave_up = False
             while True:
                 with lock:
                     if sem[i] == turn:
@@ -255,10 +259,12 @@ def simulate_relay(s, kv_first=None, timeout_s=2.0):
                 if time.time() - t0 > timeout_s:
                     with lock:
                         expired.append((i, j))
+                    gave_up = True
                     break
                 time.sleep(0.0005)
             with lock:
                 log[i].append(j)
+                sums[i] += float("nan") if gave_up else float(2 ** j)
                 sem[i] = turn + 1
 
     ts = [threading.Thread(target=visitor, args=(j,)) for j in range(nk)]
@@ -266,7 +272,7 @@ def simulate_relay(s, kv_first=None, timeout_s=2.0):
         t.start()
     for t in ts:
         t.join()
-    return log, expired
+    return log, expired, sums
 
 
 @pytest.mark.parametrize("mha", [False, True])
@@ -276,10 +282,11 @@ def simulate_relay(s, kv_first=None, timeout_s=2.0):
 def test_relay_simulation_orders_every_q_tile(lib, lq, lk, w, br, wr, mha):
     plan = api.sdpa_bwd_plan(_desc(window_left=w, window_right=wr, bottom_right=br, Hkv=4 if mha else 2))
     s = api.sdpa_bwd_schedule(plan, lq, lk)
-    log, expired = simulate_relay(s)
+    log, expired, sums = simulate_relay(s)
     assert not expired
     for i in range(s["n_q"]):
         assert log[i] == list(range(s["kv_first"][i], s["kv_last"][i] + 1))
+        assert sums[i] == sum(2.0 ** j for j in log[i])
 
 
 def test_relay_simulation_with_wrong_first_visitor_times_out(lib):
@@ -288,8 +295,27 @@ def test_relay_simulation_with_wrong_first_visitor_times_out(lib):
     # visitor takes: the watchdog, not a hang, ends the run.
     plan = api.sdpa_bwd_plan(_desc(window_left=64))
     s = api.sdpa_bwd_schedule(plan, 512, 512)
-    log, expired = simulate_relay(s, kv_first=[0] * s["n_q"], timeout_s=0.3)
+    log, expired, sums = simulate_relay(s, kv_first=[0] * s["n_q"], timeout_s=0.3)
     assert expired
+    # a q-tile whose wait gave up ends poisoned (NaN), never with a plausible
+    # sum; the others keep the ordered sum
+    bad = {i for i, _ in expired}
+    for i in range(s["n_q"]):
+        if i in bad:
+            assert sums[i] != sums[i]
+        else:
+            assert sums[i] == sum(2.0 ** j for j in log[i])
+
+
+def test_relay_watchdog_hook_validates_and_status_names(lib):
+    plan = api.sdpa_bwd_plan(_desc(deterministic=2))
+    assert lib.sdpa_bwd_plan_set_relay_watchdog(plan.handle, -1, 0) == _lib.SDPA_ERR_INVALID_ARG
+    assert b"spin_limit" in lib.sdpa_last_error()
+    assert lib.sdpa_bwd_plan_set_relay_watchdog(plan.handle, 16, 2) == _lib.SDPA_ERR_INVALID_ARG
+    assert lib.sdpa_bwd_plan_set_relay_watchdog(None, 16, 1) == _lib.SDPA_ERR_INVALID_ARG
+    assert lib.sdpa_bwd_plan_set_relay_watchdog(plan.handle, 16, 1) == _lib.SDPA_OK
+    assert lib.sdpa_bwd_plan_set_relay_watchdog(plan.handle, 0, 0) == _lib.SDPA_OK
+    assert lib.sdpa_status_string(_lib.SDPA_ERR_RELAY_TIMEOUT) == b"SDPA_ERR_RELAY_TIMEOUT"
 
 
 # ---- the streaming kernel's shift-form schedule, brute force (C++) --------------
@@ -310,3 +336,4 @@ def test_stream_schedule_shift_forms_brute_force(tmp_path):
                    check=True, capture_output=True, text=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "stream sched: ok" in r.stdout, r.stdout + r.stderr
+
