@@ -1,6 +1,6 @@
 """Benchmark of the sliding-window attention backward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c3|c3_atomic|c1|c2_4k|c2_8k|c2_4k_det|c2_8k_det|c4|c4_f16|c5]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--repeats R]
     python bench.py --copy-calibration ...      (appends a copy of known size)
     python bench.py --summarize-stats DIR --out FILE --command CMD
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --out FILE --command CMD
@@ -9,24 +9,43 @@
 A step is one full backward, sdpa_bwd_run: the dot preprocess, the main
 window-bounded kernel with its dQ accumulation (ordered relay, fp32 atomics
 at the streaming kernel's chunk boundaries, or the separate q-major dQ
-pass), the dQ conversion where an accumulator is used, and dSink (with
-sinks), on inputs already resident in HBM.  The default workload is the
-long-sequence shape of the pages' measurements: batch 2, 16 heads,
-head_dim 64, S = 32768, causal top-left with a left window of 128, bf16,
-deterministic relay.  Prints one JSON line; ``extra`` carries the other
-workloads and the forward's time per call for each.
+pass), and dSink (with sinks), on inputs already resident in HBM.  The
+default workload is the long-sequence shape of the pages' measurements:
+batch 2, 16 heads, head_dim 64, S = 32768, causal top-left with a left
+window of 128, bf16, deterministic relay.  Prints one JSON line; ``extra``
+carries every other workload.
+
+Timing follows the pages' protocol (cudnn-frontend PR #2352, Measurement:
+three repeats with fresh tensors, median per repeat, warm caches): each
+repeat draws fresh inputs, runs the forward, then W warm-up steps and K
+timed steps with a HIP event recorded on the launch stream between
+consecutive steps; a repeat's figure is the median of its K per-step times,
+and the reported step time is the median over the repeats.  Before the first
+repeat of each workload the backward also runs for at least 0.5 s of wall
+time, whatever W is, so that the first timed step does not meet an idle,
+clocked-down GPU.  The K steps of each repeat are also timed as a whole with
+host clocks (``host_mean_ms``), which shows what the per-step events cost.
 
 FLOPs count attended (query, key) pairs only: 10 * head_dim per pair per
-query head for the backward, 4 * head_dim for the forward.  The roofline
-entry is for the dominant kernel (the streaming main kernel at the default
-workload), timed with HIP events recorded on its launch stream around every
-launch of a second run of as many steps (the timed steps themselves run
-uninstrumented, since the event packets lengthen a step).  Its ``traffic`` is the HBM bytes per launch that rocprofv3's
-FETCH_SIZE and WRITE_SIZE counters read for it, each divided by what the
-same counter reads per byte for an elementwise copy of known size; the
-figures are kept in a text summary under profiles/ together with a hash of
-the kernel's sources, and ``traffic`` is null when the sources no longer
-match.
+query head for the backward, 4 * head_dim for the forward.  Each workload
+reports the fraction of bf16 MFMA peak and the fraction of its attainable
+roofline, min(MFMA peak, arithmetic intensity x 8 TB/s), with the
+compulsory bytes of Q, O, dO, dQ (per query-head row), K, V, dK, dV (per
+kv-head row) and LSE.  The roofline entry of the JSON line is for the
+dominant kernel (the streaming main kernel at the default workload), timed
+with HIP events around every launch of a separate run; its ``traffic`` is
+the HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE
+counters read for it, each divided by what the same counter reads per byte
+for an elementwise copy of known size; the figures are kept in a text
+summary under profiles/ together with a hash of the kernel's sources, and
+``traffic`` is null when the sources no longer match.
+
+The CPU leg (skipped with --no-cpu-baseline) runs the fp64 oracle on the
+same inputs as each workload's last repeat: its wall time on the host's
+cores, and the per-gradient parity errors of the GPU outputs (relative
+Frobenius error and max-abs error over max|ref|), on the whole workload or,
+where that is too slow, on whole batch entries or sequences (named in
+``sample``).
 """
 from __future__ import annotations
 
@@ -66,6 +85,7 @@ def _hip():
     lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
     lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -83,6 +103,7 @@ def workloads():
         "c4": CONFIGS["c4"],
         "c4_f16": CONFIGS["c4_f16"],
         "c5": CONFIGS["c5"],
+        "nonsquare": CONFIGS["nonsquare"],
     }
 
 
@@ -96,11 +117,28 @@ def main_kernel_bytes(w) -> int:
     return rows_q * (3 * w.head_dim * 2 + 8) + rows_kv * (4 * w.head_dim * 2)
 
 
-def time_backward(w, steps, warmup, seed=0, forward=False):
-    """Per-step wall time of the backward (ms), the average of the main
-    kernel's HIP-event times (ms), the relay expiries, and with forward=True
-    also the forward's wall time per call (ms)."""
-    import torch
+def compulsory_bytes(w) -> int:
+    """Compulsory HBM bytes of one backward: Q, O, dO read and dQ written per
+    query-head row, K, V read and dK, dV written per kv-head row (16-bit),
+    plus the row's LSE (fp32)."""
+    rows_q = sum(w.valid_len_q()) * w.heads_q
+    rows_kv = sum(w.valid_len_kv()) * w.heads_kv
+    return rows_q * (4 * w.head_dim * 2 + 4) + rows_kv * (4 * w.head_dim * 2)
+
+
+def roofline_fractions(w, ms):
+    """(fraction of bf16 MFMA peak, fraction of the attainable roofline,
+    bound) of a step of ms milliseconds."""
+    from sliding_window_attention_flash_amd.synth import flops
+    fl = flops(w)
+    tf = fl / (ms * 1e-3) / 1e12
+    attainable = min(BF16_MFMA_PEAK_TFLOPS, fl / compulsory_bytes(w) * HBM_PEAK_GBS / 1e3)
+    bound = "mfma" if attainable >= BF16_MFMA_PEAK_TFLOPS else "hbm"
+    return tf / BF16_MFMA_PEAK_TFLOPS, tf / attainable, bound
+
+
+def _prepare(w, seed):
+    import torch  # noqa: F401
     from sliding_window_attention_flash_amd import api
     from sliding_window_attention_flash_amd.synth import make_inputs
 
@@ -115,46 +153,111 @@ def time_backward(w, steps, warmup, seed=0, forward=False):
     o, lse = fw.run()
     bw = api.Backward(inp["q"], inp["k"], inp["v"], o, inp["dO"], lse, deterministic=w.deterministic,
                       sink=inp["sink"], **mk)
+    return inp, fw, o, lse, bw
+
+
+def _median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def time_workload(w, steps, warmup, repeats=3, seed=0, forward=True, main_kernel=False, min_warm_s=0.5):
+    """Times the backward of workload w by the protocol of the module
+    docstring.  Returns a dict: ms (median over repeats of the per-repeat
+    median step), per-repeat medians, host_mean_ms, the main kernel's mean
+    HIP-event time (main_kernel=True), relay expiries, the forward's time
+    per call, and the last repeat's inputs and outputs (for the CPU leg)."""
+    import torch
+
     hip = _hip()
-    ev = []
-    for _ in range(2 * steps):
-        e = ctypes.c_void_p()
-        assert hip.hipEventCreate(ctypes.byref(e)) == 0
-        ev.append(e)
-    for _ in range(warmup):
-        bw.run()
-    # the timed steps, uninstrumented
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        bw.run()
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    # the same number of steps again, with HIP events recorded on the launch
-    # stream around the main kernel of each (the events add stream packets,
-    # so these steps are not the timed ones)
-    for s in range(steps):
-        bw.run_events(ev[2 * s].value, ev[2 * s + 1].value)
-    torch.cuda.synchronize()
-    main_ms = []
-    for s in range(steps):
+
+    def events(n):
+        ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            ev.append(e)
+        return ev
+
+    def elapsed(a, b):
         ms = ctypes.c_float()
-        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[2 * s], ev[2 * s + 1]) == 0
-        main_ms.append(ms.value)
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    res = {"repeat_ms": [], "host_mean_ms": [], "expiries": 0}
+    ev = events(steps + 1)
+    last = None
+    for r in range(repeats):
+        inp, fw, o, lse, bw = _prepare(w, seed + r)
+        for _ in range(warmup):
+            bw.run()
+        if r == 0:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < min_warm_s:
+                for _ in range(8):
+                    bw.run()
+                torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        hip.hipEventRecord(ev[0], ctypes.c_void_p(stream.cuda_stream))
+        for k in range(steps):
+            bw.run()
+            hip.hipEventRecord(ev[k + 1], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        res["repeat_ms"].append(_median([elapsed(ev[k], ev[k + 1]) for k in range(steps)]))
+        # the same number of steps timed as a whole, without events
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            bw.run()
+        torch.cuda.synchronize()
+        res["host_mean_ms"].append((time.perf_counter() - t0) / steps * 1e3)
+        if w.deterministic:
+            res["expiries"] += bw.relay_expiries()
+        last = (inp, o, lse, bw)
     for e in ev:
         hip.hipEventDestroy(e)
-    expiries = bw.relay_expiries() if w.deterministic else 0
-    if not forward:
-        return wall * 1e3, sum(main_ms) / len(main_ms), expiries
-    for _ in range(max(3, warmup // 5)):
-        fw.run()
+    res["ms"] = _median(res["repeat_ms"])
+    inp, o, lse, bw = last
+    # the last repeat's backward outputs on its inputs, for the CPU leg
+    dq, dk, dv, dsink = bw.run()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fw.run()
-    torch.cuda.synchronize()
-    fwd_ms = (time.perf_counter() - t0) / steps * 1e3
-    return wall * 1e3, sum(main_ms) / len(main_ms), expiries, fwd_ms
+    res["last"] = dict(inp=inp, o=o, lse=lse, dq=dq, dk=dk, dv=dv, dsink=dsink)
+    if main_kernel:
+        # events right around the main kernel of each step (extra stream
+        # packets, so these steps are not the timed ones); they are the
+        # main kernel's last dispatches of the run (profile summaries rely
+        # on that)
+        mev = events(2 * steps)
+        for k in range(steps):
+            bw.run_events(mev[2 * k].value, mev[2 * k + 1].value)
+        torch.cuda.synchronize()
+        res["main_ms"] = sum(elapsed(mev[2 * k], mev[2 * k + 1]) for k in range(steps)) / steps
+        for e in mev:
+            hip.hipEventDestroy(e)
+    if forward:
+        fwd = _forward_of(w, inp)
+        for _ in range(max(3, warmup)):
+            fwd.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fwd.run()
+        torch.cuda.synchronize()
+        res["forward_ms"] = (time.perf_counter() - t0) / steps * 1e3
+    return res
+
+
+def _forward_of(w, inp):
+    from sliding_window_attention_flash_amd import api
+    mk = dict(causal=w.causal, bottom_right=w.bottom_right, window_left=w.window_left,
+              window_right=w.window_right, scale=w.softmax_scale, cu_seqlens_q=inp["cu_seqlens_q"],
+              cu_seqlens_kv=inp["cu_seqlens_kv"], seq_lens_q=inp["seq_lens_q"], seq_lens_kv=inp["seq_lens_kv"])
+    if w.layout == "thd":
+        mk.update(max_seqlen_q=w.seq_q, max_seqlen_kv=w.seq_kv)
+    return api.Forward(inp["q"], inp["k"], inp["v"], sink=inp["sink"], **mk)
 
 
 def kernel_source_hash() -> str:
@@ -339,39 +442,85 @@ def summarize_counters(dirs, out, commands, workload):
     print("\n".join(lines))
 
 
-def cpu_baseline(w):
-    """The fp64 oracle's backward timed on the whole workload when it is a
-    dense multi-head one (the oracle runs one (sequence, kv head) unit per
-    host thread), scaled to attended TFLOP/s; other workloads are sampled to
-    one sequence."""
-    import oracle
-    from sliding_window_attention_flash_amd.synth import make_inputs
+# oracle work (attended pairs x head_dim x query heads) above which the CPU
+# leg checks whole batch entries instead of the whole dense workload: about
+# 8 s of oracle time on 16 host threads
+ORACLE_FULL_WORK = 1.2e10
 
-    ws = w if w.layout == "bhsd" and w.batch * w.heads_kv <= 64 else w.with_(batch=1, name=w.name + "_b0")
-    inp = make_inputs(ws, device="cpu", seed=0)
-    p = oracle.Problem.dense(ws.batch, ws.heads_q, ws.heads_kv, ws.seq_q, ws.seq_kv, ws.head_dim,
-                             causal=ws.causal, bottom_right=ws.bottom_right,
-                             window_left=ws.window_left, scale=ws.softmax_scale)
+
+def cpu_leg(w, last):
+    """The fp64 oracle on the inputs of the workload's last timed repeat:
+    its wall time and the per-gradient parity errors of the GPU outputs.
+    Dense workloads too large for one oracle run are checked on their first
+    batch entries (as many as fit ORACLE_FULL_WORK, at least one)."""
+    import oracle
+    import torch
+    from sliding_window_attention_flash_amd.synth import attended_pairs_per_head
+
+    work = attended_pairs_per_head(w) * w.heads_q * w.head_dim
+    nb = w.batch
+    if w.layout == "bhsd" and work > ORACLE_FULL_WORK:
+        nb = max(1, int(ORACLE_FULL_WORK / (work / w.batch)))
+    ws = w if nb == w.batch else w.with_(name=f"{w.name}_b0-{nb - 1}", batch=nb,
+                                         pad_len_q=w.pad_len_q[:nb] if w.pad_len_q else None,
+                                         pad_len_kv=w.pad_len_kv[:nb] if w.pad_len_kv else None)
+    inp = last["inp"]
+    cpu = {}
+    for k in ("q", "k", "v", "dO"):
+        cpu[k] = inp[k][:nb].cpu() if ws is not w else inp[k].cpu()
+    sink = inp["sink"].cpu() if inp["sink"] is not None else None
+    p = oracle.Problem.for_workload(ws)
     t0 = time.perf_counter()
-    oracle.backward(p, inp["q"], inp["k"], inp["v"], inp["dO"], None)
+    ref = oracle.backward(p, cpu["q"], cpu["k"], cpu["v"], cpu["dO"], sink)
     dt = time.perf_counter() - t0
-    pairs = oracle.attended_pairs(p) * ws.heads_q
-    flops = 10.0 * ws.head_dim * pairs
+    errs = {}
+    pairs = [("dQ", "dq", "dq"), ("dK", "dk", "dk"), ("dV", "dv", "dv")]
+    if w.sink and ws is w:
+        pairs.append(("dSink", "dsink", "dsink"))
+    for name, gk, rk in pairs:
+        g = last[gk]
+        g = (g[:nb] if ws is not w and name != "dSink" else g).double().cpu().reshape(-1)
+        r = ref[rk].reshape(-1)
+        rn, rmax = float(r.norm()), float(r.abs().max())
+        d = g - r
+        errs[name] = {"rel_fro": float(d.norm()) / rn if rn else float(g.abs().max()),
+                      "max_abs_over_max_ref": float(d.abs().max()) / rmax if rmax else float(g.abs().max()),
+                      "nan": bool(torch.isnan(g).any())}
     units = ws.batch * ws.heads_kv
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(oracle.num_threads(), units),
-            "kind": "oracle",
-            "sample": f"fp64 oracle backward (forward recompute included) on {ws.batch} sequence(s) x "
-                      f"{ws.heads_q} head(s) of {w.name}: {pairs} attended pairs in {dt:.2f} s"}
+    sample_pairs = attended_pairs_per_head(ws) * ws.heads_q
+    return {"oracle_ms": dt * 1e3, "cores": min(oracle.num_threads(), units),
+            "sample": ("whole workload" if ws is w else f"batch entries 0..{nb - 1} of {w.batch}")
+                      + f": {sample_pairs} attended pairs, fp64 forward + backward",
+            "oracle_tflops": 10.0 * ws.head_dim * sample_pairs / dt / 1e12,
+            "parity": errs}
+
+
+def workload_entry(w, t):
+    from sliding_window_attention_flash_amd.synth import flops
+    fl = flops(w)
+    f_peak, f_roof, bound = roofline_fractions(w, t["ms"])
+    e = {"workload": w.name, "ms": t["ms"], "tflops": fl / (t["ms"] * 1e-3) / 1e12,
+         "repeat_ms": t["repeat_ms"], "host_mean_ms": _median(t["host_mean_ms"]),
+         "frac_bf16_mfma_peak": f_peak, "frac_attainable_roofline": f_roof, "roofline_bound": bound,
+         "compulsory_bytes": compulsory_bytes(w), "attended_flops": fl, "relay_expiries": t["expiries"]}
+    if "forward_ms" in t:
+        e["forward_ms"] = t["forward_ms"]
+        e["forward_tflops"] = 0.4 * fl / (t["forward_ms"] * 1e-3) / 1e12
+    if "main_ms" in t:
+        e["main_ms"] = t["main_ms"]
+    return e
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--repeats", type=int, default=3)
     ap.add_argument("--workload", default="c3", choices=sorted(workloads()))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 4k / 8k / atomic side timings")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU leg (oracle time and parity errors)")
+    ap.add_argument("--no-extra", action="store_true", help="time the headline workload only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"after timing, copy {COPY_BYTES} bytes three times (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR")
@@ -397,41 +546,27 @@ def main():
         sys.exit(2)
 
     import torch
-    from sliding_window_attention_flash_amd.synth import flops
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     wl = workloads()
     w = wl[args.workload]
-    ms, main_ms, exp, fwd_ms = time_backward(w, args.steps, args.warmup, forward=True)
-    fl = flops(w)
-    tflops = fl / (ms * 1e-3) / 1e12
+    t = time_workload(w, args.steps, args.warmup, args.repeats, main_kernel=True)
+    head = workload_entry(w, t)
     nbytes = main_kernel_bytes(w)
-    achieved = nbytes / (main_ms * 1e-3) / 1e9
-    extra = {"main_kernel": MAIN_KERNEL, "main_kernel_ms": main_ms,
+    achieved = nbytes / (t["main_ms"] * 1e-3) / 1e9
+    extra = {"timing": f"median over {args.repeats} repeats (fresh tensors each) of the median of "
+                       f"{args.steps} per-step HIP-event times, after {args.warmup} warm-up steps and "
+                       "at least 0.5 s of backward steps",
+             "main_kernel": MAIN_KERNEL, "main_kernel_ms": t["main_ms"],
              "main_kernel_algorithmic_bytes": nbytes,
-             "main_kernel_attended_tflops": fl / (main_ms * 1e-3) / 1e12,
-             "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS, "relay_expiries": exp,
-             "attended_flops": fl, "forward_ms": fwd_ms,
-             "forward_tflops": 0.4 * fl / (fwd_ms * 1e-3) / 1e12}
-    if not args.no_extra:
-        # every other workload, timed the same way (the large GQA one with
-        # fewer steps); each entry names its workload's shape
-        for name in ("c3_atomic", "c1", "c2_4k", "c2_8k", "c2_4k_det", "c2_8k_det", "c4", "c4_f16", "c5"):
-            if name == args.workload:
-                continue
-            wx = wl[name]
-            big = wx.batch * wx.heads_q * wx.seq_q * wx.head_dim > (1 << 30)
-            st, wu = (max(3, args.steps // 4), max(3, args.warmup // 10)) if big else (max(5, args.steps // 2), args.warmup)
-            m2, mm2, _, fm2 = time_backward(wx, st, wu, forward=True)
-            extra[name] = {"workload": wx.name, "ms": m2, "tflops": flops(wx) / (m2 * 1e-3) / 1e12, "main_ms": mm2,
-                           "frac_bf16_mfma_peak": flops(wx) / (m2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                           "forward_ms": fm2, "forward_tflops": 0.4 * flops(wx) / (fm2 * 1e-3) / 1e12}
+             "main_kernel_attended_tflops": head["attended_flops"] / (t["main_ms"] * 1e-3) / 1e12,
+             "headline": head}
     line = {
-        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "metric": METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "repeats": args.repeats, "ms_per_step": t["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "head_dim": w.head_dim, "seq_len": w.seq_q, "window_left": w.window_left,
                    "mask": "causal_bottom_right" if w.bottom_right else "causal_top_left",
@@ -441,7 +576,28 @@ def main():
         "extra": extra,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+        c = cpu_leg(w, t["last"])
+        head["oracle"] = {k: c[k] for k in ("oracle_ms", "cores", "sample")}
+        head["parity"] = c["parity"]
+        line["cpu_baseline"] = {"value": c["oracle_tflops"], "unit": "TFLOP/s", "cores": c["cores"],
+                                "kind": "oracle", "sample": c["sample"] + f" of {w.name}, "
+                                f"{c['oracle_ms'] / 1e3:.2f} s"}
+    del t
+    if not args.no_extra:
+        for name in ("c3_atomic", "c1", "c2_4k", "c2_8k", "c2_4k_det", "c2_8k_det", "c4", "c4_f16", "c5",
+                     "nonsquare"):
+            if name == args.workload:
+                continue
+            wx = wl[name]
+            tx = time_workload(wx, args.steps, args.warmup, args.repeats)
+            e = workload_entry(wx, tx)
+            if not args.no_cpu_baseline:
+                c = cpu_leg(wx, tx["last"])
+                e["oracle"] = {k: c[k] for k in ("oracle_ms", "cores", "sample")}
+                e["parity"] = c["parity"]
+            extra[name] = e
+            del tx
+            torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
     if args.copy_calibration:
         copy_calibration()

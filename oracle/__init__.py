@@ -164,6 +164,25 @@ class Problem:
                        q_numel=int(total_q) * Hq * D, kv_numel=int(total_kv) * Hkv * D,
                        window_right=window_right)
 
+    @staticmethod
+    def for_workload(w) -> "Problem":
+        """The problem of a synthetic workload description: any object with
+        the fields of ``sliding_window_attention_flash_amd.synth.Workload``
+        (batch, heads, head_dim, lengths, mask, scale, sink, layout and the
+        packed slot capacities)."""
+        kw = dict(causal=w.causal, bottom_right=w.bottom_right, window_left=w.window_left,
+                  window_right=w.window_right, scale=w.softmax_scale, has_sink=w.sink)
+        if w.layout == "thd":
+            cu_q, cu_kv = [0], [0]
+            for c in w.cap_q:
+                cu_q.append(cu_q[-1] + c)
+            for c in w.cap_kv:
+                cu_kv.append(cu_kv[-1] + c)
+            return Problem.packed(w.heads_q, w.heads_kv, w.head_dim, cu_q, cu_kv, w.valid_len_q(),
+                                  w.valid_len_kv(), w.total_q, w.total_kv, **kw)
+        return Problem.dense(w.batch, w.heads_q, w.heads_kv, w.seq_q, w.seq_kv, w.head_dim,
+                             len_q=w.valid_len_q(), len_kv=w.valid_len_kv(), **kw)
+
     def _c(self, dtype_code: int) -> _Problem:
         self._keep = [self.len_q.contiguous(), self.len_kv.contiguous(),
                       self.row0_q.contiguous(), self.row0_kv.contiguous()]

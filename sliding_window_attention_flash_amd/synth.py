@@ -120,6 +120,11 @@ CONFIGS = {
     "c4_f16": Workload("c4_f16_b24_gqa28x4_d128_s128_br_w8000", torch.float16, 24, 28, 4, 128,
                        128, 128, bottom_right=True, window_left=8000),
     "c5": _c5(),
+    # the non-square class of the mixed study (PR #2352, opening section):
+    # short query, long key sequences under a long window (dtype not stated
+    # there; bf16 like the study's first class)
+    "nonsquare": Workload("ns_b12_gqa40x8_d64_q128_kv8960_br_w8000_bf16", torch.bfloat16, 12, 40, 8, 64,
+                          128, 8960, bottom_right=True, window_left=8000),
 }
 
 

@@ -55,19 +55,7 @@ def gpu_backward(w: Workload, inp: dict, o, lse, deterministic=None, nan_fill=Tr
 
 
 def oracle_problem(w: Workload) -> oracle.Problem:
-    kw = dict(causal=w.causal, bottom_right=w.bottom_right, window_left=w.window_left,
-              window_right=w.window_right, scale=w.softmax_scale, has_sink=w.sink)
-    if w.layout == "thd":
-        cu_q = [0]
-        for c in w.cap_q:
-            cu_q.append(cu_q[-1] + c)
-        cu_kv = [0]
-        for c in w.cap_kv:
-            cu_kv.append(cu_kv[-1] + c)
-        return oracle.Problem.packed(w.heads_q, w.heads_kv, w.head_dim, cu_q, cu_kv,
-                                     w.valid_len_q(), w.valid_len_kv(), w.total_q, w.total_kv, **kw)
-    return oracle.Problem.dense(w.batch, w.heads_q, w.heads_kv, w.seq_q, w.seq_kv, w.head_dim,
-                                len_q=w.valid_len_q(), len_kv=w.valid_len_kv(), **kw)
+    return oracle.Problem.for_workload(w)
 
 
 def row_masks(w: Workload, device="cpu"):
@@ -114,13 +102,22 @@ def assert_close(name: str, gpu: torch.Tensor, ref: torch.Tensor, rel_tol=REL_FR
     assert mab <= max_tol, f"{name}: max-abs error {mab:.3e} > {max_tol} * max|ref|"
 
 
-def compare_full(w: Workload, inp_cpu: dict, gpu: dict, check_fwd=True):
-    """Element-by-element comparison against the full fp64 oracle."""
+def oracle_full(w: Workload, inp_cpu: dict) -> dict:
+    """The full fp64 oracle backward (with its forward) on the inputs."""
     p = oracle_problem(w)
     t0 = time.time()
     ref = oracle.backward(p, inp_cpu["q"], inp_cpu["k"], inp_cpu["v"], inp_cpu["dO"],
                           inp_cpu["sink"])
     say(f"    oracle backward {time.time() - t0:.1f}s ({oracle.num_threads()} threads)")
+    return ref
+
+
+def compare_full(w: Workload, inp_cpu: dict, gpu: dict, check_fwd=True, ref=None):
+    """Element-by-element comparison against the full fp64 oracle (computed
+    here unless ``ref``, an earlier oracle_full result on the same inputs,
+    is given)."""
+    if ref is None:
+        ref = oracle_full(w, inp_cpu)
     vq, pq, vk, pk = row_masks(w)
     if check_fwd:
         o = gpu["o"].cpu()
@@ -162,6 +159,26 @@ def _lse_to_gpu_layout(w: Workload, lse_ref: torch.Tensor) -> torch.Tensor:
         n = w.valid_len_q()[b]
         out[b, :, :n] = lse_ref[b, :, :n]
     return out
+
+
+def batch_entries(w: Workload, inp_cpu: dict, gpu: dict, idx):
+    """A dense workload restricted to the batch entries ``idx``: the
+    workload, its CPU inputs and its GPU outputs (so the full oracle can
+    check whole entries of a workload too large to check at once)."""
+    assert w.layout == "bhsd"
+    sel = torch.tensor(idx)
+    pads = {}
+    if w.pad_len_q:
+        pads["pad_len_q"] = tuple(w.pad_len_q[i] for i in idx)
+    if w.pad_len_kv:
+        pads["pad_len_kv"] = tuple(w.pad_len_kv[i] for i in idx)
+    ws = w.with_(name=f"{w.name}_b{'_'.join(map(str, idx))}", batch=len(idx), **pads)
+    inp = {k: (v[sel] if isinstance(v, torch.Tensor) and k in ("q", "k", "v", "dO") else v)
+           for k, v in inp_cpu.items()}
+    gsel = sel.to(gpu["dq"].device)
+    out = {k: (v[gsel] if isinstance(v, torch.Tensor) and k in ("o", "lse", "dq", "dk", "dv") else v)
+           for k, v in gpu.items()}
+    return ws, inp, out
 
 
 def run_gpu(w: Workload, seed=0, deterministic=None, runs=1):

@@ -1,15 +1,16 @@
 """GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
 
-Small problems (several tiles, ragged tails, every mask variant) are compared
-element by element with the full oracle; the full-size workloads are
-compared on sampled gradient rows computed one at a time by the oracle, plus
-properties over the whole output.  Outputs start as NaN so an element the
+Every problem is compared element by element with the full oracle: small
+problems (several tiles, ragged tails, every mask variant) and the full-size
+workloads (the largest GQA one on whole batch entries), which additionally
+get a sampled-row comparison.  Outputs start as NaN so an element the
 kernels never write fails the test.
 """
 import pytest
 import torch
 
-from gpu_harness import (assert_close, compare_full, compare_sampled, run_gpu, say)
+from gpu_harness import (assert_close, batch_entries, compare_full, compare_sampled, oracle_full, run_gpu,
+                         say)
 from sliding_window_attention_flash_amd.synth import CONFIGS, Workload, packed_lengths
 
 pytestmark = pytest.mark.gpu
@@ -164,6 +165,9 @@ def test_keys_outside_every_window_are_exact_zero():
 
 
 # ---- full-size workloads -----------------------------------------------------
+# Every full-size workload is compared element by element with the full
+# oracle (c4, too large for one oracle run, on whole batch entries), with the
+# sampled row comparison kept as an extra check.
 
 
 def test_c2_s4096_full_oracle():
@@ -173,31 +177,42 @@ def test_c2_s4096_full_oracle():
     compare_full(w, inp, out)
 
 
-def test_c2_s8192_sampled():
+def test_c2_s8192_full_oracle():
     w = CONFIGS["c2_8k"]
-    say(f"case {w.name} (sampled)")
+    say(f"case {w.name} (full oracle, then sampled rows)")
     inp, out, _ = run_gpu(w, seed=22)
+    compare_full(w, inp, out)
     compare_sampled(w, inp, out)
 
 
-def test_c3_s32768_relay_bitwise_and_sampled():
+def test_c3_s32768_relay_bitwise_and_full_oracle_both_modes():
     w = CONFIGS["c3"]
-    say(f"case {w.name}: 3 relay runs, sampled oracle, atomic comparison")
+    say(f"case {w.name}: 3 relay runs, full oracle for the relay and the atomic run")
     inp, outs, _ = run_gpu(w, seed=23, runs=3)
     for o in outs:
         assert o["expiries"] == 0
     for key in ("dq", "dk", "dv"):
         assert torch.equal(outs[0][key], outs[1][key]) and torch.equal(outs[0][key], outs[2][key]), key
+    ref = oracle_full(w, inp)
+    say("  relay run vs oracle")
+    compare_full(w, inp, outs[0], ref=ref)
     compare_sampled(w, inp, outs[0])
     _, at, _ = run_gpu(w, seed=23, deterministic=False)
+    say("  atomic run vs oracle")
+    compare_full(w, inp, at, ref=ref)
     for key in ("dq", "dk", "dv"):
         assert_close(f"{key} det/at", outs[0][key].float(), at[key].float())
 
 
-def test_c4_gqa_s16484_sampled():
+def test_c4_gqa_s16484_whole_batch_entries_full_oracle():
     w = CONFIGS["c4"]
-    say(f"case {w.name} (sampled)")
+    say(f"case {w.name}: batch entries 0 and 11 (all 48 heads, all rows) against the full oracle")
     inp, out, _ = run_gpu(w, seed=24)
+    ws, inp2, out2 = batch_entries(w, inp, out, [0, w.batch - 1])
+    compare_full(ws, inp2, out2)
+    # every entry: no element left unwritten
+    for name in ("dq", "dk", "dv"):
+        assert not torch.isnan(out[name]).any(), f"{name}: NaN somewhere in the full output"
     compare_sampled(w, inp, out, n_q=192, n_kv=96)
 
 
