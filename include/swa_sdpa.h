@@ -192,6 +192,24 @@ sdpa_status sdpa_bwd_run_events(const sdpa_bwd_plan_t* plan, const sdpa_bwd_tens
 void sdpa_bwd_plan_destroy(sdpa_bwd_plan_t* plan);
 
 /*
+ * sdpa_bwd_run_noalloc -- sdpa_bwd_run for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same kernels and results as
+ * sdpa_bwd_run (bitwise in the ordered modes), but the workspace is the
+ * library's own 64 MiB scratch array: each GPU the library runs on holds
+ * one until the process ends.  The caller still passes (and owns) the
+ * inputs and outputs.  No allocation and no synchronization happen here.
+ * Errors: SDPA_ERR_WORKSPACE (with a message naming both sizes) when the
+ * plan's workspace (the size sdpa_bwd_plan reported) exceeds 64 MiB;
+ * SDPA_ERR_HIP if the scratch address cannot be looked up; otherwise those
+ * of sdpa_bwd_run.  Every call on one GPU shares that GPU's array and it
+ * keeps the last call's contents (the kernels clear what must start at
+ * zero): calls that overlap on one GPU, on any streams, race.
+ */
+sdpa_status sdpa_bwd_run_noalloc(const sdpa_bwd_plan_t* plan, const sdpa_bwd_tensors* tensors,
+                                 hipStream_t stream);
+
+/*
  * sdpa_fwd_plan / sdpa_fwd_run -- the window-trimmed forward
  * ([PR866] Problem: the forward already trims its kv range by the window):
  * each q-tile walks only the kv-tiles [kv_first, kv_last] its rows can see

@@ -51,6 +51,7 @@ EXPORTS = [
     "sdpa_bwd_plan", "sdpa_bwd_run", "sdpa_bwd_run_events", "sdpa_bwd_plan_destroy",
     "sdpa_fwd_plan", "sdpa_fwd_run", "sdpa_fwd_plan_destroy", "sdpa_bwd_schedule",
     "sdpa_bwd_relay_expiries", "sdpa_bwd_plan_set_relay_watchdog", "sdpa_status_string", "sdpa_last_error",
+    "sdpa_bwd_run_noalloc",
 ]
 
 _lib = None
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_bwd_run.argtypes = [_vp, ctypes.POINTER(BwdTensors), _vp, ctypes.c_size_t, _vp]
     lib.sdpa_bwd_run_events.argtypes = [_vp, ctypes.POINTER(BwdTensors), _vp, ctypes.c_size_t,
                                         _vp, _vp, _vp]
+    lib.sdpa_bwd_run_noalloc.argtypes = [_vp, ctypes.POINTER(BwdTensors), _vp]
+    lib.sdpa_bwd_run_noalloc.restype = ctypes.c_int
     lib.sdpa_bwd_plan_destroy.argtypes = [_vp]
     lib.sdpa_bwd_plan_destroy.restype = None
     lib.sdpa_fwd_plan.argtypes = [ctypes.POINTER(AttnDesc), PP, sz]

@@ -67,6 +67,12 @@ def sdpa_bwd_run(plan: BwdPlan, tensors: BwdTensors, workspace: Optional[torch.T
           "sdpa_bwd_run")
 
 
+def sdpa_bwd_run_noalloc(plan: BwdPlan, tensors: BwdTensors, stream=None) -> None:
+    """The backward on the library's own scratch workspace (no allocation)."""
+    check(_lib.load().sdpa_bwd_run_noalloc(plan.handle, ctypes.byref(tensors), _stream(stream)),
+          "sdpa_bwd_run_noalloc")
+
+
 def sdpa_bwd_run_events(plan: BwdPlan, tensors: BwdTensors, workspace, stream, start_event,
                         stop_event) -> None:
     """``start_event`` / ``stop_event`` are raw hipEvent_t handles (ints)."""

@@ -337,3 +337,16 @@ def test_stream_schedule_shift_forms_brute_force(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "stream sched: ok" in r.stdout, r.stdout + r.stderr
 
+
+def test_noalloc_rejects_a_workspace_beyond_its_scratch(lib):
+    # batch 2, 16 heads, S = 32768, window 128, ordered: ~0.5 GB of workspace,
+    # more than the 64 MiB scratch; rejected before any device call
+    d = _desc(B=2, Hq=16, Hkv=16, D=64, Sq=32768, Skv=32768, window_left=128, deterministic=1)
+    plan = api.sdpa_bwd_plan(d)
+    assert plan.workspace_bytes > 64 << 20
+    t = _lib.BwdTensors()
+    rc = lib.sdpa_bwd_run_noalloc(plan.handle, ctypes.byref(t), None)
+    assert rc == _lib.SDPA_ERR_WORKSPACE
+    msg = lib.sdpa_last_error()
+    assert b"scratch" in msg and str(plan.workspace_bytes).encode() in msg
+    assert lib.sdpa_bwd_run_noalloc(None, ctypes.byref(t), None) == _lib.SDPA_ERR_INVALID_ARG
