@@ -448,26 +448,42 @@ def summarize_counters(dirs, out, commands, workload):
 ORACLE_FULL_WORK = 1.2e10
 
 
+def _leading(w, n):
+    """Workload w cut to its first n batch entries or packed sequences."""
+    if w.layout == "thd":
+        return w.with_(name=f"{w.name}_s0-{n - 1}", batch=n, len_q=w.len_q[:n], len_kv=w.len_kv[:n],
+                       cap_q=w.cap_q[:n], cap_kv=w.cap_kv[:n], seq_q=max(w.cap_q[:n]),
+                       seq_kv=max(w.cap_kv[:n]))
+    return w.with_(name=f"{w.name}_b0-{n - 1}", batch=n,
+                   pad_len_q=w.pad_len_q[:n] if w.pad_len_q else None,
+                   pad_len_kv=w.pad_len_kv[:n] if w.pad_len_kv else None)
+
+
 def cpu_leg(w, last):
     """The fp64 oracle on the inputs of the workload's last timed repeat:
     its wall time and the per-gradient parity errors of the GPU outputs.
-    Dense workloads too large for one oracle run are checked on their first
-    batch entries (as many as fit ORACLE_FULL_WORK, at least one)."""
+    Workloads too large for one oracle run are checked on their leading
+    batch entries or packed sequences (as many as fit ORACLE_FULL_WORK, at
+    least one)."""
     import oracle
     import torch
     from sliding_window_attention_flash_amd.synth import attended_pairs_per_head
 
-    work = attended_pairs_per_head(w) * w.heads_q * w.head_dim
+    def work(wx):
+        return attended_pairs_per_head(wx) * wx.heads_q * wx.head_dim
+
+    # the leading batch entries (dense) or packed sequences that fit the
+    # budget, at least one; rows [0, nq) / [0, nk) of the packed tensors
     nb = w.batch
-    if w.layout == "bhsd" and work > ORACLE_FULL_WORK:
-        nb = max(1, int(ORACLE_FULL_WORK / (work / w.batch)))
-    ws = w if nb == w.batch else w.with_(name=f"{w.name}_b0-{nb - 1}", batch=nb,
-                                         pad_len_q=w.pad_len_q[:nb] if w.pad_len_q else None,
-                                         pad_len_kv=w.pad_len_kv[:nb] if w.pad_len_kv else None)
+    if work(w) > ORACLE_FULL_WORK:
+        nb = 1
+        while nb < w.batch and work(_leading(w, nb + 1)) <= ORACLE_FULL_WORK:
+            nb += 1
+    ws = w if nb == w.batch else _leading(w, nb)
+    nq = sum(ws.cap_q) if w.layout == "thd" else nb
+    nk = sum(ws.cap_kv) if w.layout == "thd" else nb
     inp = last["inp"]
-    cpu = {}
-    for k in ("q", "k", "v", "dO"):
-        cpu[k] = inp[k][:nb].cpu() if ws is not w else inp[k].cpu()
+    cpu = {k: inp[k][:(nk if k in ("k", "v") else nq)].cpu() for k in ("q", "k", "v", "dO")}
     sink = inp["sink"].cpu() if inp["sink"] is not None else None
     p = oracle.Problem.for_workload(ws)
     t0 = time.perf_counter()
@@ -475,11 +491,13 @@ def cpu_leg(w, last):
     dt = time.perf_counter() - t0
     errs = {}
     pairs = [("dQ", "dq", "dq"), ("dK", "dk", "dk"), ("dV", "dv", "dv")]
-    if w.sink and ws is w:
+    if w.sink and ws is w:  # dSink sums over every sequence
         pairs.append(("dSink", "dsink", "dsink"))
     for name, gk, rk in pairs:
         g = last[gk]
-        g = (g[:nb] if ws is not w and name != "dSink" else g).double().cpu().reshape(-1)
+        if name != "dSink":
+            g = g[:(nk if name in ("dK", "dV") else nq)]
+        g = g.double().cpu().reshape(-1)
         r = ref[rk].reshape(-1)
         rn, rmax = float(r.norm()), float(r.abs().max())
         d = g - r
@@ -488,8 +506,9 @@ def cpu_leg(w, last):
                       "nan": bool(torch.isnan(g).any())}
     units = ws.batch * ws.heads_kv
     sample_pairs = attended_pairs_per_head(ws) * ws.heads_q
+    what = "packed sequences" if w.layout == "thd" else "batch entries"
     return {"oracle_ms": dt * 1e3, "cores": min(oracle.num_threads(), units),
-            "sample": ("whole workload" if ws is w else f"batch entries 0..{nb - 1} of {w.batch}")
+            "sample": ("whole workload" if ws is w else f"{what} 0..{nb - 1} of {w.batch}")
                       + f": {sample_pairs} attended pairs, fp64 forward + backward",
             "oracle_tflops": 10.0 * ws.head_dim * sample_pairs / dt / 1e12,
             "parity": errs}

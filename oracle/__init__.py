@@ -63,7 +63,7 @@ class _Problem(ctypes.Structure):
 def build(out_path: str = _LIB_PATH, mutant: int = 0) -> str:
     """Compile the oracle with gcc (``mutant`` > 0 plants a known mistake,
     used only by the test that checks the pins catch mistakes)."""
-    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-o", out_path, _SRC, "-lm"]
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-o", out_path, _SRC, "-lm", "-lpthread"]
     if mutant:
         cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
     subprocess.run(cmd, check=True)
