@@ -365,33 +365,49 @@ def _pick(means, pat):
 
 
 def summarize_traffic(fetch_dir, write_dir, out, command, workload):
+    """HBM bytes per dispatch of every backward kernel in two rocprofv3
+    --pmc runs (FETCH_SIZE, then WRITE_SIZE), each counter divided by what it
+    reads per byte moved by the calibration copy.  The TRAFFIC record (what
+    the JSON line's roofline.traffic reads) is written for the dominant
+    kernel of the default workload when it ran."""
     w = workloads()[workload]
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
-    nf, kf = _pick(fetch, MAIN_KERNEL)
-    nw, kw = _pick(write, MAIN_KERNEL)
     _, cf = _pick(fetch, COPY_KERNEL)
     _, cw = _pick(write, COPY_KERNEL)
     copy_kib = COPY_BYTES / 1024
     ff, fw = cf / copy_kib, cw / copy_kib  # counter KiB per byte-KiB moved
-    traffic = kf * 1024 / ff + kw * 1024 / fw
-    algo = main_kernel_bytes(w)
-    rec = {"kernel": MAIN_KERNEL, "workload": w.name, "launches_fetch": nf, "launches_write": nw,
-           "fetch_kib_per_launch": kf, "write_kib_per_launch": kw, "copy_bytes": COPY_BYTES,
-           "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_factor": ff, "write_factor": fw,
-           "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": algo,
-           "source_sha256": kernel_source_hash()}
-    lines = [f"# HBM traffic of {MAIN_KERNEL}, workload {w.name}", "",
+    lines = [f"# HBM traffic per kernel, workload {w.name}", "",
              "commands (FETCH_SIZE pass, then WRITE_SIZE pass):", *[f"    {c}" for c in command], "",
-             f"FETCH_SIZE per launch   {kf:14.1f} KiB  ({nf} launches)",
-             f"WRITE_SIZE per launch   {kw:14.1f} KiB  ({nw} launches)",
              f"calibration copy of {COPY_BYTES} bytes ({COPY_KERNEL}): FETCH_SIZE {cf:.1f} KiB, "
              f"WRITE_SIZE {cw:.1f} KiB",
-             f"factors (counter bytes per byte moved): fetch {ff:.4f}, write {fw:.4f}",
-             f"HBM traffic per launch  {traffic / 1e6:14.2f} MB  (fetch {kf * 1024 / ff / 1e6:.2f} MB, "
-             f"write {kw * 1024 / fw / 1e6:.2f} MB)",
-             f"algorithmic bytes       {algo / 1e6:14.2f} MB  (traffic / algorithmic = {traffic / algo:.3f})",
-             "", "TRAFFIC " + json.dumps(rec)]
+             f"factors (counter bytes per byte moved): fetch {ff:.4f}, write {fw:.4f}", "",
+             f"{'kernel':20s} {'launches':>8s} {'fetch MB':>10s} {'write MB':>10s} {'total MB':>10s}"]
+    rec = None
+    total = 0.0
+    for k in SQ_KERNELS:
+        try:
+            nf, kf = _pick(fetch, k)
+            nw, kw = _pick(write, k)
+        except RuntimeError:
+            continue
+        fb, wb = kf * 1024 / ff, kw * 1024 / fw
+        total += fb + wb if k != "fwd_kernel" else 0.0
+        lines.append(f"{k:20s} {nf:8d} {fb / 1e6:10.2f} {wb / 1e6:10.2f} {(fb + wb) / 1e6:10.2f}")
+        if k == MAIN_KERNEL:
+            algo = main_kernel_bytes(w)
+            rec = {"kernel": MAIN_KERNEL, "workload": w.name, "launches_fetch": nf, "launches_write": nw,
+                   "fetch_kib_per_launch": kf, "write_kib_per_launch": kw, "copy_bytes": COPY_BYTES,
+                   "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_factor": ff, "write_factor": fw,
+                   "traffic_bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": algo,
+                   "source_sha256": kernel_source_hash()}
+    comp = compulsory_bytes(w)
+    lines += ["", f"backward kernels together   {total / 1e6:10.2f} MB per step; compulsory bytes "
+                  f"{comp / 1e6:.2f} MB (traffic / compulsory = {total / comp:.3f})"]
+    if rec:
+        lines += [f"{MAIN_KERNEL}: algorithmic bytes {rec['algorithmic_bytes_per_launch'] / 1e6:.2f} MB "
+                  f"(traffic / algorithmic = {rec['traffic_bytes_per_launch'] / rec['algorithmic_bytes_per_launch']:.3f})",
+                  "", "TRAFFIC " + json.dumps(rec)]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -536,6 +552,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--repeats", type=int, default=3)
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="backward steps run before each workload's first repeat, in seconds of wall time")
     ap.add_argument("--workload", default="c3", choices=sorted(workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU leg (oracle time and parity errors)")
@@ -571,13 +589,13 @@ def main():
         sys.exit(1)
     wl = workloads()
     w = wl[args.workload]
-    t = time_workload(w, args.steps, args.warmup, args.repeats, main_kernel=True)
+    t = time_workload(w, args.steps, args.warmup, args.repeats, main_kernel=True, min_warm_s=args.warm_seconds)
     head = workload_entry(w, t)
     nbytes = main_kernel_bytes(w)
     achieved = nbytes / (t["main_ms"] * 1e-3) / 1e9
     extra = {"timing": f"median over {args.repeats} repeats (fresh tensors each) of the median of "
                        f"{args.steps} per-step HIP-event times, after {args.warmup} warm-up steps and "
-                       "at least 0.5 s of backward steps",
+                       f"at least {args.warm_seconds} s of backward steps",
              "main_kernel": MAIN_KERNEL, "main_kernel_ms": t["main_ms"],
              "main_kernel_algorithmic_bytes": nbytes,
              "main_kernel_attended_tflops": head["attended_flops"] / (t["main_ms"] * 1e-3) / 1e12,
@@ -608,7 +626,7 @@ def main():
             if name == args.workload:
                 continue
             wx = wl[name]
-            tx = time_workload(wx, args.steps, args.warmup, args.repeats)
+            tx = time_workload(wx, args.steps, args.warmup, args.repeats, min_warm_s=args.warm_seconds)
             e = workload_entry(wx, tx)
             if not args.no_cpu_baseline:
                 c = cpu_leg(wx, tx["last"])

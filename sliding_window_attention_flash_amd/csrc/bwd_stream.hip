@@ -47,8 +47,9 @@
 // Measured on gfx950 (SQ_LDS_BANK_CONFLICT): 16-byte row reads are
 // conflict-free in any layout, and this permutation also makes the
 // transposed reads conflict-free (a plain 128-byte pitch costs 4x).  Band
-// rows are 208 elements apart (416 bytes): the 8 rows one half-wave's
-// transposed read touches then fall on 8 disjoint groups of 8 banks.
+// rows are 208 elements apart (416 bytes), each group of 4 rows 8 bytes
+// further than the one before: the dS^T writes and the transposed reads
+// of the bands are then conflict-free as well (see band_wr).
 // Transposed operands use ds_read_b64_tr_b16: within each 16-lane group,
 // lane i receives element (i % 4) of lanes i / 4 + 4e (e = 0..3), so a lane
 // pointing at row r0 + i / 4, column c0 + 4 (i % 4) receives rows
@@ -71,11 +72,14 @@ constexpr int NTHR = 64 * NWAVE;
 constexpr int NPAIR = 5;      // block pairs a band holds
 constexpr int BPOS = 2 * NPAIR + 2;  // band block positions, guards included
 constexpr int BP = 208;       // band row pitch (elements), >= 16 * BPOS
+constexpr int BSH = 4;        // extra offset (elements) per 4-row group of a band
+constexpr int BAND = 16 * BP + 4 * BSH;  // elements of one wave's band
 
 static_assert(STEP == StreamSched::kStep && kTile == StreamSched::kTileQ,
               "the kernel's kv-step and q-tile are the shift forms' tiles");
 static_assert(NACT >= (STEP + 128) / 64 + 1, "a kv-step feeds at most ceil((128 + W) / 64) + 1 q-tiles, W <= 128");
 static_assert(2 * NPAIR >= (16 + 128 + 15) / 16 + 1, "a 16-key band spans at most 10 16-row blocks, W <= 128");
+static_assert(BAND % 8 == 0, "bands are cleared in 16-byte vectors");
 
 typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
 
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   __shared__ __align__(16) T sRing[2][NRB][16 * TROW];
   __shared__ __align__(16) float sLD[2][NRB][16];
   __shared__ __align__(16) T sK[STEP * TROW];
-  __shared__ __align__(16) T sBand[NWAVE][16 * BP];  // dS^T [key][block position, row]
+  __shared__ __align__(16) T sBand[NWAVE][BAND];  // dS^T [key][block position, row]
   __shared__ int sTicket;
 
   const Problem& p = a.p;
@@ -242,8 +246,15 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   // K^T columns of this wave's dQ half (kept out of a runtime-indexed array,
   // which the compiler would place in scratch memory)
   const int tr_off_k0 = tr_lane_off(c, gq, 2 * wd), tr_off_k1 = tr_lane_off(c, gq, 2 * wd + 1);
-  const int band_wr = c * BP + 4 * gq;                         // dS^T write: key c, rows 4 gq ..
-  const int band_rd = (4 * gq + (c >> 2)) * BP + 4 * (c & 3);  // transposed read
+  // Band row r starts at r BP + BSH (r / 4) elements.  8-byte LDS accesses
+  // are served 16 lanes at a time over 32 banks (SQ_LDS_BANK_CONFLICT: a
+  // plain 416-byte pitch costs 4x on the dS^T writes, a shift of rows
+  // 8 .. 15 alone 2x): 8 bytes per 4-row group put the 16 rows of a
+  // write's lane group on distinct bank pairs, while the 4 rows of a
+  // transposed read's lane group keep disjoint 32-byte spans.
+  const int band_wr = c * BP + BSH * (c >> 2) + 4 * gq;  // dS^T write: key c, rows 4 gq ..
+  const int band_rd_row = 4 * gq + (c >> 2);
+  const int band_rd = band_rd_row * BP + BSH * (band_rd_row >> 2) + 4 * (c & 3);  // transposed read
   T* const myband = sBand[w];
   const uint32_t band0 = lds_addr(&sBand[0][0]);
 
@@ -390,7 +401,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     // While they are in flight: the bands start (and their guard positions
     // stay) zero, and so does the ring, so that a ring slot read before any
     // tile was staged in it holds finite values (see the pair geometry).
-    for (int e = tid; e < NWAVE * 16 * BP / 8; e += NTHR) reinterpret_cast<V8*>(&sBand[0][0])[e] = zero8;
+    for (int e = tid; e < NWAVE * BAND / 8; e += NTHR) reinterpret_cast<V8*>(&sBand[0][0])[e] = zero8;
     for (int e = tid; e < 2 * NRB * 16 * TROW / 8; e += NTHR) reinterpret_cast<V8*>(&sRing[0][0][0])[e] = zero8;
     for (int e = tid; e < 2 * NRB * 16 / 4; e += NTHR)
       reinterpret_cast<f32x4*>(&sLD[0][0][0])[e] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -611,8 +622,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < NACT; ++k) {
           if (!((act >> k) & 1u)) continue;
-          const uint32_t ya = bbase + (uint32_t)(2 * ks * 16 * BP * sizeof(T)) + 32 * (4 * k - 2 * ks);
-          const u32x2 lo = lds_tr4(ya), hi = lds_tr4(ya + 16 * BP * sizeof(T) - 32);
+          const uint32_t ya = bbase + (uint32_t)(2 * ks * BAND * sizeof(T)) + 32 * (4 * k - 2 * ks);
+          const u32x2 lo = lds_tr4(ya), hi = lds_tr4(ya + BAND * sizeof(T) - 32);
           const V8 st = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
           dQa[k][0] = mfma16(kt0, st, dQa[k][0]);
           dQa[k][1] = mfma16(kt1, st, dQa[k][1]);
