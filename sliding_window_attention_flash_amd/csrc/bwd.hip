@@ -346,6 +346,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
     stage_store();
   }
   __syncthreads();
+  // Every load so far has landed (or the loop below never runs), but on the
+  // path that skips the staging the compiler would keep the K / V loads
+  // outstanding and make each visit's first products wait for the next
+  // visit's prefetch: settle them here, once.
+  __builtin_amdgcn_s_waitcnt(0);
 
   T* dqp = static_cast<T*>(a.dq);
   for (int v = 0; v < nvisit; ++v) {

@@ -139,6 +139,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
   load_kv(cj);
   store_kv(0);
   __syncthreads();
+  // The compiler may issue the Q loads after the K / V loads, so that the
+  // staging above does not wait for them; left outstanding, they would make
+  // every pair's first products wait for that pair's K / V prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
   for (int n = 0;; ++n) {
     int ni = ci, nj = cj + 1;
     if (nj > g.kv_last(ci)) {
@@ -243,6 +247,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
     if (!more) break;
     store_kv(buf ^ 1);
     __syncthreads();  // buffer buf is free; the next one is staged
+    // the next q-tile's rows (if this pair ended one) are needed by the next
+    // pair's first products: settle them before its prefetch is issued
+    if (RUN) __builtin_amdgcn_s_waitcnt(0);
     ci = ni;
     cj = nj;
   }
