@@ -188,6 +188,11 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
     p.fwd_tiles = d->head_dim == 128 && band <= 256 ? 8 : (band <= 64 ? 4 : 1);
     if (d->q_run_tiles > 0) p.dq_tiles = p.fwd_tiles = d->q_run_tiles;
   }
+  // Where the dQ pass walks runs of q-tiles (short windows, whose passes
+  // stream Q / dO / O at full size), it also forms delta from the dO rows
+  // it holds, replacing the bwd_dot pass and its second read of dO; the
+  // per-q-tile dSink partials stay with bwd_dot.
+  p.dq_delta = p.split_dq && p.dq_tiles > 1 && !d->has_sink;
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one
     // block per MI355X CU, never shorter than 2 steps (so a q-tile has at
@@ -368,15 +373,18 @@ sdpa_status bwd_run(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensors* t, void* 
   a.relay_bias = pl->relay_bias;
 
   hipError_t e;
-  if ((e = swa::launch_bwd_dot(a, stream)) != hipSuccess)
+  // dq_delta: the dQ pass forms delta, so it runs first and bwd_dot not at all
+  if (!a.p.dq_delta && (e = swa::launch_bwd_dot(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dot launch: %s", hipGetErrorString(e));
+  if (a.p.dq_delta && (e = swa::launch_bwd_dq(a, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "bwd_dq launch: %s", hipGetErrorString(e));
   if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   if ((e = swa::launch_bwd_main(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_main launch: %s", hipGetErrorString(e));
   if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if (a.p.split_dq && (e = swa::launch_bwd_dq(a, stream)) != hipSuccess)
+  if (a.p.split_dq && !a.p.dq_delta && (e = swa::launch_bwd_dq(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dq launch: %s", hipGetErrorString(e));
   if (d.has_sink && (e = swa::launch_bwd_dsink(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dsink launch: %s", hipGetErrorString(e));

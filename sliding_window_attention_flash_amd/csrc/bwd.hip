@@ -518,10 +518,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
 // leaves each lane with 4 consecutive head-dim values of one row: one 8-byte
 // store per 16 columns.  A wave skips the 16-key blocks its rows cannot see.
 
+// With DELTA (runs of q-tiles, no sink) the pass also forms each row's
+// delta = <dO, O> from the dO rows it holds and an extra read of O, and
+// stores it for bwd_main, which then runs after it: the separate bwd_dot
+// pass, which reads dO and O once more, is not launched.
+//
 // Occupancy: two blocks per CU, four for single-tile blocks at D = 64, whose
 // registers fit in 128 per lane.
-template <typename T, int D, bool RUN>
+template <typename T, int D, bool RUN, bool DELTA>
 __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_kernel(BwdArgs a) {
+  static_assert(!DELTA || RUN, "delta is formed on the q-tile-run path");
   typedef typename Elem<T>::vec8 V8;
   constexpr int NS = D / 32;   // k-steps over the head dim
   constexpr int NDB = D / 16;  // 16-column blocks of the head dim
@@ -535,6 +541,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
   const Problem& p = a.p;
   const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // bwd_dot is not launched: clear the control words it would have
+  if (DELTA && blockIdx.x == 0 && tid < 2) a.ctl[tid] = 0;
 
   // block -> (sequence, kv head, run of q-tiles, head within the group): the
   // heads that share a kv head, and neighbouring runs, read the same K / V
@@ -587,10 +595,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
   // past the sequence repeat its last row and carry LSE = +inf, so that
   // P = exp2(-inf) = 0
   V8 qB[NS], oB[NS], nqB[NS], noB[NS];
+  V8 xB[DELTA ? NS : 1], nxB[DELTA ? NS : 1];  // O rows (DELTA)
   float lse2, del, nlse2 = 0.f, ndel = 0.f;
   const T* q0h = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, h, 0) + 8 * gq;
   const T* o0h = static_cast<const T*>(a.dO) + elem_off(p, p.sdo, b, s.row0_q, h, 0) + 8 * gq;
-  auto load_q = [&](int i, V8* qv, V8* ov, float& l2, float& dl) {
+  const T* x0h = static_cast<const T*>(a.o) + elem_off(p, p.so, b, s.row0_q, h, 0) + 8 * gq;
+  auto load_q = [&](int i, V8* qv, V8* ov, V8* xv, float& l2, float& dl) {
     const int row = i * kTile + 16 * w + c;
     const int qr = min(row, s.len_q - 1);
     const T* qrow = row_at(q0h, qr, p.sq[2]);
@@ -600,13 +610,34 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
       qv[st] = ld8(qrow + 32 * st);
       ov[st] = ld8(orow + 32 * st);
     }
+    if (DELTA) {
+      const T* xrow = row_at(x0h, qr, p.so[2]);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) xv[st] = ld8(xrow + 32 * st);
+    }
     l2 = INFINITY;
     dl = 0.f;
     if (row < s.len_q) {
       const int64_t si = s.stat0 + h * s.stat_hs + row;
       l2 = a.lse[si] * kLog2e;
-      dl = a.delta[si];
+      if (!DELTA) dl = a.delta[si];
     }
+  };
+  // DELTA: delta of the lane's row from its dO and O slices (the 4 lanes
+  // holding a row's head-dim quarters reduce by two exchanges); 0 past the
+  // sequence; stored for bwd_main for every row of the slot
+  auto form_delta = [&](int i, const V8* ov, const V8* xv) {
+    float acc = 0.f;
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += Elem<T>::to_float(ov[st][e]) * Elem<T>::to_float(xv[st][e]);
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    const int row = i * kTile + 16 * w + c;
+    const float dl = row < s.len_q ? acc : 0.f;
+    if (gq == 0 && row < s.cap_q) a.delta[s.stat0 + h * s.stat_hs + row] = dl;
+    return dl;
   };
 
   // K / V staging (a visited kv-tile: len_kv > 0); rows past the sequence
@@ -643,7 +674,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
   const int tlo = p.causal ? -p.right : -(1 << 28), thi = p.window >= 0 ? p.window : (1 << 28);
   const unsigned trange = (unsigned)(thi - tlo);
 
-  load_q(ci, qB, oB, lse2, del);
+  load_q(ci, qB, oB, xB, lse2, del);
+  if (DELTA) del = form_delta(ci, oB, xB);
   load_kv(cj);
   store_kv(0);
   __syncthreads();
@@ -658,7 +690,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
     const bool more = ni < ib;
     if (more) {
       load_kv(nj);
-      if (RUN && ni != ci) load_q(ni, nqB, noB, nlse2, ndel);
+      if (RUN && ni != ci) load_q(ni, nqB, noB, nxB, nlse2, ndel);
     }
     const int buf = n & 1;
     const T* cK = sK[buf];
@@ -731,7 +763,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
           oB[st] = noB[st];
         }
         lse2 = nlse2;
-        del = ndel;
+        del = DELTA ? form_delta(ni, noB, nxB) : ndel;
       }
     }
     if (!more) break;
@@ -796,15 +828,19 @@ static hipError_t dq_t(const BwdArgs& a, hipStream_t st) {
   const int n = a.p.B * a.p.Hq * ((a.p.n_q_tiles + a.p.dq_tiles - 1) / a.p.dq_tiles);
   const bool run = a.p.dq_tiles > 1;
   if (a.p.D == 64) {
-    if (run)
-      hipLaunchKernelGGL((bwd_dq_kernel<T, 64, true>), dim3(n), dim3(kThreads), 0, st, a);
+    if (a.p.dq_delta)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 64, true, true>), dim3(n), dim3(kThreads), 0, st, a);
+    else if (run)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 64, true, false>), dim3(n), dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<T, 64, false>), dim3(n), dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 64, false, false>), dim3(n), dim3(kThreads), 0, st, a);
   } else {
-    if (run)
-      hipLaunchKernelGGL((bwd_dq_kernel<T, 128, true>), dim3(n), dim3(kThreads), 0, st, a);
+    if (a.p.dq_delta)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 128, true, true>), dim3(n), dim3(kThreads), 0, st, a);
+    else if (run)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 128, true, false>), dim3(n), dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<T, 128, false>), dim3(n), dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, 128, false, false>), dim3(n), dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -44,6 +44,7 @@ struct Problem {
   // chunk and chunks per sequence; stream == 0 selects the per-tile kernel
   int split_dq;  // general path, unordered mode: dQ by its own q-major pass
   int dq_tiles;  // consecutive q-tiles one block of that pass walks
+  int dq_delta;  // that pass forms delta and runs before bwd_main (no bwd_dot)
   int fwd_tiles; // the same for the forward
   int stream;
   int step_kv;

@@ -116,20 +116,23 @@ def test_relay_bitwise_repeatable_and_matches_atomic():
     compare_full(w, inp, outs[0], check_fwd=False)
 
 
-@pytest.mark.parametrize("det", [1, 2], ids=["ordered", "tile_relay"])
-def test_general_path_bitwise_repeatable(det):
-    # GQA, bottom-right, sinks, head_dim 128: the per-tile kernel with the
-    # q-major dQ pass (1) or the per-kv-tile relay (2)
-    w = _wl("det_gqa_br_w100_d128_s777", BF16, 2, 8, 2, 128, 777, 900, bottom_right=True, window_left=100,
-            sink=True)
+@pytest.mark.parametrize("det,sink", [(1, True), (2, True), (1, False)],
+                         ids=["ordered", "tile_relay", "ordered_delta_in_dq_pass"])
+def test_general_path_bitwise_repeatable(det, sink):
+    # GQA, bottom-right, head_dim 128: the per-tile kernel with the q-major
+    # dQ pass (1) or the per-kv-tile relay (2); without a sink the dQ pass
+    # walks q-tile runs and forms delta itself
+    w = _wl(f"det_gqa_br_w100_d128_s777_sink{int(sink)}", BF16, 2, 8, 2, 128, 777, 900, bottom_right=True,
+            window_left=100, sink=sink)
     say(f"case {w.name} det={det}: 3 runs + 1 unordered run")
     inp, outs, _ = run_gpu(w, seed=19, deterministic=det, runs=3)
     for o in outs:
         assert o["expiries"] == 0
-    for key in ("dq", "dk", "dv", "dsink"):
+    keys = ("dq", "dk", "dv", "dsink") if sink else ("dq", "dk", "dv")
+    for key in keys:
         assert torch.equal(outs[0][key], outs[1][key]) and torch.equal(outs[0][key], outs[2][key]), key
     _, un, _ = run_gpu(w, seed=19, deterministic=0)
-    for key in ("dq", "dk", "dv", "dsink"):
+    for key in keys:
         assert_close(f"{key} det/un", outs[0][key].float().cpu(), un[key].double().cpu())
     compare_full(w, inp, outs[0], check_fwd=False)
 
