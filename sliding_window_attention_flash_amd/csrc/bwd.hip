@@ -16,6 +16,8 @@
 // (Summary, review comments) for the dot / main / reduce split, GQA,
 // per-sequence lengths and dSink.  The kernel design itself is written for
 // CDNA4 and is not taken from those pages.
+#include <type_traits>
+
 #include "kernels.h"
 #include "tiles.h"
 
@@ -700,58 +702,68 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
     const int u0 = ci * kTile + 16 * w + g.diag - tlo - kv0;      // t - tlo at (row 16 w, key kv0)
     const int tq = u0 + c - 4 * gq;                               // t - tlo at (row, key kv0 + 4 gq), minus 16 nb + r
 
-    f32x4 St[4], dPt[4];
-    bool live[4];
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int um = u0 - 16 * nb;  // the block spans t - tlo in [um - 15, um + 15]
-      live[nb] = um + 15 >= 0 && um - 15 <= (int)trange && 16 * nb < kvn;
-      if (!live[nb]) {
-        St[nb] = dPt[nb] = zero4;
-        continue;
-      }
-      // the first product starts from a literal zero accumulator
-      St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[0]]), qB[0], zero4);
-      dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[0]]), oB[0], zero4);
-#pragma unroll
-      for (int st = 1; st < NS; ++st) {
-        St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[st]]), qB[st], St[nb]);
-        dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[st]]), oB[st], dPt[nb]);
-      }
-    }
-    // dS^T of key 16 nb + 4 gq + r; blocks 2 ks and 2 ks + 1 form the
-    // 32-key B operand of step ks.  Where the wave's 16 rows see all 64 keys
-    // (t - tlo in [u0 - 63, u0 + 15] inside [0, trange], every key in the
-    // sequence) the mask drops out.
+    // The pair's products.  Where the wave's 16 rows see all 64 keys (t - tlo
+    // in [u0 - 63, u0 + 15] inside [0, trange], every key in the sequence)
+    // the mask and the per-block liveness tests drop out: FULL is the
+    // straight-line body for that case (nearly every pair of a long window),
+    // the other one skips the 16-key blocks the rows cannot see and masks.
     const bool full = u0 >= 63 && u0 + 15 <= (int)trange && kvn >= kTile;
-    V8 bS[2];
+    auto pair_body = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      f32x4 St[4], dPt[4];
+      bool live[4];
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      float dsv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (full) {
+      for (int nb = 0; nb < 4; ++nb) {
+        const int um = u0 - 16 * nb;  // the block spans t - tlo in [um - 15, um + 15]
+        live[nb] = FULL || (um + 15 >= 0 && um - 15 <= (int)trange && 16 * nb < kvn);
+        if (!live[nb]) {
+          St[nb] = dPt[nb] = zero4;
+          continue;
+        }
+        // the first product starts from a literal zero accumulator
+        St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[0]]), qB[0], zero4);
+        dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[0]]), oB[0], zero4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dsv[r] = fast_exp2(St[nb][r] * p.scale_log2 - lse2) * (dPt[nb][r] - del);
-      } else if (live[nb]) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = St[nb][r] * p.scale_log2 - lse2;
-          asm("" : "+v"(x));
-          const bool vis = (unsigned)(tq - 16 * nb - r) <= trange && 16 * nb + 4 * gq + r < kvn;
-          dsv[r] = fast_exp2(vis ? x : -INFINITY) * (dPt[nb][r] - del);
+        for (int st = 1; st < NS; ++st) {
+          St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[st]]), qB[st], St[nb]);
+          dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[st]]), oB[st], dPt[nb]);
         }
       }
+      // dS^T of key 16 nb + 4 gq + r; blocks 2 ks and 2 ks + 1 form the
+      // 32-key B operand of step ks
+      V8 bS[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bS[nb >> 1][(nb & 1) * 4 + r] = Elem<T>::from_float(dsv[r]);
-    }
+      for (int nb = 0; nb < 4; ++nb) {
+        float dsv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (FULL) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (!live[2 * ks] && !live[2 * ks + 1]) continue;
+          for (int r = 0; r < 4; ++r) dsv[r] = fast_exp2(St[nb][r] * p.scale_log2 - lse2) * (dPt[nb][r] - del);
+        } else if (live[nb]) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dQt[db] = mfma16(trpair(&cK[32 * ks * D + tr_off[db]], &cK[(32 * ks + 16) * D + tr_off[db]]), bS[ks],
-                         dQt[db]);
-    }
+          for (int r = 0; r < 4; ++r) {
+            float x = St[nb][r] * p.scale_log2 - lse2;
+            asm("" : "+v"(x));
+            const bool vis = (unsigned)(tq - 16 * nb - r) <= trange && 16 * nb + 4 * gq + r < kvn;
+            dsv[r] = fast_exp2(vis ? x : -INFINITY) * (dPt[nb][r] - del);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bS[nb >> 1][(nb & 1) * 4 + r] = Elem<T>::from_float(dsv[r]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (!live[2 * ks] && !live[2 * ks + 1]) continue;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dQt[db] = mfma16(trpair(&cK[32 * ks * D + tr_off[db]], &cK[(32 * ks + 16) * D + tr_off[db]]), bS[ks],
+                           dQt[db]);
+      }
+    };
+    if (full)
+      pair_body(std::true_type());
+    else
+      pair_body(std::false_type());
     if (ni != ci) {  // q-tile ci is complete
       store_dq(ci, dQt);
 #pragma unroll
