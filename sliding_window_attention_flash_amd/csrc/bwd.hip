@@ -290,17 +290,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
   V8 rq[NPASS], rdo[NPASS];
   float rlse = 0.f, rdelta = 0.f;
   int st_i = 0;
-  auto visit_hi = [&](int v, int& h, int& i) {
-    h = hk * p.G + v / nit;
-    i = qlo + (nit - 1 - v % nit);  // descending q-tiles within a head
+  // Visits go head by head through the group, q-tiles descending within a
+  // head: visit v is (head hk G + v / nit, q-tile qlo + nit - 1 - v % nit),
+  // walked here with two counters instead of a division per visit.
+  auto next_visit = [&](int& vh, int& vi) {
+    if (vi > qlo) {
+      --vi;
+    } else {
+      ++vh;
+      vi = qlo + nit - 1;
+    }
   };
   // this thread's 16-byte chunk of row 0, head 0; a row r of head h is
   // r * (row stride) + h * (head stride) further in either layout
   const T* q00 = qp + elem_off(p, p.sq, b, s.row0_q, 0, 0) + 8 * (tid % CH);
   const T* o00 = dop + elem_off(p, p.sdo, b, s.row0_q, 0, 0) + 8 * (tid % CH);
-  auto stage_load = [&](int v) {  // a visited q-tile: the sequence has rows
-    int h, i;
-    visit_hi(v, h, i);
+  auto stage_load = [&](int h, int i) {  // a visited q-tile: the sequence has rows
     st_i = i;
     const int row0 = i * kTile;
     const T* qh = q00 + h * p.sq[1];
@@ -343,8 +348,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
   for (int mb = 0; mb < 4; ++mb) ds_w[mb] = toff<kTile>(16 * w + c, 2 * mb + (gq >> 1)) + 4 * (gq & 1);
   const int ds_tr = troff<kTile>(c, gq, w);  // dS^T columns (q) 16 w ..
 
+  int h = hk * p.G, i = qlo + nit - 1;  // the current visit
   if (nvisit > 0) {
-    stage_load(0);
+    stage_load(h, i);
     stage_store();
   }
   __syncthreads();
@@ -355,82 +361,104 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
 
   T* dqp = static_cast<T*>(a.dq);
-  for (int v = 0; v < nvisit; ++v) {
-    int h, i;
-    visit_hi(v, h, i);
-    if (v + 1 < nvisit) stage_load(v + 1);
+  int nh = h, ni = i;  // the next visit
+  for (int v = 0; v < nvisit; ++v, h = nh, i = ni) {
+    nh = h;
+    ni = i;
+    next_visit(nh, ni);
+    if (v + 1 < nvisit) stage_load(nh, ni);
     const int q0 = i * kTile;
     // t - tlo of (row q0, key kv0 + 16 w); block mb spans [u_mb - 15, u_mb + 15]
     const int u0 = q0 + g.diag - (kv0 + 16 * w) - tlo;
 
-    f32x4 S[4], dP[4];
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int um = u0 + 16 * mb;
-      if (um + 15 < 0 || um - 15 > (int)trange) {
-        S[mb] = dP[mb] = zero4;
-        continue;
-      }
-      // the first product starts from a literal zero accumulator
-      S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[0]]), kB[0], zero4);
-      dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[0]]), vB[0], zero4);
-#pragma unroll
-      for (int st = 1; st < NS; ++st) {
-        S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[st]]), kB[st], S[mb]);
-        dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[st]]), vB[st], dP[mb]);
-      }
-    }
     // Where the wave's 16 keys see all 64 rows (t - tlo in [u0 - 15,
-    // u0 + 63] inside [0, trange], every key in the sequence) the mask drops
-    // out; rows past the sequence still get P = 0 from LSE = +inf.
+    // u0 + 63] inside [0, trange], every key in the sequence) the mask and
+    // the per-block tests drop out (FULL: straight-line products, one
+    // 16-row block at a time to bound register use); rows past the sequence
+    // still get P = 0 from LSE = +inf.
+    // Otherwise the wave skips its 16-row blocks and 32-row halves that see
+    // no key, and masks.
     const bool full = u0 >= 15 && u0 + 63 <= (int)trange && kv0 + 16 * w + 15 < s.len_kv;
-    V8 pP[2], pS[2];
+    auto visit_body = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      f32x4 S[4], dP[4];
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int um = u0 + 16 * mb;
-      const bool any = um + 15 >= 0 && um - 15 <= (int)trange;
-      float pv[4] = {0.f, 0.f, 0.f, 0.f}, dsv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (full) {
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&sLse[16 * mb + 4 * gq]);
-        const f32x4 del4 = *reinterpret_cast<const f32x4*>(&sDelta[16 * mb + 4 * gq]);
+      for (int mb = 0; mb < 4; ++mb) {
+        const int um = u0 + 16 * mb;
+        if (!FULL && (um + 15 < 0 || um - 15 > (int)trange)) {
+          S[mb] = dP[mb] = zero4;
+          continue;
+        }
+        // the first product starts from a literal zero accumulator
+        S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[0]]), kB[0], zero4);
+        dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[0]]), vB[0], zero4);
+#pragma unroll
+        for (int st = 1; st < NS; ++st) {
+          S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[st]]), kB[st], S[mb]);
+          dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[st]]), vB[st], dP[mb]);
+        }
+        if (FULL) __builtin_amdgcn_sched_barrier(0);
+      }
+      V8 pP[2], pS[2];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int um = u0 + 16 * mb;
+        const bool any = FULL || (um + 15 >= 0 && um - 15 <= (int)trange);
+        float pv[4] = {0.f, 0.f, 0.f, 0.f}, dsv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (FULL) {
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&sLse[16 * mb + 4 * gq]);
+          const f32x4 del4 = *reinterpret_cast<const f32x4*>(&sDelta[16 * mb + 4 * gq]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pv[r] = fast_exp2(S[mb][r] * p.scale_log2 - lse4[r]);
+            dsv[r] = pv[r] * (dP[mb][r] - del4[r]);
+          }
+        } else if (any) {
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&sLse[16 * mb + 4 * gq]);
+          const f32x4 del4 = *reinterpret_cast<const f32x4*>(&sDelta[16 * mb + 4 * gq]);
+          const int tb = q0 + 16 * mb + 4 * gq + tkey;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = S[mb][r] * p.scale_log2 - lse4[r];
+            asm("" : "+v"(x));
+            pv[r] = fast_exp2((unsigned)(tb + r) <= trange ? x : -INFINITY);
+            dsv[r] = pv[r] * (dP[mb][r] - del4[r]);
+          }
+        }
+        T pk[4], sk[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pv[r] = fast_exp2(S[mb][r] * p.scale_log2 - lse4[r]);
-          dsv[r] = pv[r] * (dP[mb][r] - del4[r]);
+          pk[r] = Elem<T>::from_float(pv[r]);
+          sk[r] = Elem<T>::from_float(dsv[r]);
+          pP[mb >> 1][(mb & 1) * 4 + r] = pk[r];
+          pS[mb >> 1][(mb & 1) * 4 + r] = sk[r];
         }
-      } else if (any) {
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&sLse[16 * mb + 4 * gq]);
-        const f32x4 del4 = *reinterpret_cast<const f32x4*>(&sDelta[16 * mb + 4 * gq]);
-        const int tb = q0 + 16 * mb + 4 * gq + tkey;
+        if (RELAY) *reinterpret_cast<u32x2*>(&sdSt[ds_w[mb]]) = __builtin_bit_cast(u32x2, sk);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS over 32-row halves that see any key
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = S[mb][r] * p.scale_log2 - lse4[r];
-          asm("" : "+v"(x));
-          pv[r] = fast_exp2((unsigned)(tb + r) <= trange ? x : -INFINITY);
-          dsv[r] = pv[r] * (dP[mb][r] - del4[r]);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int um = u0 + 32 * s2;  // rows +0..31: t - tlo in [um - 15, um + 31]
+        if (!FULL && (um + 31 < 0 || um - 15 > (int)trange)) continue;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dV[db] = mfma16(trpair(&sdO[32 * s2 * D + tr_off[db]], &sdO[(32 * s2 + 16) * D + tr_off[db]]), pP[s2],
+                          dV[db]);
+          dK[db] = mfma16(trpair(&sQ[32 * s2 * D + tr_off[db]], &sQ[(32 * s2 + 16) * D + tr_off[db]]), pS[s2],
+                          dK[db]);
         }
       }
-      T pk[4], sk[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pk[r] = Elem<T>::from_float(pv[r]);
-        sk[r] = Elem<T>::from_float(dsv[r]);
-        pP[mb >> 1][(mb & 1) * 4 + r] = pk[r];
-        pS[mb >> 1][(mb & 1) * 4 + r] = sk[r];
-      }
-      if (RELAY) *reinterpret_cast<u32x2*>(&sdSt[ds_w[mb]]) = __builtin_bit_cast(u32x2, sk);
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS over 32-row halves that see any key
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int um = u0 + 32 * s2;  // rows +0..31: t - tlo in [um - 15, um + 31]
-      if (um + 31 < 0 || um - 15 > (int)trange) continue;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dV[db] = mfma16(trpair(&sdO[32 * s2 * D + tr_off[db]], &sdO[(32 * s2 + 16) * D + tr_off[db]]), pP[s2], dV[db]);
-        dK[db] = mfma16(trpair(&sQ[32 * s2 * D + tr_off[db]], &sQ[(32 * s2 + 16) * D + tr_off[db]]), pS[s2], dK[db]);
-      }
+    };
+    // (the straight-line body is kept to head_dim 64 without the relay: in
+    // the others it would cost occupancy or spill)
+    if constexpr (D == 64 && !RELAY) {
+      if (full)
+        visit_body(std::true_type());
+      else
+        visit_body(std::false_type());
+    } else {
+      visit_body(std::false_type());
     }
     __syncthreads();  // dS^T complete; the Q / dO tile is free
     if (v + 1 < nvisit) stage_store();
