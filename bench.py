@@ -94,12 +94,12 @@ def workloads():
     c3 = CONFIGS["c3"]
     return {
         "c3": c3,
-        "c3_atomic": c3.with_(name=c3.name.replace("_det", "_atomic"), deterministic=False),
+        "c3_atomic": c3.with_(name=c3.name.replace("_det", "_atomic"), deterministic=False, engine=1),
         "c1": CONFIGS["c1"],
         "c2_4k": CONFIGS["c2_4k"],
         "c2_8k": CONFIGS["c2_8k"],
-        "c2_4k_det": CONFIGS["c2_4k"].with_(name=CONFIGS["c2_4k"].name + "_det", deterministic=True),
-        "c2_8k_det": CONFIGS["c2_8k"].with_(name=CONFIGS["c2_8k"].name + "_det", deterministic=True),
+        "c2_4k_det": CONFIGS["c2_4k"].with_(name=CONFIGS["c2_4k"].name + "_det", deterministic=True, engine=0),
+        "c2_8k_det": CONFIGS["c2_8k"].with_(name=CONFIGS["c2_8k"].name + "_det", deterministic=True, engine=0),
         "c4": CONFIGS["c4"],
         "c4_f16": CONFIGS["c4_f16"],
         "c5": CONFIGS["c5"],
@@ -152,7 +152,7 @@ def _prepare(w, seed):
     fw = api.Forward(inp["q"], inp["k"], inp["v"], sink=inp["sink"], **mk)
     o, lse = fw.run()
     bw = api.Backward(inp["q"], inp["k"], inp["v"], o, inp["dO"], lse, deterministic=w.deterministic,
-                      sink=inp["sink"], **mk)
+                      engine=w.engine, sink=inp["sink"], **mk)
     return inp, fw, o, lse, bw
 
 
@@ -607,7 +607,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "head_dim": w.head_dim, "seq_len": w.seq_q, "window_left": w.window_left,
                    "mask": "causal_bottom_right" if w.bottom_right else "causal_top_left",
-                   "dq_mode": "relay" if w.deterministic else "atomic"},
+                   "dq_mode": {1: "fp32 atomics"}.get(w.engine, "ordered relay" if w.deterministic else "plan's choice")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(w)},
         "extra": extra,

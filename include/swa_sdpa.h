@@ -104,6 +104,20 @@ typedef struct sdpa_attn_desc {
                            q-tiles one block of the q-major passes (forward,
                            unordered dQ of the per-tile path) walks; for
                            tuning studies                                     */
+  int32_t engine;       /* backward kernels and dQ mechanism.  0: chosen by
+                           the plan from a measured table, among those the
+                           deterministic option allows.  For tuning studies,
+                           1..4 force one: 1 streaming kernel with fp32
+                           atomics at chunk boundaries, 2 streaming kernel
+                           with the chunk relay, 3 per-tile kernels with the
+                           q-major dQ pass, 4 per-tile kernel with the
+                           per-kv-tile relay.  1 and 2 need heads_q ==
+                           heads_kv, causal, window_right 0, window_left
+                           0..128, head_dim 64 (SDPA_ERR_UNSUPPORTED
+                           otherwise); 1 needs deterministic 0, and
+                           deterministic 2 admits only 4
+                           (SDPA_ERR_INVALID_ARG otherwise).  The forward
+                           ignores it.                                        */
   /* Element strides (batch, head, row) of each tensor; the head_dim axis is
    * contiguous.  THD ignores the batch entry (rows are tokens).  Rows and
    * base pointers must be 16-byte aligned; row strides below 2^32 elements

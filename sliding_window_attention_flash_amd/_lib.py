@@ -27,7 +27,7 @@ class AttnDesc(ctypes.Structure):
         ("heads_kv", _i32), ("head_dim", _i32), ("seq_q", _i32), ("seq_kv", _i32),
         ("total_q", _i64), ("total_kv", _i64), ("causal", _i32), ("bottom_right", _i32),
         ("window_left", _i32), ("window_right", _i32), ("scale", _f32), ("deterministic", _i32), ("has_sink", _i32),
-        ("has_seq_lens", _i32), ("q_run_tiles", _i32),
+        ("has_seq_lens", _i32), ("q_run_tiles", _i32), ("engine", _i32),
         ("stride_q", _i64 * 3), ("stride_k", _i64 * 3), ("stride_v", _i64 * 3),
         ("stride_o", _i64 * 3), ("stride_do", _i64 * 3), ("stride_dq", _i64 * 3),
         ("stride_dk", _i64 * 3), ("stride_dv", _i64 * 3),

@@ -179,8 +179,8 @@ def geometry(q, k, cu_seqlens_q=None, max_seqlen_q=None, max_seqlen_kv=None) -> 
 
 
 def make_desc(g: Geometry, dtype, *, causal=True, bottom_right=False, window_left=-1,
-              window_right=0, q_run_tiles=0, scale=None, deterministic=False, has_sink=False, has_seq_lens=False,
-              q=None, k=None, v=None, o=None, dO=None, dq=None, dk=None, dv=None) -> AttnDesc:
+              window_right=0, q_run_tiles=0, engine=0, scale=None, deterministic=False, has_sink=False,
+              has_seq_lens=False, q=None, k=None, v=None, o=None, dO=None, dq=None, dk=None, dv=None) -> AttnDesc:
     if dtype not in _DT:
         raise ValueError(f"dtype {dtype} not supported (bf16 / f16)")
     packed = g.layout == _lib.SDPA_LAYOUT_THD
@@ -189,7 +189,7 @@ def make_desc(g: Geometry, dtype, *, causal=True, bottom_right=False, window_lef
     d.heads_q, d.heads_kv, d.head_dim = g.heads_q, g.heads_kv, g.head_dim
     d.seq_q, d.seq_kv, d.total_q, d.total_kv = g.seq_q, g.seq_kv, g.total_q, g.total_kv
     d.causal, d.bottom_right, d.window_left = int(causal), int(bottom_right), int(window_left)
-    d.window_right, d.q_run_tiles = int(window_right), int(q_run_tiles)
+    d.window_right, d.q_run_tiles, d.engine = int(window_right), int(q_run_tiles), int(engine)
     d.scale = float(scale) if scale is not None else g.head_dim ** -0.5
     d.deterministic, d.has_sink, d.has_seq_lens = int(deterministic), int(has_sink), int(has_seq_lens)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dO), ("dq", dq), ("dk", dk), ("dv", dv)):
@@ -240,8 +240,8 @@ class Backward:
     the tests to rerun the same launch)."""
 
     def __init__(self, q, k, v, o, dO, lse, *, causal=True, bottom_right=False, window_left=-1,
-                 window_right=0, q_run_tiles=0, scale=None, deterministic=False, sink=None, cu_seqlens_q=None,
-                 cu_seqlens_kv=None, seq_lens_q=None, seq_lens_kv=None, max_seqlen_q=None,
+                 window_right=0, q_run_tiles=0, engine=0, scale=None, deterministic=False, sink=None,
+                 cu_seqlens_q=None, cu_seqlens_kv=None, seq_lens_q=None, seq_lens_kv=None, max_seqlen_q=None,
                  max_seqlen_kv=None, dq=None, dk=None, dv=None, dsink=None, workspace=None):
         g = geometry(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_kv)
         self.dq = torch.empty_like(q) if dq is None else dq
@@ -252,7 +252,7 @@ class Backward:
             self.dsink = torch.empty(g.heads_q, dtype=torch.float32, device=q.device) if dsink is None else dsink
         desc = make_desc(g, q.dtype, causal=causal, bottom_right=bottom_right,
                          window_left=window_left, window_right=window_right,
-                         q_run_tiles=q_run_tiles, scale=scale, deterministic=deterministic,
+                         q_run_tiles=q_run_tiles, engine=engine, scale=scale, deterministic=deterministic,
                          has_sink=sink is not None, has_seq_lens=seq_lens_q is not None,
                          q=q, k=k, v=v, o=o, dO=dO, dq=self.dq, dk=self.dk, dv=self.dv)
         self.plan = sdpa_bwd_plan(desc)

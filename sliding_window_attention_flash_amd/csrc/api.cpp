@@ -121,7 +121,58 @@ sdpa_status check_desc(const sdpa_attn_desc* d, bool backward) {
   return SDPA_OK;
 }
 
-swa::Problem make_problem(const sdpa_attn_desc* d) {
+// The streaming kernel covers multi-head attention with a causal mask and a
+// left window of at most 128 keys at head_dim 64 (its ring of q-tile slots
+// is sized for that), without a right band.  It addresses rows with 32-bit
+// row strides, and one (batch, head)'s fp32 dQ partial rows with 32-bit
+// byte offsets.
+bool stream_eligible(const sdpa_attn_desc* d) {
+  bool small_rows = (int64_t)d->seq_q * d->head_dim * (int64_t)sizeof(float) <= INT32_MAX;
+  for (const int64_t rs : {d->stride_q[2], d->stride_k[2], d->stride_v[2], d->stride_do[2], d->stride_dq[2],
+                           d->stride_dk[2], d->stride_dv[2]})
+    small_rows &= rs > 0 && rs <= INT32_MAX;
+  return d->heads_q == d->heads_kv && d->causal && d->window_right == 0 && d->window_left >= 0 &&
+         d->window_left <= 128 && d->head_dim == 64 && small_rows;
+}
+
+enum { ENGINE_STREAM_ATOMIC = 1, ENGINE_STREAM_RELAY = 2, ENGINE_TILE_QMAJOR = 3, ENGINE_TILE_RELAY = 4 };
+
+// The backward's kernels and dQ mechanism: a forced engine (validated
+// against the shape and the deterministic promise) or the plan's default.
+sdpa_status resolve_engine(const sdpa_attn_desc* d, int* engine) {
+  const bool stream_ok = stream_eligible(d);
+  if (d->engine < 0 || d->engine > 4) return fail(SDPA_ERR_INVALID_ARG, "engine %d is not 0..4", d->engine);
+  if (d->engine) {
+    if ((d->engine == ENGINE_STREAM_ATOMIC || d->engine == ENGINE_STREAM_RELAY) && !stream_ok)
+      return fail(SDPA_ERR_UNSUPPORTED,
+                  "engine %d (streaming kernel) needs heads_q == heads_kv, causal, window_right 0, window_left "
+                  "0..128, head_dim 64 and row strides below 2^31", d->engine);
+    if (d->engine == ENGINE_STREAM_ATOMIC && d->deterministic)
+      return fail(SDPA_ERR_INVALID_ARG, "engine 1 (fp32 atomics) is not repeatable: it needs deterministic 0");
+    if (d->deterministic == 2 && d->engine != ENGINE_TILE_RELAY)
+      return fail(SDPA_ERR_INVALID_ARG, "deterministic 2 asks for the per-kv-tile relay: engine must be 0 or 4");
+    *engine = d->engine;
+    return SDPA_OK;
+  }
+  // The measured table (MI355X, head_dim 64, causal, windows 64 / 128, both
+  // anchors; batch x heads 2 .. 128, 1K .. 16K rows; the engine study of
+  // this package): the streaming kernel, one block per CU, leaves the chip
+  // idle below about 2^16 query rows (B Hq S_q) and there loses to the
+  // per-tile kernels by 24-50%; above, it wins by 15-30%.  Its chunk relay
+  // ties or beats its fp32 atomics everywhere (within 1.5% at the largest
+  // shape) and is repeatable, so it serves both deterministic 0 and 1.
+  const int64_t q_rows =
+      (d->layout == SDPA_LAYOUT_THD ? d->total_q : (int64_t)d->batch * d->seq_q) * (int64_t)d->heads_q;
+  if (d->deterministic == 2)
+    *engine = ENGINE_TILE_RELAY;
+  else if (stream_ok && q_rows >= (int64_t(1) << 16))
+    *engine = ENGINE_STREAM_RELAY;
+  else
+    *engine = ENGINE_TILE_QMAJOR;
+  return SDPA_OK;
+}
+
+swa::Problem make_problem(const sdpa_attn_desc* d, int engine) {
   swa::Problem p{};
   p.B = d->batch;
   p.Hq = d->heads_q;
@@ -154,24 +205,15 @@ swa::Problem make_problem(const sdpa_attn_desc* d) {
   }
   p.n_q_tiles = (d->seq_q + kTile - 1) / kTile;
   p.n_kv_tiles = (d->seq_kv + kTile - 1) / kTile;
-  // The streaming kernel covers multi-head attention with a causal mask and
-  // a left window of at most 128 keys at head_dim 64 (its ring of q-tile
-  // slots is sized for that); everything else runs the per-tile kernel.
-  // It addresses rows with 32-bit row strides, and one (batch, head)'s fp32
-  // dQ partial rows with 32-bit byte offsets.
-  bool small_rows = (int64_t)d->seq_q * d->head_dim * (int64_t)sizeof(float) <= INT32_MAX;
-  for (const int64_t rs : {p.sq[2], p.sk[2], p.sv[2], p.sdo[2], p.sdq[2], p.sdk[2], p.sdv[2]})
-    small_rows &= rs > 0 && rs <= INT32_MAX;
-  // deterministic = 2 asks for the per-kv-tile relay, which only the
-  // per-tile kernel has.
-  p.stream = p.G == 1 && d->causal && p.right == 0 && d->window_left >= 0 && d->window_left <= 128 &&
-             d->head_dim == 64 && small_rows && d->deterministic != 2;
+  // Engines: the streaming kernel (boundary q-tiles of its chunks through
+  // fp32 atomics or the chunk relay), or the per-tile kernel with dQ from
+  // the q-major pass (no fp32 accumulator: each dQ row is summed inside one
+  // block in a fixed order, so this is bitwise repeatable) or from the
+  // per-kv-tile relay of the pages.
+  p.stream = engine == ENGINE_STREAM_ATOMIC || engine == ENGINE_STREAM_RELAY;
+  p.stream_relay = engine == ENGINE_STREAM_RELAY;
   p.step_kv = p.stream ? 128 : kTile;
-  // The per-tile kernel leaves dQ to a q-major pass (no fp32 accumulator).
-  // Each dQ row is summed inside one block in a fixed order and each dK / dV
-  // row likewise, so this path is bitwise repeatable and serves both the
-  // unordered and the repeatable mode; deterministic = 2 runs the relay.
-  p.split_dq = !p.stream && d->deterministic != 2;
+  p.split_dq = engine == ENGINE_TILE_QMAJOR;
   // Consecutive q-tiles one block of the q-major passes walks.  A run
   // pays the block's start-up latency once, but needs registers for the
   // next q-tile's rows; a measured study over head_dim and band width on
@@ -254,10 +296,12 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   *plan = nullptr;
   sdpa_status st = check_desc(desc, true);
   if (st) return st;
+  int engine = 0;
+  if ((st = resolve_engine(desc, &engine))) return st;
   auto* pl = new (std::nothrow) struct sdpa_bwd_plan();
   if (!pl) return fail(SDPA_ERR_INVALID_ARG, "out of host memory");
   pl->desc = *desc;
-  pl->prob = make_problem(desc);
+  pl->prob = make_problem(desc, engine);
   const swa::Problem& p = pl->prob;
   pl->stat_rows = (int64_t)p.Hq * p.total_q;
   size_t off = 0;
@@ -269,7 +313,7 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
     // the streaming kernel's unordered mode keeps each q-tile's partial sum
     // in a 64-row slot of its own (stream_slot: dense B x Hq x n_q_tiles
     // slots, packed Hq x (total_q / 64 + B + 1))
-    if (p.stream && !desc->deterministic) {
+    if (p.stream && !p.stream_relay) {
       const size_t slots = p.layout == swa::LAYOUT_THD
                                ? (size_t)p.Hq * (size_t)((p.total_q >> 6) + p.B + 1)
                                : (size_t)p.B * p.Hq * p.n_q_tiles;
@@ -278,7 +322,7 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
     off = align256(off + sizeof(float) * acc_floats);
   }
   pl->off_stash = off;
-  if (p.stream && desc->deterministic) off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
+  if (p.stream && p.stream_relay) off = align256(off + sizeof(float) * (size_t)pl->stat_rows * p.D);
   pl->off_sem = off;
   off = align256(off + sizeof(int) * (size_t)p.B * p.Hq * p.n_q_tiles);
   pl->off_ctl = off;
@@ -479,7 +523,7 @@ sdpa_status sdpa_fwd_plan(const sdpa_attn_desc* desc, sdpa_fwd_plan_t** plan, si
   auto* pl = new (std::nothrow) struct sdpa_fwd_plan();
   if (!pl) return fail(SDPA_ERR_INVALID_ARG, "out of host memory");
   pl->desc = *desc;
-  pl->prob = make_problem(desc);
+  pl->prob = make_problem(desc, ENGINE_TILE_QMAJOR);  // (the backward's engine does not apply)
   *plan = pl;
   *workspace_bytes = 0;
   g_err[0] = 0;

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
   const int tile0 = blockIdx.x * DOT_TILES, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const Seq s = load_seq(p, b);
   if (tile0 == 0 && h == 0 && b == 0 && tid < 2) a.ctl[tid] = 0;
-  if ((a.deterministic || p.stream) && tid < DOT_TILES && tile0 + tid < p.n_q_tiles)
+  if (!p.split_dq && tid < DOT_TILES && tile0 + tid < p.n_q_tiles)  // relay or chunk counters
     a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile0 + tid] = 0;
 
   constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
       for (int e = tid; e < rows * CH; e += kThreads)
         st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
-    } else if (!a.deterministic && nv > 1) {
+    } else if (p.stream && !p.stream_relay && nv > 1) {
       float4* acc = reinterpret_cast<float4*>(a.dq_acc + stream_slot(p, s, b, h, tile) * kTile * D);
       const float4 z = {0.f, 0.f, 0.f, 0.f};
       for (int e = tid; e < kTile * (D / 4); e += kThreads) acc[e] = z;

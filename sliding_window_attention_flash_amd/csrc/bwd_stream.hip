@@ -692,12 +692,12 @@ hipError_t launch_bwd_stream(const BwdArgs& a, hipStream_t st) {
   const int n = a.p.B * a.p.Hq * a.p.n_chunks;
   if (n == 0) return hipSuccess;
   if (a.dtype == 0) {
-    if (a.deterministic)
+    if (a.p.stream_relay)
       hipLaunchKernelGGL((bwd_stream_kernel<__bf16, true>), dim3(n), dim3(NTHR), 0, st, a);
     else
       hipLaunchKernelGGL((bwd_stream_kernel<__bf16, false>), dim3(n), dim3(NTHR), 0, st, a);
   } else {
-    if (a.deterministic)
+    if (a.p.stream_relay)
       hipLaunchKernelGGL((bwd_stream_kernel<_Float16, true>), dim3(n), dim3(NTHR), 0, st, a);
     else
       hipLaunchKernelGGL((bwd_stream_kernel<_Float16, false>), dim3(n), dim3(NTHR), 0, st, a);

@@ -47,6 +47,7 @@ struct Problem {
   int dq_delta;  // that pass forms delta and runs before bwd_main (no bwd_dot)
   int fwd_tiles; // the same for the forward
   int stream;
+  int stream_relay;  // streaming kernel: boundary q-tiles by the chunk relay (else fp32 atomics)
   int step_kv;
   int chunk;
   int n_chunks;

@@ -45,6 +45,7 @@ class Workload:
     window_right: int = 0  # causal only: inclusive right band (0: plain causal)
     scale: Optional[float] = None
     deterministic: bool = False
+    engine: int = 0  # backward kernels / dQ mechanism: 0 the plan's choice, 1..4 forced
     sink: bool = False
     layout: str = "bhsd"  # "bhsd" ([B,H,S,D]) or "thd" ([T,H,D] packed)
     # packed layout: per-sequence valid lengths and slot capacities
@@ -109,10 +110,11 @@ def _c5() -> Workload:
 CONFIGS = {
     "c1": Workload("c1_tiny_b1_h2_d64_s256_w64_bf16", torch.bfloat16, 1, 2, 2, 64, 256, 256,
                    window_left=64, scale=0.125),
+    # fp32-atomic dQ, as the pages' gpt_oss-style rows are measured
     "c2_4k": Workload("c2_b2_h16_d64_s4096_w128_bf16", torch.bfloat16, 2, 16, 16, 64, 4096, 4096,
-                      window_left=128, scale=0.125),
+                      window_left=128, scale=0.125, engine=1),
     "c2_8k": Workload("c2_b2_h16_d64_s8192_w128_bf16", torch.bfloat16, 2, 16, 16, 64, 8192, 8192,
-                      window_left=128, scale=0.125),
+                      window_left=128, scale=0.125, engine=1),
     "c3": Workload("c3_b2_h16_d64_s32768_w128_bf16_det", torch.bfloat16, 2, 16, 16, 64, 32768,
                    32768, window_left=128, scale=0.125, deterministic=True),
     "c4": Workload("c4_b12_gqa48x6_d128_s16484_br_w96_bf16", torch.bfloat16, 12, 48, 6, 128,

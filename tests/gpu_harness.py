@@ -41,15 +41,32 @@ def gpu_forward(w: Workload, inp: dict):
     return api.forward(inp["q"], inp["k"], inp["v"], sink=inp["sink"], **mask_kw(w), **seq_kw(w, inp))
 
 
-def gpu_backward(w: Workload, inp: dict, o, lse, deterministic=None, nan_fill=True):
+def stream_eligible(w: Workload) -> bool:
+    """Shapes the streaming kernel applies to (its engines 1 and 2)."""
+    return (w.heads_q == w.heads_kv and w.causal and w.window_right == 0 and 0 <= w.window_left <= 128
+            and w.head_dim == 64)
+
+
+def stream_engine(w: Workload, det: int) -> int:
+    """The engine that runs the streaming kernel in dQ mode ``det`` (fp32
+    atomics, chunk relay; the per-kv-tile relay for 2) where it applies,
+    else 0 (the plan's choice): small shapes would otherwise take the
+    per-tile kernels by the measured table."""
+    if not stream_eligible(w):
+        return 0
+    return {0: 1, 1: 2, 2: 4}[int(det)]
+
+
+def gpu_backward(w: Workload, inp: dict, o, lse, deterministic=None, nan_fill=True, engine=None):
     det = w.deterministic if deterministic is None else deterministic
+    engine = w.engine if engine is None else engine
     q, k, v = inp["q"], inp["k"], inp["v"]
     fill = float("nan") if nan_fill else 0.0
     dq, dk, dv = (torch.full_like(t, fill) for t in (q, k, v))
     dsink = None
     if inp["sink"] is not None:
         dsink = torch.full((w.heads_q,), fill, dtype=torch.float32, device=q.device)
-    bw = api.Backward(q, k, v, o, inp["dO"], lse, deterministic=det, sink=inp["sink"],
+    bw = api.Backward(q, k, v, o, inp["dO"], lse, deterministic=det, sink=inp["sink"], engine=engine,
                       dq=dq, dk=dk, dv=dv, dsink=dsink, **mask_kw(w), **seq_kw(w, inp))
     return bw
 
@@ -181,12 +198,13 @@ def batch_entries(w: Workload, inp_cpu: dict, gpu: dict, idx):
     return ws, inp, out
 
 
-def run_gpu(w: Workload, seed=0, deterministic=None, runs=1):
-    """Inputs on the GPU, forward, then the backward; returns CPU copies of
-    the inputs and the GPU outputs (a list when runs > 1)."""
+def run_gpu(w: Workload, seed=0, deterministic=None, runs=1, engine=None):
+    """Inputs on the GPU, forward, then the backward (engine: the workload's
+    unless given; 0 is the plan's choice); returns CPU copies of the inputs
+    and the GPU outputs (a list when runs > 1)."""
     inp = make_inputs(w, device="cuda", seed=seed)
     o, lse = gpu_forward(w, inp)
-    bw = gpu_backward(w, inp, o, lse, deterministic=deterministic)
+    bw = gpu_backward(w, inp, o, lse, deterministic=deterministic, engine=engine)
     outs = []
     for _ in range(runs):
         dq, dk, dv, dsink = bw.run()

@@ -23,9 +23,9 @@ pytestmark = pytest.mark.gpu
 BF16 = torch.bfloat16
 
 CASES = [
-    # streaming kernel: chunk relay (ordered) and chunk-boundary atomics
-    (Workload("conc_stream_w128_s1500", BF16, 2, 4, 4, 64, 1500, 1500, window_left=128), 1),
-    (Workload("conc_stream_w128_s1500", BF16, 2, 4, 4, 64, 1500, 1500, window_left=128), 0),
+    # streaming kernel (forced): chunk relay (ordered) and chunk-boundary atomics
+    (Workload("conc_stream_w128_s1500", BF16, 2, 4, 4, 64, 1500, 1500, window_left=128, engine=2), 1),
+    (Workload("conc_stream_w128_s1500", BF16, 2, 4, 4, 64, 1500, 1500, window_left=128, engine=1), 0),
     # per-tile path: q-major dQ pass, and the per-kv-tile relay
     (Workload("conc_gqa_br_w90_d128_sink", BF16, 2, 8, 2, 128, 300, 420, bottom_right=True, window_left=90,
               sink=True), 1),

@@ -6,7 +6,7 @@ row strides of H * D elements."""
 import pytest
 import torch
 
-from gpu_harness import assert_close, gpu_backward, gpu_forward, say
+from gpu_harness import assert_close, gpu_backward, gpu_forward, say, stream_engine
 from sliding_window_attention_flash_amd.synth import Workload
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +33,9 @@ def test_sequence_major_matches_contiguous(w, det):
     say(f"case {w.name} det={det}: sequence-major against contiguous")
     inp = make_inputs(w, device="cuda", seed=13)
     o, lse = gpu_forward(w, inp)
-    ref = [None if t is None else t.clone() for t in gpu_backward(w, inp, o, lse, deterministic=det).run()]
+    eng = stream_engine(w, det)  # the streaming kernel where it applies
+    ref = [None if t is None else t.clone()
+           for t in gpu_backward(w, inp, o, lse, deterministic=det, engine=eng).run()]
 
     sinp = dict(inp)
     for key in ("q", "k", "v", "dO"):
@@ -42,7 +44,7 @@ def test_sequence_major_matches_contiguous(w, det):
     so, slse = gpu_forward(w, sinp)
     assert so.stride() == sinp["q"].stride()
     assert torch.equal(so, o) and torch.equal(slse, lse)
-    out = gpu_backward(w, sinp, so, slse, deterministic=det).run()
+    out = gpu_backward(w, sinp, so, slse, deterministic=det, engine=eng).run()
     assert out[0].stride() == sinp["q"].stride() and out[1].stride() == sinp["k"].stride()
     for name, got, want in zip(("dq", "dk", "dv", "dsink"), out, ref):
         if want is None:

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from gpu_harness import (assert_close, batch_entries, compare_full, compare_sampled, oracle_full, run_gpu,
-                         say)
+                         say, stream_engine)
 from sliding_window_attention_flash_amd.synth import CONFIGS, Workload, packed_lengths
 
 pytestmark = pytest.mark.gpu
@@ -67,10 +67,31 @@ DET = dict(argvalues=[0, 1, 2], ids=["unordered", "ordered", "tile_relay"])
 @pytest.mark.parametrize("det", **DET)
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_small_full_oracle(w, det):
+    # shapes the streaming kernel applies to run it (these small ones would
+    # take the per-tile kernels by the plan's table, which ENGINE_CASES and
+    # the other shapes cover)
     say(f"case {w.name} det={det}")
-    inp, out, _ = run_gpu(w, seed=3, deterministic=det)
+    inp, out, _ = run_gpu(w, seed=3, deterministic=det, engine=stream_engine(w, det))
     assert out["expiries"] == 0
     compare_full(w, inp, out)
+
+
+# every engine, forced, on shapes the streaming kernel applies to (so all
+# four run): 1 streaming + atomics, 2 streaming + chunk relay, 3 per-tile +
+# q-major dQ pass, 4 per-tile + per-kv-tile relay
+ENGINE_CASES = [
+    _wl("eng_mha_tl_w128_s1500", BF16, 2, 4, 4, 64, 1500, 1500, window_left=128, scale=0.125),
+    _wl("eng_mha_br_w77_s600x1100_padded_f16", F16, 2, 3, 3, 64, 600, 1100, bottom_right=True, window_left=77,
+        pad_len_q=(600, 411), pad_len_kv=(1100, 950), sink=True),
+]
+
+
+@pytest.mark.parametrize("engine", [1, 2, 3, 4])
+@pytest.mark.parametrize("w", ENGINE_CASES, ids=[w.name for w in ENGINE_CASES])
+def test_forced_engines_full_oracle(w, engine):
+    say(f"case {w.name} engine={engine}")
+    inp, out, _ = run_gpu(w, seed=17, deterministic=0, engine=engine)
+    compare_full(w, inp, out, check_fwd=engine == 1)
 
 
 def _thd_small(sink=True, dtype=F16, D=64, hkv=2, wr=0):
@@ -89,7 +110,7 @@ def _thd_small(sink=True, dtype=F16, D=64, hkv=2, wr=0):
 def test_thd_padded_with_sinks(det, D, hkv, wr):
     w = _thd_small(D=D, hkv=hkv, wr=wr)
     say(f"case {w.name} det={det}")
-    inp, out, _ = run_gpu(w, seed=5, deterministic=det)
+    inp, out, _ = run_gpu(w, seed=5, deterministic=det, engine=stream_engine(w, det))
     compare_full(w, inp, out)
 
 
@@ -103,14 +124,14 @@ def test_c1_tiny_full_oracle():
 
 def test_relay_bitwise_repeatable_and_matches_atomic():
     w = _wl("det_b2_h4_s2048_w128", BF16, 2, 4, 4, 64, 2048, 2048, window_left=128, scale=0.125,
-            deterministic=True)
-    say(f"case {w.name}: 3 relay runs + 1 atomic run")
+            deterministic=True, engine=2)
+    say(f"case {w.name}: 3 chunk-relay runs + 1 atomic run")
     inp, outs, _ = run_gpu(w, seed=9, runs=3)
     for o in outs:
         assert o["expiries"] == 0
     for key in ("dq", "dk", "dv"):
         assert torch.equal(outs[0][key], outs[1][key]) and torch.equal(outs[0][key], outs[2][key]), key
-    _, at, _ = run_gpu(w, seed=9, deterministic=False)
+    _, at, _ = run_gpu(w, seed=9, deterministic=False, engine=1)
     for key in ("dq", "dk", "dv"):
         assert_close(f"{key} det/at", outs[0][key].cpu(), at[key].cpu().double())
     compare_full(w, inp, outs[0], check_fwd=False)
@@ -200,7 +221,7 @@ def test_c3_s32768_relay_bitwise_and_full_oracle_both_modes():
     say("  relay run vs oracle")
     compare_full(w, inp, outs[0], ref=ref)
     compare_sampled(w, inp, outs[0])
-    _, at, _ = run_gpu(w, seed=23, deterministic=False)
+    _, at, _ = run_gpu(w, seed=23, deterministic=False, engine=1)
     say("  atomic run vs oracle")
     compare_full(w, inp, at, ref=ref)
     for key in ("dq", "dk", "dv"):
@@ -217,6 +238,23 @@ def test_c4_gqa_s16484_whole_batch_entries_full_oracle():
     for name in ("dq", "dk", "dv"):
         assert not torch.isnan(out[name]).any(), f"{name}: NaN somewhere in the full output"
     compare_sampled(w, inp, out, n_q=192, n_kv=96)
+
+
+def test_nonsquare_class_whole_batch_entries_full_oracle():
+    # the pages' non-square class: b12, 40/8 heads, d64, q128 / kv8960,
+    # bottom-right, W8000 (every row sees 8001 keys)
+    w = CONFIGS["nonsquare"]
+    say(f"case {w.name}: batch entries 0 and 11 against the full oracle, in all three dQ modes")
+    ref = None
+    for det in (0, 1, 2):
+        inp, out, _ = run_gpu(w, seed=27, deterministic=det)
+        ws, inp2, out2 = batch_entries(w, inp, out, [0, w.batch - 1])
+        if ref is None:
+            ref = oracle_full(ws, inp2)
+        say(f"  det={det}")
+        compare_full(ws, inp2, out2, check_fwd=det == 0, ref=ref)
+        for name in ("dq", "dk", "dv"):
+            assert not torch.isnan(out[name]).any(), f"{name}: NaN somewhere in the full output"
 
 
 def test_c4_f16_variant_full_oracle():

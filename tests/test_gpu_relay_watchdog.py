@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # streaming kernel, chunk relay (boundary q-tiles have two visiting chunks)
     (Workload("wd_stream_b2_h4_s4096_w128", torch.bfloat16, 2, 4, 4, 64, 4096, 4096, window_left=128,
-              scale=0.125), 1),
+              scale=0.125, engine=2), 1),
     # per-tile kernel, the per-kv-tile relay
     (Workload("wd_tile_gqa_br_w100_d128", torch.bfloat16, 2, 8, 2, 128, 500, 700, bottom_right=True,
               window_left=100), 2),

@@ -132,7 +132,8 @@ def test_streaming_workspace_size(lib, det):
     # Unordered: one 64-row fp32 slot per (batch, head, q-tile) for the
     # boundary partials; ordered: the partial rows plus the relay stash.
     B, H, S, D = 2, 4, 300, 64
-    plan = api.sdpa_bwd_plan(_desc(B=B, Hq=H, Hkv=H, D=D, Sq=S, Skv=S, window_left=128, deterministic=det))
+    plan = api.sdpa_bwd_plan(_desc(B=B, Hq=H, Hkv=H, D=D, Sq=S, Skv=S, window_left=128, deterministic=det,
+                                   engine=1 if det == 0 else 2))
     rows, ntq = B * H * S, 5
     acc = 4 * B * H * ntq * 64 * D if det == 0 else 4 * rows * D
     stash = 4 * rows * D if det == 1 else 0
@@ -148,7 +149,7 @@ def test_streaming_workspace_packed_scales_with_rows_not_batch_times_longest(lib
     g = api.Geometry(_lib.SDPA_LAYOUT_THD, B, H, H, D, S, S, T, T)
     q = torch.empty(T, H, D, dtype=torch.bfloat16)
     d = api.make_desc(g, torch.bfloat16, q=q, k=q, v=q, o=q, dO=q, dq=q, dk=q, dv=q, window_left=128,
-                      has_seq_lens=True)
+                      has_seq_lens=True, engine=1)
     plan = api.sdpa_bwd_plan(d)
     rows, ntq = H * T, S // 64
     slots = H * ((T >> 6) + B + 1)
@@ -181,9 +182,11 @@ def _schedule_cases():
 @pytest.mark.parametrize("mha", [False, True], ids=["gqa_tiles", "mha"])
 @pytest.mark.parametrize("lq,lk,w,br,causal,wr", _schedule_cases())
 def test_schedule_covers_the_mask_exactly(lib, lq, lk, w, br, causal, wr, mha):
-    # multi-head causal plans with a window <= 128 (and no right band)
-    # schedule 128-key kv-steps
-    d = _desc(window_left=w, window_right=wr, bottom_right=br, Hkv=4 if mha else 2)
+    # multi-head causal plans with a window <= 128 (and no right band) run
+    # the streaming kernel's 128-key kv-steps (forced: this small shape
+    # would take the per-tile kernels by the plan's table)
+    stream = mha and causal and wr == 0 and 0 <= w <= 128
+    d = _desc(window_left=w, window_right=wr, bottom_right=br, Hkv=4 if mha else 2, engine=2 if stream else 0)
     d.causal = int(causal)
     plan = api.sdpa_bwd_plan(d)
     s = api.sdpa_bwd_schedule(plan, lq, lk)
@@ -280,7 +283,9 @@ def simulate_relay(s, kv_first=None, timeout_s=2.0):
                                            (500, 500, 0, False, 0), (500, 500, 40, False, 90),
                                            (300, 700, 100, True, 33)])
 def test_relay_simulation_orders_every_q_tile(lib, lq, lk, w, br, wr, mha):
-    plan = api.sdpa_bwd_plan(_desc(window_left=w, window_right=wr, bottom_right=br, Hkv=4 if mha else 2))
+    stream = mha and wr == 0 and 0 <= w <= 128
+    plan = api.sdpa_bwd_plan(_desc(window_left=w, window_right=wr, bottom_right=br, Hkv=4 if mha else 2,
+                                   engine=2 if stream else 0))
     s = api.sdpa_bwd_schedule(plan, lq, lk)
     log, expired, sums = simulate_relay(s)
     assert not expired
@@ -350,3 +355,48 @@ def test_noalloc_rejects_a_workspace_beyond_its_scratch(lib):
     msg = lib.sdpa_last_error()
     assert b"scratch" in msg and str(plan.workspace_bytes).encode() in msg
     assert lib.sdpa_bwd_run_noalloc(None, ctypes.byref(t), None) == _lib.SDPA_ERR_INVALID_ARG
+
+
+# ---- engine choice -----------------------------------------------------------------
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(engine=5), _lib.SDPA_ERR_INVALID_ARG, "engine 5"),
+    (dict(engine=1, Hkv=2), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
+    (dict(engine=2, Hkv=4, window_left=200), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
+    (dict(engine=2, Hkv=4, D=128), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
+    (dict(engine=1, Hkv=4, deterministic=1), _lib.SDPA_ERR_INVALID_ARG, "not repeatable"),
+    (dict(engine=3, Hkv=4, deterministic=2), _lib.SDPA_ERR_INVALID_ARG, "per-kv-tile relay"),
+])
+def test_plan_rejects_engines_that_do_not_apply(lib, kw, status, needle):
+    with pytest.raises(_lib.SdpaError) as e:
+        api.sdpa_bwd_plan(_desc(**kw))
+    assert e.value.status == status and needle in str(e.value)
+
+
+@pytest.mark.parametrize("engine,det,tile_kv", [(1, 0, 128), (2, 0, 128), (2, 1, 128), (3, 0, 64), (3, 1, 64),
+                                                (4, 0, 64), (4, 2, 64)])
+def test_forced_engine_sets_the_schedule_and_workspace(lib, engine, det, tile_kv):
+    # multi-head, causal, window 128, head_dim 64: every engine applies
+    B, H, S, D = 2, 4, 300, 64
+    plan = api.sdpa_bwd_plan(_desc(B=B, Hq=H, Hkv=H, D=D, Sq=S, Skv=S, window_left=128, engine=engine,
+                                   deterministic=det))
+    s = api.sdpa_bwd_schedule(plan, S, S)
+    assert s["tile_kv"] == tile_kv
+    rows, ntq = B * H * S, 5
+    acc = {1: 4 * B * H * ntq * 64 * D, 2: 4 * rows * D, 3: 0, 4: 4 * rows * D}[engine]
+    stash = 4 * rows * D if engine == 2 else 0
+    assert plan.workspace_bytes == _sections(4 * rows, acc, stash, 4 * B * H * ntq, 16, 4 * H * B * ntq)
+
+
+@pytest.mark.parametrize("B,H,S,det,stream", [
+    (2, 16, 32768, 1, True),    # 2^20 query rows: the streaming kernel (chunk relay)
+    (2, 16, 32768, 0, True),    # unordered too: the chunk relay ties or beats the atomics
+    (2, 16, 2048, 0, True),     # exactly 2^16 rows
+    (2, 16, 1024, 0, False),    # 2^15 rows: the per-tile kernels
+    (1, 2, 16384, 1, False),
+    (2, 16, 32768, 2, False),   # deterministic 2: the per-kv-tile relay
+])
+def test_default_engine_follows_the_measured_table(lib, B, H, S, det, stream):
+    plan = api.sdpa_bwd_plan(_desc(B=B, Hq=H, Hkv=H, D=64, Sq=S, Skv=S, window_left=128, deterministic=det))
+    assert (api.sdpa_bwd_schedule(plan, S, S)["tile_kv"] == 128) == stream
