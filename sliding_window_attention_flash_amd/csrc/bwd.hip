@@ -225,15 +225,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
     L = xcd_remap(blockIdx.x, gridDim.x);
   }
   const int nbh = p.B * p.Hkv;
-  int bh, jt;
+  int b, hk, jt;
   if (RELAY) {
     jt = L / nbh;
-    bh = L % nbh;
+    b = (L % nbh) / p.Hkv;
+    hk = L % p.Hkv;
   } else {
-    bh = L / p.n_kv_tiles;
+    // kv-head-major: an XCD's contiguous range holds one (or a few) kv heads
+    // of every sequence, so sequences of different lengths do not load the
+    // XCDs unevenly; a (kv head, sequence)'s kv-tiles stay together
     jt = L % p.n_kv_tiles;
+    b = (L / p.n_kv_tiles) % p.B;
+    hk = L / (p.n_kv_tiles * p.B);
   }
-  const int b = bh / p.Hkv, hk = bh % p.Hkv;
   const Seq s = load_seq(p, b);
   const int kv0 = jt * kTile;
   if (kv0 >= s.cap_kv) return;
@@ -574,16 +578,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
   // bwd_dot is not launched: clear the control words it would have
   if (DELTA && blockIdx.x == 0 && tid < 2) a.ctl[tid] = 0;
 
-  // block -> (sequence, kv head, run of q-tiles, head within the group): the
+  // block -> (kv head, sequence, run of q-tiles, head within the group): the
   // heads that share a kv head, and neighbouring runs, read the same K / V
-  // tiles and run next to each other on one XCD
+  // tiles and run next to each other on one XCD; kv-head-major, so an XCD's
+  // range spans every sequence (balanced over mixed lengths), and runs
+  // descending, so the later q-tiles, which a causal mask gives the most
+  // kv-tiles, start first
   const int nruns = (p.n_q_tiles + p.dq_tiles - 1) / p.dq_tiles;
   int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = L % p.G;
   L /= p.G;
-  const int run = L % nruns;
+  const int run = nruns - 1 - L % nruns;
   L /= nruns;
-  const int hk = L % p.Hkv, b = L / p.Hkv, h = hk * p.G + hg;
+  const int b = L % p.B, hk = L / p.B, h = hk * p.G + hg;
   const Seq s = load_seq(p, b);
   const int ia = run * p.dq_tiles;
   const int ib = min(ia + p.dq_tiles, (s.cap_q + kTile - 1) / kTile);  // q-tiles holding slot rows

@@ -37,14 +37,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
   const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // block -> (sequence, kv head, run of q-tiles, head within the group)
+  // block -> (kv head, sequence, run of q-tiles, head within the group),
+  // kv-head-major with runs descending, as in the q-major dQ pass
   const int nruns = (p.n_q_tiles + p.fwd_tiles - 1) / p.fwd_tiles;
   int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = L % p.G;
   L /= p.G;
-  const int run = L % nruns;
+  const int run = nruns - 1 - L % nruns;
   L /= nruns;
-  const int hk = L % p.Hkv, b = L / p.Hkv, h = hk * p.G + hg;
+  const int b = L % p.B, hk = L / p.B, h = hk * p.G + hg;
   const Seq s = load_seq(p, b);
   const int ia = run * p.fwd_tiles;
   const int ib = min(ia + p.fwd_tiles, (s.cap_q + kTile - 1) / kTile);  // q-tiles holding slot rows
