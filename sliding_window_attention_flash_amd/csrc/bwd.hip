@@ -201,12 +201,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
   constexpr int RPP = kThreads / CH;
   constexpr int NPASS = kTile / RPP;
 
-  __shared__ __align__(16) T sQ[kTile * D];
-  __shared__ __align__(16) T sdO[kTile * D];
+  // Q / dO tiles (Q, then dO) and their row statistics (LSE in log2 units,
+  // then delta), double-buffered as separately named arrays: every access
+  // names its array, so the compiler sees that reads of one buffer need not
+  // wait for the loads streaming into the other.  The relay keeps one tile
+  // buffer (its K tile and dS^T take the room; two blocks still fit on a CU
+  // at head_dim 128) and refills it while the relay step runs.
+  __shared__ __align__(16) T sQO0[2 * kTile * D];
+  __shared__ __align__(16) T sQO1[RELAY ? 8 : 2 * kTile * D];
+  __shared__ __align__(16) float sLD0[2 * kTile];
+  __shared__ __align__(16) float sLD1[2 * kTile];
   __shared__ __align__(16) T sK[kTile * D];
   __shared__ __align__(16) T sdSt[kTile * kTile];  // dS^T [key][q], 64-wide swizzled rows
-  __shared__ __align__(16) float sLse[kTile];
-  __shared__ __align__(16) float sDelta[kTile];
   __shared__ int sTicket;
 
   const Problem& p = a.p;
@@ -290,8 +296,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dV[db] = dK[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Staging of one visit's Q / dO tile (registers first, then LDS).
-  V8 rq[NPASS], rdo[NPASS];
+  // Staging of one visit's Q / dO tile, straight into LDS, and of its row
+  // statistics (registers first, then LDS).
   float rlse = 0.f, rdelta = 0.f;
   int st_i = 0;
   // Visits go head by head through the group, q-tiles descending within a
@@ -306,39 +312,38 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
     }
   };
   // this thread's 16-byte chunk of row 0, head 0; a row r of head h is
-  // r * (row stride) + h * (head stride) further in either layout
-  const T* q00 = qp + elem_off(p, p.sq, b, s.row0_q, 0, 0) + 8 * (tid % CH);
-  const T* o00 = dop + elem_off(p, p.sdo, b, s.row0_q, 0, 0) + 8 * (tid % CH);
-  auto stage_load = [&](int h, int i) {  // a visited q-tile: the sequence has rows
+  // r * (row stride) + h * (head stride) further in either layout.  Lane l
+  // of a wave fills bytes 16 l of the wave's 1 KB piece of a pass: row
+  // tid / CH + ps RPP, stored chunk tid % CH, which holds logical chunk
+  // (tid % CH) ^ tsw(row) (the same in every pass).  Rows past the sequence
+  // repeat its last row: finite values, and P = 0 there (LSE = +inf).
+  const int qch = (tid % CH) ^ tsw<D>(tid / CH);
+  const T* q00 = qp + elem_off(p, p.sq, b, s.row0_q, 0, 0) + 8 * qch;
+  const T* o00 = dop + elem_off(p, p.sdo, b, s.row0_q, 0, 0) + 8 * qch;
+  auto stage_load = [&](int h, int i, T* dst) {  // a visited q-tile: the sequence has rows
     st_i = i;
     const int row0 = i * kTile;
-    const T* qh = q00 + h * p.sq[1];
-    const T* oh = o00 + h * p.sdo[1];
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int qi = min(row0 + tid / CH + ps * RPP, s.len_q - 1);
-      rq[ps] = ld8(row_at(qh, qi, p.sq[2]));
-      rdo[ps] = ld8(row_at(oh, qi, p.sdo[2]));
-    }
+    // the statistics first: waiting for them does not wait for the tiles
     if (tid < kTile) {
       const int64_t si = s.stat0 + h * s.stat_hs + min(row0 + tid, s.len_q - 1);
       rlse = a.lse[si];
       rdelta = a.delta[si];
     }
-  };
-  auto stage_store = [&]() {
-    const int row0 = st_i * kTile;
+    const T* qh = q00 + h * p.sq[1];
+    const T* oh = o00 + h * p.sdo[1];
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = tid / CH + ps * RPP, ch = tid % CH;
-      const bool ok = row0 + r < s.len_q;
-      *reinterpret_cast<V8*>(&sQ[toff<D>(r, ch)]) = ok ? rq[ps] : zero8;
-      *reinterpret_cast<V8*>(&sdO[toff<D>(r, ch)]) = ok ? rdo[ps] : zero8;
+      const int qi = min(row0 + tid / CH + ps * RPP, s.len_q - 1);
+      const int piece = (ps * kThreads + 64 * w) * 8;  // wave-uniform element offset
+      ld16_to_lds(row_at(qh, qi, p.sq[2]), dst + piece);
+      ld16_to_lds(row_at(oh, qi, p.sdo[2]), dst + kTile * D + piece);
     }
+  };
+  auto stage_stats = [&](float* ld) {
     if (tid < kTile) {
-      const bool ok = row0 + tid < s.len_q;
-      sLse[tid] = ok ? rlse * kLog2e : INFINITY;  // exp2(x - inf) = 0: padding rows carry no weight
-      sDelta[tid] = ok ? rdelta : 0.f;
+      const bool ok = st_i * kTile + tid < s.len_q;
+      ld[tid] = ok ? rlse * kLog2e : INFINITY;  // exp2(x - inf) = 0: padding rows carry no weight
+      ld[kTile + tid] = ok ? rdelta : 0.f;
     }
   };
 
@@ -354,23 +359,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
 
   int h = hk * p.G, i = qlo + nit - 1;  // the current visit
   if (nvisit > 0) {
-    stage_load(h, i);
-    stage_store();
+    stage_load(h, i, sQO0);
+    stage_stats(sLD0);
   }
-  __syncthreads();
-  // Every load so far has landed (or the loop below never runs), but on the
-  // path that skips the staging the compiler would keep the K / V loads
+  // Every load has landed before the first visit (and on the path that
+  // skips the staging the compiler would otherwise keep the K / V loads
   // outstanding and make each visit's first products wait for the next
-  // visit's prefetch: settle them here, once.
+  // visit's prefetch).
   __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   T* dqp = static_cast<T*>(a.dq);
-  int nh = h, ni = i;  // the next visit
-  for (int v = 0; v < nvisit; ++v, h = nh, i = ni) {
+  int v = 0, nh = h, ni = i;  // the visit count and the next visit
+  // One visit: reads the tile in (sQ, sdO) and its statistics (sLse,
+  // sDelta), and streams the next visit's into (nQO, nLD), which were last
+  // read before the previous barrier.  False after the last visit.
+  auto visit = [&](const T* sQ, const float* sLse, T* nQO, float* nLD) -> bool {
+    const T* sdO = sQ + kTile * D;
+    const float* sDelta = sLse + kTile;
     nh = h;
     ni = i;
     next_visit(nh, ni);
-    if (v + 1 < nvisit) stage_load(nh, ni);
+    const bool more = v + 1 < nvisit;
+    if (!RELAY && more) stage_load(nh, ni, nQO);
     const int q0 = i * kTile;
     // t - tlo of (row q0, key kv0 + 16 w); block mb spans [u_mb - 15, u_mb + 15]
     const int u0 = q0 + g.diag - (kv0 + 16 * w) - tlo;
@@ -464,12 +475,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
     } else {
       visit_body(std::false_type());
     }
-    __syncthreads();  // dS^T complete; the Q / dO tile is free
-    if (v + 1 < nvisit) stage_store();
     if (!RELAY) {
-      __syncthreads();  // next tile staged
-      continue;
+      if (more) stage_stats(nLD);
+      __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed
+      __syncthreads();                // and this one is free
+      ++v;
+      h = nh;
+      i = ni;
+      return more;
     }
+    __syncthreads();  // dS^T complete; the Q / dO tile is free
+    if (more) stage_load(nh, ni, nQO);
 
     // dQ rows q0 + 16 w + 4 gq + r, d = 16 db + c: each relay add covers 16
     // consecutive floats of 4 rows
@@ -507,7 +523,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
                      outr + 16 * db);
     }
     relay_release(semp, turn, nv, tid);
+    if (more) stage_stats(nLD);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // next tile staged; dS^T reads done
+    ++v;
+    h = nh;
+    i = ni;
+    return more;
+  };
+  if (nvisit > 0) {
+    if constexpr (RELAY) {
+      while (visit(sQO0, sLD0, sQO0, sLD1) && visit(sQO0, sLD1, sQO0, sLD0)) {
+      }
+    } else {
+      while (visit(sQO0, sLD0, sQO1, sLD1) && visit(sQO1, sLD1, sQO0, sLD0)) {
+      }
+    }
   }
 
   // Epilogue: dK = scale * sum dS^T Q, dV = sum P^T dO; a tile that visited
@@ -569,8 +600,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
   constexpr int RPP = kThreads / CH;
   constexpr int NPASS = kTile / RPP;
 
-  __shared__ __align__(16) T sK[2][kTile * D];
-  __shared__ __align__(16) T sV[2][kTile * D];
+  // K / V double buffer as two arrays (K tile, then V tile): every access
+  // names its array, so the compiler sees that reads of one buffer need not
+  // wait for the loads streaming into the other
+  __shared__ __align__(16) T sKV0[2 * kTile * D];
+  __shared__ __align__(16) T sKV1[2 * kTile * D];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
@@ -640,6 +674,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
   auto load_q = [&](int i, V8* qv, V8* ov, V8* xv, float& l2, float& dl) {
     const int row = i * kTile + 16 * w + c;
     const int qr = min(row, s.len_q - 1);
+    // the row statistics first: waiting for them then does not wait for
+    // the row loads behind them
+    l2 = INFINITY;
+    dl = 0.f;
+    if (row < s.len_q) {
+      const int64_t si = s.stat0 + h * s.stat_hs + row;
+      l2 = a.lse[si];
+      if (!DELTA) dl = a.delta[si];
+    }
     const T* qrow = row_at(q0h, qr, p.sq[2]);
     const T* orow = row_at(o0h, qr, p.sdo[2]);
 #pragma unroll
@@ -651,13 +694,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
       const T* xrow = row_at(x0h, qr, p.so[2]);
 #pragma unroll
       for (int st = 0; st < NS; ++st) xv[st] = ld8(xrow + 32 * st);
-    }
-    l2 = INFINITY;
-    dl = 0.f;
-    if (row < s.len_q) {
-      const int64_t si = s.stat0 + h * s.stat_hs + row;
-      l2 = a.lse[si] * kLog2e;
-      if (!DELTA) dl = a.delta[si];
     }
   };
   // DELTA: delta of the lane's row from its dO and O slices (the 4 lanes
@@ -679,23 +715,20 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
 
   // K / V staging (a visited kv-tile: len_kv > 0); rows past the sequence
   // repeat its last key (finite values; the mask gives them zero weight)
-  const T* k0 = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, 0) + 8 * (tid % CH);
-  const T* v0 = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, 0) + 8 * (tid % CH);
-  V8 rk[NPASS], rv[NPASS];
-  auto load_kv = [&](int j) {
+  // Straight into LDS: lane l of a wave fills bytes 16 l of the wave's 1 KB
+  // piece of a pass, i.e. row tid / CH + ps RPP, stored chunk tid % CH,
+  // which holds logical chunk (tid % CH) ^ tsw(row) (rows of a pass differ
+  // by multiples of 8, so the chunk is the same in every pass).
+  const int kch = (tid % CH) ^ tsw<D>(tid / CH);
+  const T* k0 = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, 0) + 8 * kch;
+  const T* v0 = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, 0) + 8 * kch;
+  auto load_kv = [&](int j, T* dK, T* dV) {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int kk = min(j * kTile + tid / CH + ps * RPP, s.len_kv - 1);
-      rk[ps] = ld8(row_at(k0, kk, p.sk[2]));
-      rv[ps] = ld8(row_at(v0, kk, p.sv[2]));
-    }
-  };
-  auto store_kv = [&](int buf) {
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = tid / CH + ps * RPP, ch = tid % CH;
-      *reinterpret_cast<V8*>(&sK[buf][toff<D>(r, ch)]) = rk[ps];
-      *reinterpret_cast<V8*>(&sV[buf][toff<D>(r, ch)]) = rv[ps];
+      const int piece = (ps * kThreads + 64 * w) * 8;  // wave-uniform element offset
+      ld16_to_lds(row_at(k0, kk, p.sk[2]), dK + piece);
+      ld16_to_lds(row_at(v0, kk, p.sv[2]), dV + piece);
     }
   };
 
@@ -712,11 +745,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
   const unsigned trange = (unsigned)(thi - tlo);
 
   load_q(ci, qB, oB, xB, lse2, del);
+  lse2 *= kLog2e;
+  load_kv(cj, sKV0, sKV0 + kTile * D);
   if (DELTA) del = form_delta(ci, oB, xB);
-  load_kv(cj);
-  store_kv(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int n = 0;; ++n) {
+  // One pair: reads the tiles in (cK, cV) and streams the next pair's into
+  // (nK, nV), which were last read before the previous barrier.  False once
+  // the run is done.
+  auto step = [&](const T* cK, const T* cV, T* nK, T* nV) -> bool {
     // the pair after (ci, cj): the next kv-tile of ci, else the first of
     // the next visited q-tile of the run
     int ni = ci, nj = cj + 1;
@@ -726,12 +763,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
     }
     const bool more = ni < ib;
     if (more) {
-      load_kv(nj);
+      load_kv(nj, nK, nV);
       if (RUN && ni != ci) load_q(ni, nqB, noB, nxB, nlse2, ndel);
     }
-    const int buf = n & 1;
-    const T* cK = sK[buf];
-    const T* cV = sV[buf];
     const int kv0 = cj * kTile;
     const int kvn = s.len_kv - kv0;                               // keys of this tile inside the sequence
     const int u0 = ci * kTile + 16 * w + g.diag - tlo - kv0;      // t - tlo at (row 16 w, key kv0)
@@ -809,15 +843,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
           qB[st] = nqB[st];
           oB[st] = noB[st];
         }
-        lse2 = nlse2;
+        lse2 = nlse2 * kLog2e;
         del = DELTA ? form_delta(ni, noB, nxB) : ndel;
       }
     }
-    if (!more) break;
-    store_kv(buf ^ 1);
-    __syncthreads();  // buffer buf is free; the next one is staged
+    if (!more) return false;
+    __builtin_amdgcn_s_waitcnt(0);  // the next tiles have landed in LDS
+    __syncthreads();                // and (cK, cV) are free
     ci = ni;
     cj = nj;
+    return true;
+  };
+  while (step(sKV0, sKV0 + kTile * D, sKV1, sKV1 + kTile * D) &&
+         step(sKV1, sKV1 + kTile * D, sKV0, sKV0 + kTile * D)) {
   }
 }
 

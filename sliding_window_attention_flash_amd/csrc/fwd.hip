@@ -26,12 +26,15 @@
 namespace swa {
 
 template <typename T, int D, bool RUN>
-__global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
   constexpr int NS = D / 32, NDB = D / 16;
   constexpr int CH = D / 8, RPP = kThreads / CH, NPASS = kTile / RPP;
-  __shared__ __align__(16) T sK[2][kTile * D];
-  __shared__ __align__(16) T sV[2][kTile * D];
+  // K / V double buffer as two arrays (K tile, then V tile): every access
+  // names its array, so the compiler sees that reads of one buffer need not
+  // wait for the loads streaming into the other
+  __shared__ __align__(16) T sKV0[2 * kTile * D];
+  __shared__ __align__(16) T sKV1[2 * kTile * D];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
@@ -103,24 +106,21 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
     for (int st = 0; st < NS; ++st) qv[st] = ld8(qrow + 32 * st);
   };
   // K / V staging (a visited kv-tile: len_kv > 0); rows past the sequence
-  // repeat its last key (finite values; the mask gives them zero weight)
-  const T* k0 = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, 0) + 8 * (tid % CH);
-  const T* v0 = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, 0) + 8 * (tid % CH);
-  V8 rk[NPASS], rv[NPASS];
-  auto load_kv = [&](int j) {
+  // repeat its last key (finite values; the mask gives them zero weight).
+  // Straight into LDS: lane l of a wave fills bytes 16 l of the wave's 1 KB
+  // piece of a pass, i.e. row tid / CH + ps RPP, stored chunk tid % CH,
+  // which holds logical chunk (tid % CH) ^ tsw(row) (rows of a pass differ
+  // by multiples of 8, so the chunk is the same in every pass).
+  const int kch = (tid % CH) ^ tsw<D>(tid / CH);
+  const T* k0 = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, 0) + 8 * kch;
+  const T* v0 = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, 0) + 8 * kch;
+  auto load_kv = [&](int j, T* dK, T* dV) {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int kk = min(j * kTile + tid / CH + ps * RPP, s.len_kv - 1);
-      rk[ps] = ld8(row_at(k0, kk, p.sk[2]));
-      rv[ps] = ld8(row_at(v0, kk, p.sv[2]));
-    }
-  };
-  auto store_kv = [&](int buf) {
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = tid / CH + ps * RPP, ch = tid % CH;
-      *reinterpret_cast<V8*>(&sK[buf][toff<D>(r, ch)]) = rk[ps];
-      *reinterpret_cast<V8*>(&sV[buf][toff<D>(r, ch)]) = rv[ps];
+      const int piece = (ps * kThreads + 64 * w) * 8;  // wave-uniform element offset
+      ld16_to_lds(row_at(k0, kk, p.sk[2]), dK + piece);
+      ld16_to_lds(row_at(v0, kk, p.sv[2]), dV + piece);
     }
   };
 
@@ -137,14 +137,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
   const unsigned trange = (unsigned)(thi - tlo);
 
   load_q(ci, qB);
-  load_kv(cj);
-  store_kv(0);
-  __syncthreads();
-  // The compiler may issue the Q loads after the K / V loads, so that the
-  // staging above does not wait for them; left outstanding, they would make
-  // every pair's first products wait for that pair's K / V prefetch.
+  load_kv(cj, sKV0, sKV0 + kTile * D);
   __builtin_amdgcn_s_waitcnt(0);
-  for (int n = 0;; ++n) {
+  __syncthreads();
+  // One pair: reads the tiles in (cK, cV) and streams the next pair's into
+  // (nK, nV), which were last read before the previous barrier.  False once
+  // the run is done.
+  auto step = [&](const T* cK, const T* cV, T* nK, T* nV) -> bool {
     int ni = ci, nj = cj + 1;
     if (nj > g.kv_last(ci)) {
       ni = RUN ? next_visited(ci + 1) : ib;
@@ -152,12 +151,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
     }
     const bool more = ni < ib;
     if (more) {
-      load_kv(nj);
+      load_kv(nj, nK, nV);
       if (RUN && ni != ci) load_q(ni, nqB);
     }
-    const int buf = n & 1;
-    const T* cK = sK[buf];
-    const T* cV = sV[buf];
     const int kv0 = cj * kTile;
     const int kvn = s.len_kv - kv0;                           // keys of this tile inside the sequence
     const int u0 = ci * kTile + 16 * w + g.diag - tlo - kv0;  // t - tlo at (row 16 w, key kv0)
@@ -245,14 +241,17 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void fwd_kerne
         for (int st = 0; st < NS; ++st) qB[st] = nqB[st];
       }
     }
-    if (!more) break;
-    store_kv(buf ^ 1);
-    __syncthreads();  // buffer buf is free; the next one is staged
-    // the next q-tile's rows (if this pair ended one) are needed by the next
-    // pair's first products: settle them before its prefetch is issued
-    if (RUN) __builtin_amdgcn_s_waitcnt(0);
+    if (!more) return false;
+    // the next tiles (and the next q-tile's rows, if this pair ended one)
+    // have landed, and (cK, cV) are free
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     ci = ni;
     cj = nj;
+    return true;
+  };
+  while (step(sKV0, sKV0 + kTile * D, sKV1, sKV1 + kTile * D) &&
+         step(sKV1, sKV1 + kTile * D, sKV0, sKV0 + kTile * D)) {
   }
 }
 

@@ -16,6 +16,14 @@ __device__ __forceinline__ void st8(T* p, const typename Elem<T>::vec8& v) {
   *reinterpret_cast<typename Elem<T>::vec8*>(p) = v;
 }
 
+// 16 bytes from global memory straight into LDS: lane l of the wave writes
+// bytes [16 l, 16 l + 16) after the wave-uniform LDS address `lds`.  (A
+// plain function: called with dependent pointer types inside a kernel
+// template, the builtin keeps the host pass from emitting the launch stub.)
+__device__ __forceinline__ void ld16_to_lds(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
 // Row `row` (>= 0) of a tensor whose row stride fits in 32 bits (checked
 // when a plan is made): one 32 x 32 -> 64-bit multiply-add.
 template <typename T>
