@@ -108,13 +108,14 @@ def workloads():
 
 
 def main_kernel_bytes(w) -> int:
-    """Algorithmic HBM bytes of one bwd_main launch: Q, dO read and dQ
-    written once per query-head row, plus the row's LSE and delta (fp32);
+    """Algorithmic HBM bytes of one launch of the streaming kernel: Q, dO and
+    O read and dQ written once per query-head row, plus the row's LSE (fp32)
+    -- it forms delta itself; with a sink it reads delta (fp32) instead of O;
     K, V read and dK, dV written once per kv-head row."""
-    from sliding_window_attention_flash_amd.synth import Workload  # noqa: F401
     rows_q = sum(w.valid_len_q()) * w.heads_q
     rows_kv = sum(w.valid_len_kv()) * w.heads_kv
-    return rows_q * (3 * w.head_dim * 2 + 8) + rows_kv * (4 * w.head_dim * 2)
+    per_q = 3 * w.head_dim * 2 + 8 if w.sink else 4 * w.head_dim * 2 + 4
+    return rows_q * per_q + rows_kv * (4 * w.head_dim * 2)
 
 
 def compulsory_bytes(w) -> int:

@@ -235,6 +235,7 @@ swa::Problem make_problem(const sdpa_attn_desc* d, int engine) {
   // it holds, replacing the bwd_dot pass and its second read of dO; the
   // per-q-tile dSink partials stay with bwd_dot.
   p.dq_delta = p.split_dq && p.dq_tiles > 1 && !d->has_sink;
+  p.stream_delta = p.stream && !d->has_sink;
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one
     // block per MI355X CU, never shorter than 2 steps (so a q-tile has at
@@ -417,9 +418,13 @@ sdpa_status bwd_run(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensors* t, void* 
   a.relay_bias = pl->relay_bias;
 
   hipError_t e;
-  // dq_delta: the dQ pass forms delta, so it runs first and bwd_dot not at all
-  if (!a.p.dq_delta && (e = swa::launch_bwd_dot(a, stream)) != hipSuccess)
+  // dq_delta: the dQ pass forms delta, so it runs first and bwd_dot not at
+  // all; stream_delta: the streaming kernel forms delta, and bwd_clear does
+  // the clearing bwd_dot would have done
+  if (!a.p.dq_delta && !a.p.stream_delta && (e = swa::launch_bwd_dot(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dot launch: %s", hipGetErrorString(e));
+  if (a.p.stream_delta && (e = swa::launch_bwd_clear(a, stream)) != hipSuccess)
+    return fail(SDPA_ERR_HIP, "bwd_clear launch: %s", hipGetErrorString(e));
   if (a.p.dq_delta && (e = swa::launch_bwd_dq(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dq launch: %s", hipGetErrorString(e));
   if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess)

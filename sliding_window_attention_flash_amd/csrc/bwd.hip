@@ -172,6 +172,43 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bwd_clear: where the streaming kernel forms delta itself (no sink), the
+// clearing bwd_dot would do for it: the control words, the q-tile counters,
+// the dQ rows of q-tiles no chunk visits and, with fp32 atomics, the
+// partial-sum slots of q-tiles several chunks visit.  One 16-thread group
+// per q-tile, 16 q-tiles per block (head_dim 64, the streaming kernel's).
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_clear_kernel(BwdArgs a) {
+  typedef typename Elem<T>::vec8 V8;
+  constexpr int CH = 64 / 8;  // 16-byte chunks per row
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, gl = tid & 15, h = blockIdx.y, b = blockIdx.z;
+  const int tile = blockIdx.x * 16 + (tid >> 4);
+  if (blockIdx.x == 0 && h == 0 && b == 0 && tid < 2) a.ctl[tid] = 0;
+  if (tile >= p.n_q_tiles) return;
+  if (gl == 0) a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile] = 0;
+  const Seq s = load_seq(p, b);
+  const int row_base = tile * kTile, rows = min(kTile, s.cap_q - row_base);
+  if (rows <= 0) return;
+  SeqSched g;
+  main_sched(p, s, g);
+  const int nv = chunk_visitors(p, g, tile);
+  if (nv == 0) {
+    T* dqp = static_cast<T*>(a.dq);
+    V8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
+    for (int e = gl; e < rows * CH; e += 16)
+      st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
+  } else if (!p.stream_relay && nv > 1) {
+    float4* acc = reinterpret_cast<float4*>(a.dq_acc + stream_slot(p, s, b, h, tile) * kTile * 64);
+    const float4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int e = gl; e < kTile * 64 / 4; e += 16) acc[e] = z;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bwd_main: one block (4 waves) per (kv-tile of 64 keys, kv head, sequence);
 // two blocks per CU.
 //
@@ -883,6 +920,16 @@ static hipError_t dot_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dot_kernel<T, 64>), grid, dim3(kThreads), 0, st, a);
   else
     hipLaunchKernelGGL((bwd_dot_kernel<T, 128>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_clear(const BwdArgs& a, hipStream_t st) {
+  if (a.p.n_q_tiles == 0) return hipSuccess;
+  dim3 grid((a.p.n_q_tiles + 15) / 16, a.p.Hq, a.p.B);
+  if (a.dtype == 0)
+    hipLaunchKernelGGL((bwd_clear_kernel<__bf16>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_clear_kernel<_Float16>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

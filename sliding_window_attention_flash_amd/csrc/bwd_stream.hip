@@ -161,7 +161,7 @@ __device__ __forceinline__ uint32_t pin(uint32_t x) {
 
 }  // namespace
 
-template <typename T, bool RELAY>
+template <typename T, bool RELAY, bool DELTA>
 __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
   // The ring is a circle of NRB 16-row blocks: row r of q-tile t is row
@@ -209,10 +209,12 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   const T* kb = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, h, 0);
   const T* vb = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, h, 0);
   const T* dob = static_cast<const T*>(a.dO) + elem_off(p, p.sdo, b, s.row0_q, h, 0);
+  const T* ob = static_cast<const T*>(a.o) + elem_off(p, p.so, b, s.row0_q, h, 0);  // DELTA
   T* dqb = static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, h, 0);
   T* dkb = static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, h, 0);
   T* dvb = static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, h, 0);
   const int rs_q = (int)p.sq[2], rs_k = (int)p.sk[2], rs_v = (int)p.sv[2], rs_do = (int)p.sdo[2];
+  const int rs_o = (int)p.so[2];
   const int rs_dq = (int)p.sdq[2], rs_dk = (int)p.sdk[2], rs_dv = (int)p.sdv[2];
   const float* lseb = a.lse + s.stat0 + h * s.stat_hs;
   const float* deltab = a.delta + s.stat0 + h * s.stat_hs;
@@ -283,23 +285,43 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     }
   };
   struct QRegs {
-    V8 q, o;
+    V8 q, o, x;  // x: O rows (DELTA, staged synchronously)
     float lse, delta;
     int tile;
   };
-  // only called for q-tiles the schedule visits, so the sequence has rows
-  auto load_q_tile = [&](int i, QRegs& r) {
+  // Thread tid holds 16 bytes (chunk tid % 8) of row tid / 8 of a q-tile.
+  // DELTA: delta of each row (rowsum of dO * O) is formed here from the
+  // thread's chunks, joined over the 8 lanes of the row; 0 past the
+  // sequence.
+  auto put_delta = [&](int tile, const V8& dov, const V8& xv) {
+    const int row = tid >> 3, mb = (tile % NSLOT) * 4;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += Elem<T>::to_float(dov[e]) * Elem<T>::to_float(xv[e]);
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if ((tid & 7) == 0) sLD[1][mb + (row >> 4)][row & 15] = tile * kTile + row < s.len_q ? acc : 0.f;
+  };
+  auto load_o_rows = [&](int i) {
+    const int row = tid >> 3, ch = tid & 7, qi = min(i * kTile + row, s.len_q - 1);
+    return gld8(ob + (int64_t)qi * rs_o + 8 * ch);
+  };
+  // only called for q-tiles the schedule visits, so the sequence has rows;
+  // with_o: also the O rows (DELTA), for a tile staged right away
+  auto load_q_tile = [&](int i, QRegs& r, bool with_o) {
     r.tile = i;
     const int row = tid >> 3, ch = tid & 7, qi = min(i * kTile + row, s.len_q - 1);
     r.q = gld8(qb + (int64_t)qi * rs_q + 8 * ch);
     r.o = gld8(dob + (int64_t)qi * rs_do + 8 * ch);
+    if (DELTA && with_o) r.x = load_o_rows(i);
     if (tid < kTile) {
       const int si = min(i * kTile + tid, s.len_q - 1);
       r.lse = lseb[si];
-      r.delta = deltab[si];
+      if (!DELTA) r.delta = deltab[si];
     }
   };
-  auto store_q_tile = [&](const QRegs& r) {
+  auto store_q_tile = [&](const QRegs& r, bool with_o) {
     const int mb = (r.tile % NSLOT) * 4, row = tid >> 3, ch = tid & 7;  // first block of the tile
     const bool ok = r.tile * kTile + row < s.len_q;
     *reinterpret_cast<V8*>(&sRing[0][mb + (row >> 4)][tile_off(row & 15, ch)]) = ok ? r.q : zero8;
@@ -308,8 +330,9 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const bool okr = r.tile * kTile + tid < s.len_q;
       // exp2(x - inf) = 0: padding rows carry no weight
       sLD[0][mb + (tid >> 4)][tid & 15] = okr ? r.lse * kLog2e : INFINITY;
-      sLD[1][mb + (tid >> 4)][tid & 15] = okr ? r.delta : 0.f;
+      if (!DELTA) sLD[1][mb + (tid >> 4)][tid & 15] = okr ? r.delta : 0.f;
     }
+    if (DELTA && with_o) put_delta(r.tile, r.o, r.x);
   };
 
   // ---- accumulators -------------------------------------------------------
@@ -397,7 +420,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     QRegs t0[NACT];
 #pragma unroll
     for (int k = 0; k < NACT; ++k)
-      if (k < n0) load_q_tile(loaded_hi + k, t0[k]);
+      if (k < n0) load_q_tile(loaded_hi + k, t0[k], true);
     // While they are in flight: the bands start (and their guard positions
     // stay) zero, and so does the ring, so that a ring slot read before any
     // tile was staged in it holds finite values (see the pair geometry).
@@ -408,7 +431,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < NACT; ++k)
-      if (k < n0) store_q_tile(t0[k]);
+      if (k < n0) store_q_tile(t0[k], true);
     loaded_hi += n0;
   }
   take_kv(j0, kBn, vBn);
@@ -420,8 +443,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     if (loaded_hi < qlo) loaded_hi = qlo;
     for (; loaded_hi < qhi; ++loaded_hi) {  // chunk start and gaps only
       QRegs t;
-      load_q_tile(loaded_hi, t);
-      store_q_tile(t);
+      load_q_tile(loaded_hi, t, true);
+      store_q_tile(t, true);
     }
     __syncthreads();  // T: ring ready; sK and the bands are free
 #pragma unroll
@@ -461,8 +484,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     }
     auto issue_pf = [&](int m) {
       if (m == 0 && has_next) load_kv(j + 1, kBn, vBn);
-      if (m == 1 && pf_n > 0) load_q_tile(pf_lo, pf[0]);
-      if (m == 2 && pf_n > 1) load_q_tile(pf_lo + 1, pf[1]);
+      if (m == 1 && pf_n > 0) load_q_tile(pf_lo, pf[0], false);
+      if (m == 2 && pf_n > 1) load_q_tile(pf_lo + 1, pf[1], false);
     };
 
     // ---- phase 1: this wave's band --------------------------------------------
@@ -580,9 +603,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     // so this wait is normally free; it also tells the compiler that no load
     // is outstanding past this point.
     __builtin_amdgcn_s_waitcnt(0);
-    if (pf_n > 0) store_q_tile(pf[0]);
-    if (pf_n > 1) store_q_tile(pf[1]);
+    if (pf_n > 0) store_q_tile(pf[0], false);
+    if (pf_n > 1) store_q_tile(pf[1], false);
     loaded_hi += pf_n;
+    // DELTA: the prefetched tiles' O rows load over phase 2; their delta is
+    // formed at the end of the step, before the next one reads it
+    V8 xo[2];
+    if (DELTA && pf_n > 0) xo[0] = load_o_rows(pf_lo);
+    if (DELTA && pf_n > 1) xo[1] = load_o_rows(pf_lo + 1);
     if (has_next) take_kv(j + 1, kBn, vBn);  // kB / vB of step j are no longer read
 
     // dK / dV of this step (zeros if it visited nothing) are complete after
@@ -637,6 +665,17 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < NACT; ++k)
       if (k < nret) retire(qlo + k, dQa[k]);
+    if (DELTA) {
+      // each thread reads back the dO chunk it staged
+      const int row = tid >> 3, ch = tid & 7;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k >= pf_n) break;
+        const int mb = ((pf_lo + k) % NSLOT) * 4;
+        put_delta(pf_lo + k, *reinterpret_cast<const V8*>(&sRing[1][mb + (row >> 4)][tile_off(row & 15, ch)]),
+                  xo[k]);
+      }
+    }
   }
 
   // ---- relay: boundary q-tiles this chunk joined after another chunk -------
@@ -688,20 +727,28 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
   }
 }
 
+template <typename T>
+static void stream_t(const BwdArgs& a, int n, hipStream_t st) {
+  if (a.p.stream_relay) {
+    if (a.p.stream_delta)
+      hipLaunchKernelGGL((bwd_stream_kernel<T, true, true>), dim3(n), dim3(NTHR), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_stream_kernel<T, true, false>), dim3(n), dim3(NTHR), 0, st, a);
+  } else {
+    if (a.p.stream_delta)
+      hipLaunchKernelGGL((bwd_stream_kernel<T, false, true>), dim3(n), dim3(NTHR), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_stream_kernel<T, false, false>), dim3(n), dim3(NTHR), 0, st, a);
+  }
+}
+
 hipError_t launch_bwd_stream(const BwdArgs& a, hipStream_t st) {
   const int n = a.p.B * a.p.Hq * a.p.n_chunks;
   if (n == 0) return hipSuccess;
-  if (a.dtype == 0) {
-    if (a.p.stream_relay)
-      hipLaunchKernelGGL((bwd_stream_kernel<__bf16, true>), dim3(n), dim3(NTHR), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_stream_kernel<__bf16, false>), dim3(n), dim3(NTHR), 0, st, a);
-  } else {
-    if (a.p.stream_relay)
-      hipLaunchKernelGGL((bwd_stream_kernel<_Float16, true>), dim3(n), dim3(NTHR), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_stream_kernel<_Float16, false>), dim3(n), dim3(NTHR), 0, st, a);
-  }
+  if (a.dtype == 0)
+    stream_t<__bf16>(a, n, st);
+  else
+    stream_t<_Float16>(a, n, st);
   return hipGetLastError();
 }
 

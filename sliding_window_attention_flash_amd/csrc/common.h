@@ -48,6 +48,7 @@ struct Problem {
   int fwd_tiles; // the same for the forward
   int stream;
   int stream_relay;  // streaming kernel: boundary q-tiles by the chunk relay (else fp32 atomics)
+  int stream_delta;  // streaming kernel forms delta as it stages q-tiles (no bwd_dot; no sink)
   int step_kv;
   int chunk;
   int n_chunks;

@@ -48,6 +48,7 @@ struct FwdArgs {
 };
 
 hipError_t launch_bwd_dot(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_clear(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_stream(const BwdArgs& a, hipStream_t stream);

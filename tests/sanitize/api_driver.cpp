@@ -13,6 +13,7 @@
 
 namespace swa {
 hipError_t launch_bwd_dot(const BwdArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_bwd_clear(const BwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_main(const BwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_dq(const BwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_stream(const BwdArgs&, hipStream_t) { return hipSuccess; }
