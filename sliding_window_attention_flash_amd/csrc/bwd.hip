@@ -175,36 +175,54 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
 // bwd_clear: where the streaming kernel forms delta itself (no sink), the
 // clearing bwd_dot would do for it: the control words, the q-tile counters,
 // the dQ rows of q-tiles no chunk visits and, with fp32 atomics, the
-// partial-sum slots of q-tiles several chunks visit.  One 16-thread group
-// per q-tile, 16 q-tiles per block (head_dim 64, the streaming kernel's).
+// partial-sum slots of q-tiles several chunks visit.  A block takes 64
+// q-tiles: each thread of the first 64 clears one counter and decides
+// whether its tile needs more; the whole block then clears those tiles in
+// turn (head_dim 64, the streaming kernel's).
+
+constexpr int kClearTiles = 64;
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_clear_kernel(BwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
   constexpr int CH = 64 / 8;  // 16-byte chunks per row
+  __shared__ int s_tile[kClearTiles];
+  __shared__ int s_n;
   const Problem& p = a.p;
-  const int tid = threadIdx.x, gl = tid & 15, h = blockIdx.y, b = blockIdx.z;
-  const int tile = blockIdx.x * 16 + (tid >> 4);
+  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = blockIdx.x * kClearTiles;
   if (blockIdx.x == 0 && h == 0 && b == 0 && tid < 2) a.ctl[tid] = 0;
-  if (tile >= p.n_q_tiles) return;
-  if (gl == 0) a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile] = 0;
+  if (tid == 0) s_n = 0;
+  __syncthreads();
   const Seq s = load_seq(p, b);
-  const int row_base = tile * kTile, rows = min(kTile, s.cap_q - row_base);
-  if (rows <= 0) return;
-  SeqSched g;
-  main_sched(p, s, g);
-  const int nv = chunk_visitors(p, g, tile);
-  if (nv == 0) {
-    T* dqp = static_cast<T*>(a.dq);
-    V8 z;
+  if (tid < kClearTiles && t0 + tid < p.n_q_tiles) {
+    const int tile = t0 + tid;
+    a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile] = 0;
+    if (tile * kTile < s.cap_q) {
+      SeqSched g;
+      main_sched(p, s, g);
+      const int nv = chunk_visitors(p, g, tile);
+      // nv == 0: zero dQ rows; nv > 1 with fp32 atomics: zero the slot
+      if (nv == 0) s_tile[atomicAdd(&s_n, 1)] = tile;
+      else if (!p.stream_relay && nv > 1) s_tile[atomicAdd(&s_n, 1)] = -1 - tile;
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  for (int k = 0; k < n; ++k) {
+    const int e0 = s_tile[k];
+    if (e0 >= 0) {
+      const int row_base = e0 * kTile, rows = min(kTile, s.cap_q - row_base);
+      T* dqp = static_cast<T*>(a.dq);
+      V8 z;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
-    for (int e = gl; e < rows * CH; e += 16)
-      st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
-  } else if (!p.stream_relay && nv > 1) {
-    float4* acc = reinterpret_cast<float4*>(a.dq_acc + stream_slot(p, s, b, h, tile) * kTile * 64);
-    const float4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int e = gl; e < kTile * 64 / 4; e += 16) acc[e] = z;
+      for (int e = 0; e < 8; ++e) z[e] = Elem<T>::from_float(0.f);
+      for (int e = tid; e < rows * CH; e += kThreads)
+        st8(dqp + elem_off(p, p.sdq, b, s.row0_q, h, row_base + e / CH) + 8 * (e % CH), z);
+    } else {
+      float4* acc = reinterpret_cast<float4*>(a.dq_acc + stream_slot(p, s, b, h, -1 - e0) * kTile * 64);
+      const float4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int e = tid; e < kTile * 64 / 4; e += kThreads) acc[e] = z;
+    }
   }
 }
 
@@ -925,7 +943,7 @@ static hipError_t dot_t(const BwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd_clear(const BwdArgs& a, hipStream_t st) {
   if (a.p.n_q_tiles == 0) return hipSuccess;
-  dim3 grid((a.p.n_q_tiles + 15) / 16, a.p.Hq, a.p.B);
+  dim3 grid((a.p.n_q_tiles + kClearTiles - 1) / kClearTiles, a.p.Hq, a.p.B);
   if (a.dtype == 0)
     hipLaunchKernelGGL((bwd_clear_kernel<__bf16>), grid, dim3(kThreads), 0, st, a);
   else
