@@ -107,13 +107,17 @@ typedef struct sdpa_attn_desc {
   int32_t engine;       /* backward kernels and dQ mechanism.  0: chosen by
                            the plan from a measured table, among those the
                            deterministic option allows.  For tuning studies,
-                           1..4 force one: 1 streaming kernel with fp32
+                           1..5 force one: 1 streaming kernel with fp32
                            atomics at chunk boundaries, 2 streaming kernel
                            with the chunk relay, 3 per-tile kernels with the
                            q-major dQ pass, 4 per-tile kernel with the
-                           per-kv-tile relay.  1 and 2 need heads_q ==
+                           per-kv-tile relay, 5 q-major streaming kernel
+                           (one pass; repeatable).  1 and 2 need heads_q ==
                            heads_kv, causal, window_right 0, window_left
-                           0..128, head_dim 64 (SDPA_ERR_UNSUPPORTED
+                           0..128, head_dim 64; 5 needs head_dim 128,
+                           causal, window_right 0, window_left 0..96, BHSD
+                           without seq_lens, seq_kv - seq_q a multiple of 32
+                           if bottom-right, no sink (SDPA_ERR_UNSUPPORTED
                            otherwise); 1 needs deterministic 0, and
                            deterministic 2 admits only 4
                            (SDPA_ERR_INVALID_ARG otherwise).  The forward

@@ -135,14 +135,34 @@ bool stream_eligible(const sdpa_attn_desc* d) {
          d->window_left <= 128 && d->head_dim == 64 && small_rows;
 }
 
-enum { ENGINE_STREAM_ATOMIC = 1, ENGINE_STREAM_RELAY = 2, ENGINE_TILE_QMAJOR = 3, ENGINE_TILE_RELAY = 4 };
+enum { ENGINE_STREAM_ATOMIC = 1, ENGINE_STREAM_RELAY = 2, ENGINE_TILE_QMAJOR = 3, ENGINE_TILE_RELAY = 4,
+       ENGINE_QSTREAM = 5 };
+
+// The q-major streaming kernel (bwd_qstream): head_dim 128, causal with no
+// right band, left window 0..96, dense sequences without padding lengths
+// whose diagonal offset is a multiple of 32, no sink.
+bool qstream_eligible(const sdpa_attn_desc* d) {
+  bool small_rows = true;
+  for (const int64_t rs : {d->stride_q[2], d->stride_k[2], d->stride_v[2], d->stride_o[2], d->stride_do[2],
+                           d->stride_dq[2], d->stride_dk[2], d->stride_dv[2]})
+    small_rows &= rs > 0 && rs <= INT32_MAX;
+  const int64_t diag = d->bottom_right ? (int64_t)d->seq_kv - d->seq_q : 0;
+  return d->layout == SDPA_LAYOUT_BHSD && !d->has_seq_lens && !d->has_sink && d->causal && d->window_right == 0 &&
+         d->window_left >= 0 && d->window_left <= 96 && d->head_dim == 128 && diag >= 0 && diag % 32 == 0 &&
+         d->seq_q > 0 && small_rows;
+}
 
 // The backward's kernels and dQ mechanism: a forced engine (validated
 // against the shape and the deterministic promise) or the plan's default.
 sdpa_status resolve_engine(const sdpa_attn_desc* d, int* engine) {
   const bool stream_ok = stream_eligible(d);
-  if (d->engine < 0 || d->engine > 4) return fail(SDPA_ERR_INVALID_ARG, "engine %d is not 0..4", d->engine);
+  if (d->engine < 0 || d->engine > 5) return fail(SDPA_ERR_INVALID_ARG, "engine %d is not 0..5", d->engine);
   if (d->engine) {
+    if (d->engine == ENGINE_QSTREAM && !qstream_eligible(d))
+      return fail(SDPA_ERR_UNSUPPORTED,
+                  "engine 5 (q-major streaming kernel) needs head_dim 128, causal, window_right 0, window_left "
+                  "0..96, dense sequences without seq_lens, seq_kv - seq_q a multiple of 32 (bottom-right), "
+                  "no sink and row strides below 2^31");
     if ((d->engine == ENGINE_STREAM_ATOMIC || d->engine == ENGINE_STREAM_RELAY) && !stream_ok)
       return fail(SDPA_ERR_UNSUPPORTED,
                   "engine %d (streaming kernel) needs heads_q == heads_kv, causal, window_right 0, window_left "
@@ -236,6 +256,29 @@ swa::Problem make_problem(const sdpa_attn_desc* d, int engine) {
   // per-q-tile dSink partials stay with bwd_dot.
   p.dq_delta = p.split_dq && p.dq_tiles > 1 && !d->has_sink;
   p.stream_delta = p.stream && !d->has_sink;
+  p.qstream = engine == ENGINE_QSTREAM;
+  if (p.qstream) {
+    // One 8-wave block per CU.  Chunks of consecutive 32-row q-steps per
+    // (sequence, kv head), at least 8 long, chosen so that the grid fills
+    // whole rounds of 256 CUs as closely as possible (fewer rounds on a tie).
+    const int64_t bh = (int64_t)d->batch * d->heads_kv, nqt = ((int64_t)d->seq_q + 31) / 32;
+    const int64_t n_cap = std::max<int64_t>(1, nqt / 8);
+    int best_n = 1;
+    double best_eff = 0.0;
+    for (int rounds = 1; rounds <= 16; ++rounds) {
+      const int64_t n0 = std::min(std::max<int64_t>(256 * (int64_t)rounds / bh, 1), n_cap);
+      const int64_t c = (nqt + n0 - 1) / n0, n = (nqt + c - 1) / c;
+      const int64_t blocks = bh * n;
+      const double eff = (double)blocks / (256.0 * (double)((blocks + 255) / 256));
+      if (eff > best_eff + 1e-9) {
+        best_eff = eff;
+        best_n = (int)n;
+      }
+      if (n0 == n_cap) break;
+    }
+    p.qs_chunk = (int)((nqt + best_n - 1) / best_n);
+    p.qs_nch = (int)((nqt + p.qs_chunk - 1) / p.qs_chunk);
+  }
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one
     // block per MI355X CU, never shorter than 2 steps (so a q-tile has at
@@ -309,7 +352,11 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   pl->off_delta = off;
   off = align256(off + sizeof(float) * (size_t)pl->stat_rows);
   pl->off_acc = off;
-  if (!p.split_dq) {
+  if (p.qstream) {
+    // the fp32 dK / dV partials of the 32-key tiles neighbouring chunks
+    // share: per (sequence, kv head, chunk boundary) 3 tiles x 2 sides
+    off = align256(off + sizeof(float) * (size_t)p.B * p.Hkv * p.qs_nch * 6 * 32 * 2 * p.D);
+  } else if (!p.split_dq) {
     size_t acc_floats = (size_t)pl->stat_rows * p.D;
     // the streaming kernel's unordered mode keeps each q-tile's partial sum
     // in a 64-row slot of its own (stream_slot: dense B x Hq x n_q_tiles
@@ -421,7 +468,7 @@ sdpa_status bwd_run(const sdpa_bwd_plan_t* pl, const sdpa_bwd_tensors* t, void* 
   // dq_delta: the dQ pass forms delta, so it runs first and bwd_dot not at
   // all; stream_delta: the streaming kernel forms delta, and bwd_clear does
   // the clearing bwd_dot would have done
-  if (!a.p.dq_delta && !a.p.stream_delta && (e = swa::launch_bwd_dot(a, stream)) != hipSuccess)
+  if (!a.p.dq_delta && !a.p.stream_delta && !a.p.qstream && (e = swa::launch_bwd_dot(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_dot launch: %s", hipGetErrorString(e));
   if (a.p.stream_delta && (e = swa::launch_bwd_clear(a, stream)) != hipSuccess)
     return fail(SDPA_ERR_HIP, "bwd_clear launch: %s", hipGetErrorString(e));

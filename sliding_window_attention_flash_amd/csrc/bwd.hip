@@ -968,6 +968,7 @@ static hipError_t main_td(const BwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t st) {
   if (a.p.stream) return launch_bwd_stream(a, st);
+  if (a.p.qstream) return launch_bwd_qstream(a, st);
   if (a.p.n_kv_tiles == 0) return hipSuccess;
   if (a.dtype == 0) return a.p.D == 64 ? main_td<__bf16, 64>(a, st) : main_td<__bf16, 128>(a, st);
   return a.p.D == 64 ? main_td<_Float16, 64>(a, st) : main_td<_Float16, 128>(a, st);

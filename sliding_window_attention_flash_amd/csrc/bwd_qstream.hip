@@ -1,0 +1,458 @@
+// bwd_qstream: the backward for short windows at head_dim 128 (GQA or MHA)
+// in one pass over query rows (gfx950).
+//
+// The rows of a 32-row q-step see at most 32 + W keys, four 32-key tiles for
+// W <= 96: kv-tiles i + d - 3 .. i + d for q-step i, with d = diag / 32 (the
+// plan takes this kernel only when diag is a multiple of 32, causal with no
+// right band, W <= 96, dense sequences, no sink).  One block of 8 waves (one
+// per CU) walks a chunk of consecutive q-steps of one (sequence, kv head);
+// for each q-step it takes the G query heads of the group in turn, one step
+// each.  The four kv-tiles of the window stay in a ring: K and V rows in
+// registers (B operands of S = Q K^T and dP = dO V^T), K in LDS (A operand of
+// dQ^T = K^T dS^T), and their dK^T / dV^T accumulate in registers across
+// every q-step and head that sees them.  So Q, dO and O are read once, each
+// step's dQ is complete within the step, and each kv-tile's dK / dV leave
+// once the window has passed it.
+//
+// Waves: wave w owns keys 16 (w % 2) .. + 15 of ring slot w / 2 (slot of
+// kv-tile j: j mod 4).  A step s (q-step i, head h), with its Q / dO / O
+// rows already in LDS buffer s mod 3:
+//   T  barrier; at a q-step's first head the slot entering the ring stores
+//      its K rows to LDS.
+//   1  every wave, for its 16 keys and the 32 rows: S = Q K^T, dP = dO V^T,
+//      P = exp2(S c - LSE), dS = P (dP - delta) (masked), dV^T += dO^T P,
+//      dK^T += Q^T dS, dS^T to LDS.
+//   A  this wave's loads for step s + 1 have landed; barrier.
+//   2  after a q-step's last head the oldest slot's waves retire their
+//      kv-tile and load the entering one; every wave starts the loads of
+//      step s + 2 (straight into LDS buffer (s + 2) mod 3), forms delta of
+//      step s + 1's rows, and computes and stores 16 rows x 32 head-dim
+//      columns of dQ.
+// The kv-tiles a chunk shares with its neighbours leave as fp32 partial
+// sums; bwd_qstream_fix adds the two sides in a fixed order, so the whole
+// pass is bitwise repeatable.
+//
+// All products are v_mfma_f32_16x16x32 (bf16 / f16 in, fp32 accumulate),
+// with the lane layouts and swizzled 128-wide LDS rows of the per-tile
+// kernels.
+
+#include "kernels.h"
+#include "tiles.h"
+
+namespace swa {
+
+namespace {
+
+constexpr int QD = 128;              // head dim
+constexpr int QNS = QD / 32;         // k-steps over the head dim
+constexpr int QNDB = QD / 16;        // 16-column blocks of the head dim
+constexpr int QCH = QD / 8;          // 16-byte chunks per row
+constexpr int QR = 32;               // rows of a q-step
+constexpr int QK = 32;               // keys of a ring tile
+constexpr int QSLOT = 4;             // ring tiles (W <= 96)
+constexpr int QWAVE = 2 * QSLOT;     // 16 keys per wave
+constexpr int QTHR = 64 * QWAVE;
+constexpr int QROWS = QR * QD;       // elements of a step's Q (or dO, O) rows
+constexpr int DSP = QR + 8;          // dS^T row pitch (elements): 80 bytes
+constexpr int QPART = QK * 2 * QD;   // floats of one kv-tile's dK / dV partial
+constexpr int QPIECES = 3 * QROWS * 2 / 1024;  // 1 KB pieces of a step's Q, dO, O
+constexpr int kWaitVm2 = 0xF72;      // s_waitcnt vmcnt(2) (no LDS / export wait)
+
+static_assert(QPIECES % QWAVE == 0, "a step's rows stream in whole pieces per wave");
+static_assert(QSLOT * QK >= QR + 96, "the ring holds the keys of a q-step for W <= 96");
+
+}  // namespace
+
+template <typename T>
+__global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
+  typedef typename Elem<T>::vec8 V8;
+  // Per step buffer (three, used in turn; separately named, so that reading
+  // one is no reason to wait for the loads streaming into another): Q then
+  // dO rows, O rows, and row statistics (LSE in log2 units, then delta).
+  // The ring's K tiles; dS^T [key][row].
+  __shared__ __align__(16) T sQO0[2 * QROWS];
+  __shared__ __align__(16) T sQO1[2 * QROWS];
+  __shared__ __align__(16) T sQO2[2 * QROWS];
+  __shared__ __align__(16) T sO0[QROWS];
+  __shared__ __align__(16) T sO1[QROWS];
+  __shared__ __align__(16) T sO2[QROWS];
+  __shared__ __align__(16) float sLD0[2 * QR];
+  __shared__ __align__(16) float sLD1[2 * QR];
+  __shared__ __align__(16) float sLD2[2 * QR];
+  __shared__ __align__(16) T sK[QSLOT * QK * QD];
+  __shared__ __align__(16) T sdSt[QSLOT * QK * DSP];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = w >> 1, wk = w & 1;
+  if (blockIdx.x == 0 && tid < 2) a.ctl[tid] = 0;  // no relay runs: no ticket, no expiry
+  const int nch = p.qs_nch, C = p.qs_chunk, G = p.G;
+  const int chunk = blockIdx.x % nch, bh = blockIdx.x / nch;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const Seq s = load_seq(p, b);
+  SeqSched g;
+  g.init(s.len_q, s.len_kv, p.bottom_right, 1, p.window, 0, QR, QK);
+  const int nqt = g.n_q_tiles, nkt = g.n_kv_tiles;
+  const int i0 = chunk * C, i1 = min(i0 + C, nqt);
+  if (i0 >= i1) return;
+  const int dq = g.diag / QK;  // the plan checked diag % 32 == 0
+  const int W = p.window;      // 0 <= W <= 96
+  // kv-tile in ring slot sl while q-step i runs: the one of i + dq - 3 ..
+  // i + dq congruent to sl mod 4 (outside [0, nkt): a hole)
+  auto slot_tile = [&](int sl, int i) { return i + dq - 3 + ((sl - (i + dq - 3)) & 3); };
+
+  V8 zero8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zero8[e] = Elem<T>::from_float(0.f);
+
+  // per-lane LDS offsets (elements), as in the per-tile kernels
+  int rd_off[QNS], tr_off[QNDB];
+#pragma unroll
+  for (int st = 0; st < QNS; ++st) rd_off[st] = toff<QD>(c, 4 * st + gq);
+#pragma unroll
+  for (int db = 0; db < QNDB; ++db) tr_off[db] = troff<QD>(c, gq, db);
+  // dS^T: this lane's key row of its slot, and the transposed read of phase 2
+  // (lane c of a 16-lane group points at key 4 gq + c / 4, rows 4 (c % 4) ..;
+  // it receives keys 4 gq .. + 3 of row c)
+  T* const my_ds = sdSt + (slot * QK + 16 * wk + c) * DSP + 4 * gq;
+  const int ds_rd = (4 * gq + (c >> 2)) * DSP + 4 * (c & 3);
+
+  // ---- the ring: this wave's 16 keys of its slot's kv-tile -------------------
+  V8 kB[QNS], vB[QNS];
+  f32x4 dK[QNDB], dV[QNDB];
+  int my_j = -1;  // kv-tile held (wave-uniform)
+  auto load_keys = [&](int j) {
+    my_j = j;
+    const int key = j * QK + 16 * wk + c;
+    const bool ok = j >= 0 && j < nkt && key < s.len_kv;
+    const int kr = clampi(key, 0, max(s.len_kv - 1, 0));
+    const T* krow = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, kr) + 8 * gq;
+    const T* vrow = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, kr) + 8 * gq;
+#pragma unroll
+    for (int st = 0; st < QNS; ++st) {
+      kB[st] = ok ? ld8(krow + 32 * st) : zero8;
+      vB[st] = ok ? ld8(vrow + 32 * st) : zero8;
+    }
+#pragma unroll
+    for (int db = 0; db < QNDB; ++db) dK[db] = dV[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto store_k_rows = [&]() {  // this wave's K rows into its slot's LDS tile
+    T* kt = sK + slot * QK * QD;
+#pragma unroll
+    for (int st = 0; st < QNS; ++st) *reinterpret_cast<V8*>(&kt[toff<QD>(16 * wk + c, 4 * st + gq)]) = kB[st];
+  };
+  // dK = scale dS^T Q, dV = P^T dO of kv-tile my_j: straight out when every
+  // q-step that sees it is in this chunk, else as one side's fp32 partial
+  auto retire = [&]() {
+    const int j = my_j;
+    if (j < 0 || j >= nkt) return;
+    const int key = j * QK + 16 * wk + c;
+    const int lo = g.q_lo(j), hi = lo + g.n_iters(j);
+    if (lo >= i0 && hi <= i1) {
+      if (key < s.cap_kv) {
+        T* dkp = static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, hk, key) + 4 * gq;
+        T* dvp = static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, hk, key) + 4 * gq;
+#pragma unroll
+        for (int db = 0; db < QNDB; ++db) {
+          T kx[4], vx[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            kx[r] = Elem<T>::from_float(p.scale * dK[db][r]);
+            vx[r] = Elem<T>::from_float(dV[db][r]);
+          }
+          *reinterpret_cast<u32x2*>(dkp + 16 * db) = __builtin_bit_cast(u32x2, kx);
+          *reinterpret_cast<u32x2*>(dvp + 16 * db) = __builtin_bit_cast(u32x2, vx);
+        }
+      }
+    } else {
+      // boundary k between chunks k - 1 and k: tile t = j - (k C + dq - 3)
+      // (0 .. 2); side 0 from the earlier chunk, 1 from the later
+      const int later = lo < i0;
+      const int k = later ? chunk : chunk + 1;
+      const int t = j - (k * C + dq - 3);
+      float* part = a.dq_acc + ((((int64_t)bh * nch + k) * 3 + t) * 2 + later) * QPART + (16 * wk + c) * 2 * QD;
+#pragma unroll
+      for (int db = 0; db < QNDB; ++db) {
+        *reinterpret_cast<f32x4*>(part + 16 * db + 4 * gq) = dK[db];
+        *reinterpret_cast<f32x4*>(part + QD + 16 * db + 4 * gq) = dV[db];
+      }
+    }
+  };
+
+  // ---- a step's rows -------------------------------------------------------
+  // Q / dO / O of (q-step i, head h): 24 pieces of 1 KB (4 rows each), 3 per
+  // wave, straight into LDS; lane l fills bytes 16 l of a piece: row
+  // 4 pr + l / 16, stored chunk l % 16, which holds logical chunk
+  // (l % 16) ^ tsw(row).  Rows past the sequence repeat its last row.
+  auto stream_rows = [&](int i, int h, T* qo, T* ob) {
+#pragma unroll
+    for (int k = 0; k < QPIECES / QWAVE; ++k) {
+      const int pc = (QPIECES / QWAVE) * w + k, ten = pc >> 3, pr = pc & 7;
+      const int row = 4 * pr + (l >> 4), ch = (l & 15) ^ tsw<QD>(row);
+      const int gr = min(i * QR + row, s.len_q - 1);
+      const int64_t* st = ten == 0 ? p.sq : (ten == 1 ? p.sdo : p.so);
+      const T* base = static_cast<const T*>(ten == 0 ? a.q : (ten == 1 ? a.dO : a.o));
+      T* dst = ten == 2 ? ob : qo + ten * QROWS;
+      ld16_to_lds(base + elem_off(p, st, b, s.row0_q, h, gr) + 8 * ch, dst + pr * 512);
+    }
+  };
+  auto load_lse = [&](int i, int h) {  // wave 0, lane l < 32: row l
+    return a.lse[s.stat0 + h * s.stat_hs + min(i * QR + (l & 31), s.len_q - 1)];
+  };
+  auto store_lse = [&](int i, float v, float* ld) {
+    if (w == 0 && l < QR) ld[l] = i * QR + l < s.len_q ? v * kLog2e : INFINITY;  // padding rows: P = 0
+  };
+  // delta of the step's rows from its dO (in qo) and O (in ob): 16 lanes per
+  // row, one 16-byte chunk each
+  auto form_delta = [&](int i, const T* qo, const T* ob, float* ld) {
+    const int row = tid >> 4, ch = tid & 15;
+    const V8 x = *reinterpret_cast<const V8*>(&qo[QROWS + toff<QD>(row, ch)]);
+    const V8 y = *reinterpret_cast<const V8*>(&ob[toff<QD>(row, ch)]);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += Elem<T>::to_float(x[k]) * Elem<T>::to_float(y[k]);
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 8);
+    if (ch == 0) ld[QR + row] = i * QR + row < s.len_q ? acc : 0.f;
+  };
+
+  // Mask: t = row + diag - key must lie in [0, W]; a key past the sequence
+  // is pushed out of reach through its lane term, and rows past the
+  // sequence carry LSE = +inf.
+  const unsigned trange = (unsigned)W;
+
+  // Phase 1 for this wave's keys: the 32 rows of q-step i in (qo, ld)
+  auto phase1 = [&](int i, const T* qo, const float* ld) {
+    const int j = my_j;
+    if (j < 0 || j >= nkt) return;
+    const T* sQ = qo;
+    const T* sdO = qo + QROWS;
+    const int kv0 = j * QK + 16 * wk;
+    const int key = kv0 + c;
+    const int tkey = key < s.len_kv ? g.diag - key : -(1 << 30);  // t = row + tkey
+    const int q0 = i * QR;
+    const int u0 = q0 + g.diag - kv0;  // t at (row q0, key kv0)
+    f32x4 S[2], dP[2];
+    bool live[2];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {  // 16-row block mb spans t in [um - 15, um + 15]
+      const int um = u0 + 16 * mb;
+      live[mb] = um + 15 >= 0 && um - 15 <= W;
+      S[mb] = dP[mb] = zero4;
+      if (!live[mb]) continue;
+#pragma unroll
+      for (int st = 0; st < QNS; ++st) {
+        S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * QD + rd_off[st]]), kB[st], S[mb]);
+        dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * QD + rd_off[st]]), vB[st], dP[mb]);
+      }
+    }
+    V8 pP, pS;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float pv[4] = {0.f, 0.f, 0.f, 0.f}, dsv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (live[mb]) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&ld[16 * mb + 4 * gq]);
+        const f32x4 del4 = *reinterpret_cast<const f32x4*>(&ld[QR + 16 * mb + 4 * gq]);
+        const int tb = q0 + 16 * mb + 4 * gq + tkey;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = S[mb][r] * p.scale_log2 - lse4[r];
+          asm("" : "+v"(x));
+          pv[r] = fast_exp2((unsigned)(tb + r) <= trange ? x : -INFINITY);
+          dsv[r] = pv[r] * (dP[mb][r] - del4[r]);
+        }
+      }
+      T sk[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sk[r] = Elem<T>::from_float(dsv[r]);
+        pP[mb * 4 + r] = Elem<T>::from_float(pv[r]);
+        pS[mb * 4 + r] = sk[r];
+      }
+      // dS^T [key][row] for the dQ of phase 2 (zeros where unseen)
+      *reinterpret_cast<u32x2*>(my_ds + 16 * mb) = __builtin_bit_cast(u32x2, sk);
+    }
+    if (!live[0] && !live[1]) return;
+    // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows
+#pragma unroll
+    for (int db = 0; db < QNDB; ++db) {
+      dV[db] = mfma16(trpair(&sdO[tr_off[db]], &sdO[16 * QD + tr_off[db]]), pP, dV[db]);
+      dK[db] = mfma16(trpair(&sQ[tr_off[db]], &sQ[16 * QD + tr_off[db]]), pS, dK[db]);
+    }
+  };
+
+  // Phase 2: dQ^T of rows 16 rb .. + 15 of q-step i, head h, head-dim
+  // columns 32 dq4 .. + 31, over the ring's tiles that see the rows
+  const int rb = w & 1, dq4 = w >> 1;
+  const int tr_dq[2] = {troff<QD>(c, gq, 2 * dq4), troff<QD>(c, gq, 2 * dq4 + 1)};  // (dq4 varies by wave)
+  auto phase2_dq = [&](int i, int h) {
+    const int q0 = i * QR;
+    f32x4 dQt[2];
+    dQt[0] = dQt[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < QSLOT; ++m) {
+      const int j = slot_tile(m, i);
+      if (j < 0 || j >= nkt) continue;
+      // keys 32 j .. + 31 against rows q0 + 16 rb .. + 15: t in [u - 31, u + 15]
+      const int u = q0 + 16 * rb + g.diag - j * QK;
+      if (u + 15 < 0 || u - 31 > W) continue;
+      const T* dsb = sdSt + m * QK * DSP + 16 * rb + ds_rd;
+      const V8 as = trpair(dsb, dsb + 16 * DSP);
+      const T* kt = sK + m * QK * QD;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        dQt[e] = mfma16(trpair(&kt[tr_dq[e]], &kt[16 * QD + tr_dq[e]]), as, dQt[e]);
+    }
+    const int row = q0 + 16 * rb + c;
+    if (row < s.cap_q) {
+      T* dqr = static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, h, row) + 32 * dq4 + 4 * gq;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        T x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = Elem<T>::from_float(p.scale * dQt[e][r]);
+        *reinterpret_cast<u32x2*>(dqr + 16 * e) = __builtin_bit_cast(u32x2, x);
+      }
+    }
+  };
+
+  // ---- kv-tiles no chunk's ring holds: zeros ----------------------------------
+  {
+    const int jhi = chunk == 0 ? min(max(dq - 3, 0), nkt) : 0;     // before the first window
+    const int klo = i1 == nqt ? min(max(nqt + dq, 0), nkt) : nkt;  // after the last
+    for (int pass = 0; pass < 2; ++pass) {
+      const int r0 = (pass == 0 ? 0 : klo) * QK;
+      const int r1 = min((pass == 0 ? jhi : nkt) * QK, s.cap_kv);
+      for (int e = tid; e < (r1 - r0) * QCH; e += QTHR) {
+        const int key = r0 + e / QCH, ch = e % QCH;
+        st8(static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, hk, key) + 8 * ch, zero8);
+        st8(static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, hk, key) + 8 * ch, zero8);
+      }
+    }
+  }
+
+  // ---- prologue: the ring of q-step i0 and the rows of the first two steps ----
+  int ci = i0, cg = 0;  // the current step
+  auto next_of = [&](int& i, int& gg) {
+    if (++gg == G) {
+      gg = 0;
+      ++i;
+    }
+  };
+  load_keys(slot_tile(slot, i0));
+  store_k_rows();
+  stream_rows(i0, hk * G, sQO0, sO0);
+  const float lse0 = w == 0 ? load_lse(i0, hk * G) : 0.f;
+  float nlse = 0.f;  // wave 0: the LSE of the next step's rows
+  {
+    int i = i0, gg = 0;
+    next_of(i, gg);
+    if (i < i1) {
+      stream_rows(i, hk * G + gg, sQO1, sO1);
+      if (w == 0) nlse = load_lse(i, hk * G + gg);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  store_lse(i0, lse0, sLD0);
+  form_delta(i0, sQO0, sO0, sLD0);
+
+  // One step: rows of (q-step ci, head hk G + cg) in buffer c; the next
+  // step's rows have been streaming into buffer n, and the one after that
+  // starts streaming into buffer nn.  False after the chunk's last step.
+  auto step = [&](const T* cqo, const float* cld, const T* nqo, const T* nob, float* nld, T* nnqo,
+                  T* nnob) -> bool {
+    int ni = ci, ng = cg;
+    next_of(ni, ng);
+    int ai = ni, ag = ng;
+    next_of(ai, ag);
+    const bool more = ni < i1, more2 = ai < i1;
+    const int so = (ci + dq - 3) & 3;  // the oldest slot: its kv-tile leaves after this q-step
+    __syncthreads();  // T: this step's rows and statistics are in; phase 2 of the last step is done
+    if (cg == 0 && ci > i0 && slot == ((ci + dq) & 3)) store_k_rows();  // the slot entering at ci
+    phase1(ci, cqo, cld);
+    // this wave's pieces of step s + 1 (issued before the last step's at
+    // most two dQ stores) have landed
+    __builtin_amdgcn_s_waitcnt(kWaitVm2);
+    __syncthreads();  // A: dS^T complete; everyone's rows of step s + 1 are in
+    if (more) store_lse(ni, nlse, nld);
+    if (slot == so && ng == 0) {  // the last head of q-step ci: this slot's kv-tile is done
+      retire();
+      if (more) load_keys(ni + dq);
+    }
+    if (more2) {
+      stream_rows(ai, hk * G + ag, nnqo, nnob);
+      if (w == 0) nlse = load_lse(ai, hk * G + ag);
+    }
+    if (more) form_delta(ni, nqo, nob, nld);
+    phase2_dq(ci, hk * G + cg);
+    ci = ni;
+    cg = ng;
+    return more;
+  };
+  while (step(sQO0, sLD0, sQO1, sO1, sLD1, sQO2, sO2) && step(sQO1, sLD1, sQO2, sO2, sLD2, sQO0, sO0) &&
+         step(sQO2, sLD2, sQO0, sO0, sLD0, sQO1, sO1)) {
+  }
+  // the three newer slots of the last q-step still hold kv-tiles
+  if (slot != ((i1 - 1 + dq - 3) & 3)) retire();
+}
+
+// The kv-tiles two neighbouring chunks share: dK = scale (earlier + later),
+// dV = earlier + later, in that order.  One block per (sequence, kv head,
+// chunk boundary, tile).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_qstream_fix_kernel(BwdArgs a) {
+  const Problem& p = a.p;
+  const int nch = p.qs_nch, C = p.qs_chunk;
+  int L = blockIdx.x;
+  const int t = L % 3;
+  L /= 3;
+  const int k = L % (nch - 1) + 1, bh = L / (nch - 1);
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const Seq s = load_seq(p, b);
+  SeqSched g;
+  g.init(s.len_q, s.len_kv, p.bottom_right, 1, p.window, 0, QR, QK);
+  const int j = k * C + g.diag / QK - 3 + t;
+  if (j < 0 || j >= g.n_kv_tiles) return;
+  const int lo = g.q_lo(j), hi = lo + g.n_iters(j);
+  if (!(lo < k * C && k * C < hi)) return;
+  const float* e0 = a.dq_acc + ((((int64_t)bh * nch + k) * 3 + t) * 2 + 0) * QPART;
+  const float* e1 = e0 + QPART;
+  for (int e = threadIdx.x; e < QPART / 4; e += kThreads) {
+    const int key = j * QK + e / (2 * QD / 4), col = (e % (2 * QD / 4)) * 4;
+    if (key >= s.cap_kv) continue;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(e0 + 4 * e);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(e1 + 4 * e);
+    const bool isk = col < QD;
+    const float f = isk ? p.scale : 1.f;
+    T v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = Elem<T>::from_float(f * (x[r] + y[r]));
+    T* out = isk ? static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, hk, key) + col
+                 : static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, hk, key) + (col - QD);
+    *reinterpret_cast<u32x2*>(out) = __builtin_bit_cast(u32x2, v);
+  }
+}
+
+hipError_t launch_bwd_qstream(const BwdArgs& a, hipStream_t st) {
+  const int n = a.p.B * a.p.Hkv * a.p.qs_nch;
+  if (n == 0) return hipSuccess;
+  if (a.dtype == 0)
+    hipLaunchKernelGGL((bwd_qstream_kernel<__bf16>), dim3(n), dim3(QTHR), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_qstream_kernel<_Float16>), dim3(n), dim3(QTHR), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.p.qs_nch < 2) return e;
+  const int nf = a.p.B * a.p.Hkv * (a.p.qs_nch - 1) * 3;
+  if (a.dtype == 0)
+    hipLaunchKernelGGL((bwd_qstream_fix_kernel<__bf16>), dim3(nf), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_qstream_fix_kernel<_Float16>), dim3(nf), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace swa

@@ -44,12 +44,15 @@
 //
 // LDS tiles of Q, dO and K are 64 elements (128 bytes) per row, unpadded,
 // with the 16-byte chunks of row r permuted by XOR with (r mod 8).
-// Measured on gfx950 (SQ_LDS_BANK_CONFLICT): 16-byte row reads are
-// conflict-free in any layout, and this permutation also makes the
-// transposed reads conflict-free (a plain 128-byte pitch costs 4x).  Band
-// rows are 208 elements apart (416 bytes), each group of 4 rows 8 bytes
-// further than the one before: the dS^T writes and the transposed reads
-// of the bands are then conflict-free as well (see band_wr).
+// Measured on gfx950 (SQ_LDS_BANK_CONFLICT, one access pattern at a time):
+// 16-byte row reads are conflict-free in any layout, and this permutation
+// also makes the transposed reads conflict-free (a plain 128-byte pitch
+// costs 4x).  Band rows are 208 elements apart (416 bytes), each group of 4
+// rows 8 bytes further than the one before, which takes the dS^T writes
+// from 4-way to conflict-free (see band_wr).  The whole kernel still
+// records about 2.6M conflict cycles per launch at batch 2, 16 heads,
+// S = 32768 (about 5% of its LDS instruction cycles); which accesses they
+// come from is not pinned down.
 // Transposed operands use ds_read_b64_tr_b16: within each 16-lane group,
 // lane i receives element (i % 4) of lanes i / 4 + 4e (e = 0..3), so a lane
 // pointing at row r0 + i / 4, column c0 + 4 (i % 4) receives rows

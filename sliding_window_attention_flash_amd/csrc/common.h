@@ -52,6 +52,11 @@ struct Problem {
   int step_kv;
   int chunk;
   int n_chunks;
+  // q-major streaming kernel (see bwd_qstream): q-tiles per chunk and
+  // chunks per (sequence, kv head)
+  int qstream;
+  int qs_chunk;
+  int qs_nch;
 };
 
 // One sequence (or dense batch entry): valid lengths, slot capacities,

@@ -52,6 +52,7 @@ hipError_t launch_bwd_clear(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_stream(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_qstream(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dsink(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 

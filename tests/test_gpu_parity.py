@@ -94,6 +94,42 @@ def test_forced_engines_full_oracle(w, engine):
     compare_full(w, inp, out, check_fwd=engine == 1)
 
 
+# engine 5, the q-major streaming kernel (head_dim 128, causal, W <= 96, dense,
+# diag a multiple of 32, no sink): GQA and MHA, both anchors, windows from 0
+# to 96, ragged lengths, a tail of keys no row sees (top-left, S_kv > S_q),
+# and enough 32-row steps that chunks meet (the plan's chunks are at least
+# 8 steps long)
+QSTREAM_CASES = [
+    _wl("qs_gqa8_br_w96_s700", BF16, 1, 8, 1, 128, 700, 700, bottom_right=True, window_left=96),
+    _wl("qs_mha_tl_w96_s300", BF16, 1, 2, 2, 128, 300, 300, window_left=96),
+    _wl("qs_gqa4_br_w64_s1000x1096_f16", F16, 2, 8, 2, 128, 1000, 1096, bottom_right=True, window_left=64),
+    _wl("qs_gqa2_tl_w0_s500", BF16, 1, 4, 2, 128, 500, 500, window_left=0),
+    _wl("qs_gqa2_tl_w33_s450x700", BF16, 1, 4, 2, 128, 450, 700, window_left=33),
+    _wl("qs_mha_br_w96_s2000", BF16, 1, 2, 2, 128, 2000, 2000, bottom_right=True, window_left=96),
+    _wl("qs_gqa8_br_w96_s1200x1264_f16", F16, 2, 16, 2, 128, 1200, 1264, bottom_right=True, window_left=96),
+    _wl("qs_gqa3_tl_w17_s900", BF16, 3, 6, 2, 128, 900, 900, window_left=17),
+]
+
+
+@pytest.mark.parametrize("det", [0, 1])
+@pytest.mark.parametrize("w", QSTREAM_CASES, ids=[w.name for w in QSTREAM_CASES])
+def test_qstream_engine_full_oracle(w, det):
+    say(f"case {w.name} engine=5 det={det}")
+    inp, out, _ = run_gpu(w, seed=11, deterministic=det, engine=5)
+    assert out["expiries"] == 0
+    compare_full(w, inp, out, check_fwd=False)
+
+
+def test_qstream_engine_bitwise_repeatable():
+    # every sum in a fixed order: dQ inside one step, dK / dV in registers over
+    # the chunk's steps, the two sides of a shared kv-tile added in turn
+    w = QSTREAM_CASES[-2]
+    say(f"case {w.name} engine=5: 3 runs")
+    _, outs, _ = run_gpu(w, seed=29, deterministic=1, runs=3, engine=5)
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(outs[0][key], outs[1][key]) and torch.equal(outs[0][key], outs[2][key]), key
+
+
 def _thd_small(sink=True, dtype=F16, D=64, hkv=2, wr=0):
     # one sequence with no query rows and one with no keys, slots padded
     lq = (70, 0, 130, 5, 64, 600)
@@ -228,12 +264,15 @@ def test_c3_s32768_relay_bitwise_and_full_oracle_both_modes():
         assert_close(f"{key} det/at", outs[0][key].float(), at[key].float())
 
 
-def test_c4_gqa_s16484_whole_batch_entries_full_oracle():
-    w = CONFIGS["c4"]
-    say(f"case {w.name}: batch entries 0 and 11 (all 48 heads, all rows) against the full oracle")
-    inp, out, _ = run_gpu(w, seed=24)
+@pytest.mark.parametrize("engine", [3, 5])
+def test_c4_gqa_s16484_whole_batch_entries_full_oracle(engine):
+    # both engines that apply: the per-tile kernels with the q-major dQ pass,
+    # and the q-major streaming kernel
+    w = CONFIGS["c4"].with_(engine=engine)
+    say(f"case {w.name} engine={engine}: batch entries 0 and 11 (all 48 heads, all rows) against the full oracle")
+    inp, out, _ = run_gpu(w, seed=24, engine=engine)
     ws, inp2, out2 = batch_entries(w, inp, out, [0, w.batch - 1])
-    compare_full(ws, inp2, out2)
+    compare_full(ws, inp2, out2, check_fwd=engine == 3)
     # every entry: no element left unwritten
     for name in ("dq", "dk", "dv"):
         assert not torch.isnan(out[name]).any(), f"{name}: NaN somewhere in the full output"

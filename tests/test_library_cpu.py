@@ -361,7 +361,12 @@ def test_noalloc_rejects_a_workspace_beyond_its_scratch(lib):
 
 
 @pytest.mark.parametrize("kw,status,needle", [
-    (dict(engine=5), _lib.SDPA_ERR_INVALID_ARG, "engine 5"),
+    (dict(engine=6), _lib.SDPA_ERR_INVALID_ARG, "engine 6"),
+    (dict(engine=5), _lib.SDPA_ERR_UNSUPPORTED, "q-major streaming kernel"),
+    (dict(engine=5, D=128, window_left=100), _lib.SDPA_ERR_UNSUPPORTED, "q-major streaming kernel"),
+    (dict(engine=5, D=128, window_right=3), _lib.SDPA_ERR_UNSUPPORTED, "q-major streaming kernel"),
+    (dict(engine=5, D=128, bottom_right=True, Skv=316), _lib.SDPA_ERR_UNSUPPORTED, "q-major streaming kernel"),
+    (dict(engine=5, D=128, deterministic=2), _lib.SDPA_ERR_INVALID_ARG, "per-kv-tile relay"),
     (dict(engine=1, Hkv=2), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
     (dict(engine=2, Hkv=4, window_left=200), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
     (dict(engine=2, Hkv=4, D=128), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
