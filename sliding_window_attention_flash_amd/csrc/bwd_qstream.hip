@@ -16,7 +16,7 @@
 //
 // Waves: wave w owns keys 16 (w % 2) .. + 15 of ring slot w / 2 (slot of
 // kv-tile j: j mod 4).  A step s (q-step i, head h), with its Q / dO / O
-// rows already in LDS buffer s mod 3:
+// rows already in LDS buffer s mod 4:
 //   T  barrier; at a q-step's first head the slot entering the ring stores
 //      its K rows to LDS.
 //   1  every wave, for its 16 keys and the 32 rows: S = Q K^T, dP = dO V^T,
@@ -24,10 +24,11 @@
 //      dK^T += Q^T dS, dS^T to LDS.
 //   A  this wave's loads for step s + 1 have landed; barrier.
 //   2  after a q-step's last head the oldest slot's waves retire their
-//      kv-tile and load the entering one; every wave starts the loads of
-//      step s + 2 (straight into LDS buffer (s + 2) mod 3), forms delta of
-//      step s + 1's rows, and computes and stores 16 rows x 32 head-dim
-//      columns of dQ.
+//      kv-tile and load the entering one; every wave forms delta of step
+//      s + 1's rows, computes and stores 16 rows x 32 head-dim columns of
+//      dQ, and last starts the loads of step s + 3 (straight into LDS buffer
+//      (s + 3) mod 4), so that they are the only ones the wait before the
+//      next step's barrier A leaves in flight.
 // The kv-tiles a chunk shares with its neighbours leave as fp32 partial
 // sums; bwd_qstream_fix adds the two sides in a fixed order, so the whole
 // pass is bitwise repeatable.
@@ -56,9 +57,30 @@ constexpr int QROWS = QR * QD;       // elements of a step's Q (or dO, O) rows
 constexpr int DSP = QR + 8;          // dS^T row pitch (elements): 80 bytes
 constexpr int QPART = QK * 2 * QD;   // floats of one kv-tile's dK / dV partial
 constexpr int QPIECES = 3 * QROWS * 2 / 1024;  // 1 KB pieces of a step's Q, dO, O
-constexpr int kWaitVm2 = 0xF72;      // s_waitcnt vmcnt(2) (no LDS / export wait)
+constexpr int kWaitVm3 = 0xF73;      // s_waitcnt vmcnt(3) (no LDS / export wait)
+constexpr int kWaitVm0 = 0xF70;      // s_waitcnt vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;   // s_waitcnt lgkmcnt(0)
 
 static_assert(QPIECES % QWAVE == 0, "a step's rows stream in whole pieces per wave");
+static_assert(QPIECES / QWAVE == 3, "the wait before barrier A leaves one step's 3 pieces in flight");
+
+// A barrier for LDS only: this wave's LDS accesses are complete, then
+// s_barrier.  (__syncthreads also orders global memory, which here would
+// make every barrier wait for the rows streaming in for later steps.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+}
+
+// Sum over the 16 lanes of a row (DPP: swaps within quads, then the mirrors
+// of each half-row and of the row).
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
 static_assert(QSLOT * QK >= QR + 96, "the ring holds the keys of a q-step for W <= 96");
 
 }  // namespace
@@ -66,19 +88,22 @@ static_assert(QSLOT * QK >= QR + 96, "the ring holds the keys of a q-step for W 
 template <typename T>
 __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
-  // Per step buffer (three, used in turn; separately named, so that reading
+  // Per step buffer (four, used in turn; separately named, so that reading
   // one is no reason to wait for the loads streaming into another): Q then
   // dO rows, O rows, and row statistics (LSE in log2 units, then delta).
   // The ring's K tiles; dS^T [key][row].
   __shared__ __align__(16) T sQO0[2 * QROWS];
   __shared__ __align__(16) T sQO1[2 * QROWS];
   __shared__ __align__(16) T sQO2[2 * QROWS];
+  __shared__ __align__(16) T sQO3[2 * QROWS];
   __shared__ __align__(16) T sO0[QROWS];
   __shared__ __align__(16) T sO1[QROWS];
   __shared__ __align__(16) T sO2[QROWS];
+  __shared__ __align__(16) T sO3[QROWS];
   __shared__ __align__(16) float sLD0[2 * QR];
   __shared__ __align__(16) float sLD1[2 * QR];
   __shared__ __align__(16) float sLD2[2 * QR];
+  __shared__ __align__(16) float sLD3[2 * QR];
   __shared__ __align__(16) T sK[QSLOT * QK * QD];
   __shared__ __align__(16) T sdSt[QSLOT * QK * DSP];
 
@@ -212,10 +237,7 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc += Elem<T>::to_float(x[k]) * Elem<T>::to_float(y[k]);
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    acc += __shfl_xor(acc, 8);
+    acc = row16_sum(acc);
     if (ch == 0) ld[QR + row] = i * QR + row < s.len_q ? acc : 0.f;
   };
 
@@ -335,7 +357,7 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     }
   }
 
-  // ---- prologue: the ring of q-step i0 and the rows of the first two steps ----
+  // ---- prologue: the ring of q-step i0 and the rows of the first three steps ---
   int ci = i0, cg = 0;  // the current step
   auto next_of = [&](int& i, int& gg) {
     if (++gg == G) {
@@ -355,6 +377,8 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
       stream_rows(i, hk * G + gg, sQO1, sO1);
       if (w == 0) nlse = load_lse(i, hk * G + gg);
     }
+    next_of(i, gg);
+    if (i < i1) stream_rows(i, hk * G + gg, sQO2, sO2);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -362,43 +386,48 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   form_delta(i0, sQO0, sO0, sLD0);
 
   // One step: rows of (q-step ci, head hk G + cg) in buffer c; the next
-  // step's rows have been streaming into buffer n, and the one after that
-  // starts streaming into buffer nn.  False after the chunk's last step.
-  auto step = [&](const T* cqo, const float* cld, const T* nqo, const T* nob, float* nld, T* nnqo,
-                  T* nnob) -> bool {
+  // step's rows are in buffer n (landed by barrier A), and the rows of the
+  // step after the one after that start streaming into buffer n3 at the
+  // end.  False after the chunk's last step.
+  auto step = [&](const T* cqo, const float* cld, const T* nqo, const T* nob, float* nld, T* n3qo,
+                  T* n3ob) -> bool {
     int ni = ci, ng = cg;
     next_of(ni, ng);
-    int ai = ni, ag = ng;
+    int ai = ni, ag = ng;  // step s + 2 (its LSE), then s + 3 (its rows)
     next_of(ai, ag);
+    int bi = ai, bg = ag;
+    next_of(bi, bg);
     const bool more = ni < i1, more2 = ai < i1;
     const int so = (ci + dq - 3) & 3;  // the oldest slot: its kv-tile leaves after this q-step
-    __syncthreads();  // T: this step's rows and statistics are in; phase 2 of the last step is done
+    // Everything this wave issued but the last 3 loads of the previous step
+    // (the rows of step s + 2) has completed: the rows of step s + 1, its
+    // own K / V rows, stores and LSE loads.
+    __builtin_amdgcn_s_waitcnt(kWaitVm3);
+    lds_barrier();  // T: this step's statistics are in, phase 2 of the last step is done
     if (cg == 0 && ci > i0 && slot == ((ci + dq) & 3)) store_k_rows();  // the slot entering at ci
     phase1(ci, cqo, cld);
-    // this wave's pieces of step s + 1 (issued before the last step's at
-    // most two dQ stores) have landed
-    __builtin_amdgcn_s_waitcnt(kWaitVm2);
-    __syncthreads();  // A: dS^T complete; everyone's rows of step s + 1 are in
+    lds_barrier();  // A: dS^T complete; everyone's rows of step s + 1 are in (since T)
     if (more) store_lse(ni, nlse, nld);
+    if (more2 && w == 0) nlse = load_lse(ai, hk * G + ag);
     if (slot == so && ng == 0) {  // the last head of q-step ci: this slot's kv-tile is done
       retire();
       if (more) load_keys(ni + dq);
     }
-    if (more2) {
-      stream_rows(ai, hk * G + ag, nnqo, nnob);
-      if (w == 0) nlse = load_lse(ai, hk * G + ag);
-    }
     if (more) form_delta(ni, nqo, nob, nld);
     phase2_dq(ci, hk * G + cg);
+    // (past the chunk's end: a copy of in-range rows into the free buffer, so
+    // that every step ends with the same 3 loads in flight)
+    stream_rows(bi, hk * G + bg, n3qo, n3ob);
     ci = ni;
     cg = ng;
     return more;
   };
-  while (step(sQO0, sLD0, sQO1, sO1, sLD1, sQO2, sO2) && step(sQO1, sLD1, sQO2, sO2, sLD2, sQO0, sO0) &&
-         step(sQO2, sLD2, sQO0, sO0, sLD0, sQO1, sO1)) {
+  while (step(sQO0, sLD0, sQO1, sO1, sLD1, sQO3, sO3) && step(sQO1, sLD1, sQO2, sO2, sLD2, sQO0, sO0) &&
+         step(sQO2, sLD2, sQO3, sO3, sLD3, sQO1, sO1) && step(sQO3, sLD3, sQO0, sO0, sLD0, sQO2, sO2)) {
   }
   // the three newer slots of the last q-step still hold kv-tiles
   if (slot != ((i1 - 1 + dq - 3) & 3)) retire();
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no LDS write outlives the block
 }
 
 // The kv-tiles two neighbouring chunks share: dK = scale (earlier + later),
