@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -181,10 +182,22 @@ sdpa_status resolve_engine(const sdpa_attn_desc* d, int* engine) {
   // per-tile kernels by 24-50%; above, it wins by 15-30%.  Its chunk relay
   // ties or beats its fp32 atomics everywhere (within 1.5% at the largest
   // shape) and is repeatable, so it serves both deterministic 0 and 1.
+  //
+  // Head_dim 128 (the study's d128 family: causal, windows 32 / 96, groups of
+  // 8 and multi-head, 1 .. 72 (sequence, kv head) pairs, 1K .. 16K rows):
+  // the q-major streaming kernel takes about 3 us per 32-row step whatever
+  // the window, so it wins by 4-76% once the grid holds at least 512
+  // q-steps (B Hkv S_q / 32) and either the heads are not grouped or the
+  // window is 64 keys or more; with groups of 8 and a 32-key window the
+  // per-tile kernels are within 6% or ahead, and below 512 q-steps ahead by
+  // up to 35%.  Both are bitwise repeatable (deterministic 0 and 1).
   const int64_t q_rows =
       (d->layout == SDPA_LAYOUT_THD ? d->total_q : (int64_t)d->batch * d->seq_q) * (int64_t)d->heads_q;
+  const int64_t q_steps = (int64_t)d->batch * d->heads_kv * (((int64_t)d->seq_q + 31) / 32);
   if (d->deterministic == 2)
     *engine = ENGINE_TILE_RELAY;
+  else if (qstream_eligible(d) && q_steps >= 512 && (d->heads_q == d->heads_kv || d->window_left >= 64))
+    *engine = ENGINE_QSTREAM;
   else if (stream_ok && q_rows >= (int64_t(1) << 16))
     *engine = ENGINE_STREAM_RELAY;
   else
@@ -258,26 +271,29 @@ swa::Problem make_problem(const sdpa_attn_desc* d, int engine) {
   p.stream_delta = p.stream && !d->has_sink;
   p.qstream = engine == ENGINE_QSTREAM;
   if (p.qstream) {
-    // One 8-wave block per CU.  Chunks of consecutive 32-row q-steps per
-    // (sequence, kv head), at least 8 long, chosen so that the grid fills
-    // whole rounds of 256 CUs as closely as possible (fewer rounds on a tie).
+    // One 8-wave block per CU walks a chunk of consecutive 32-row q-steps of
+    // one (sequence, kv head), one step per query head of the group.  With
+    // r rounds of 256 CUs the chunks are ceil(nqt / floor(256 r / bh))
+    // q-steps long; pick r to minimize the estimated makespan r (C G + 6)
+    // in steps (6: a chunk's start-up and its boundary tiles, as measured on
+    // MI355X for G = 8 between chunks of 4 and 19 q-steps), chunks of at
+    // least 3 q-steps (so a 32-key tile, seen by at most 4 q-steps, is
+    // shared by at most two chunks); fewer rounds on a tie.
     const int64_t bh = (int64_t)d->batch * d->heads_kv, nqt = ((int64_t)d->seq_q + 31) / 32;
-    const int64_t n_cap = std::max<int64_t>(1, nqt / 8);
-    int best_n = 1;
-    double best_eff = 0.0;
-    for (int rounds = 1; rounds <= 16; ++rounds) {
-      const int64_t n0 = std::min(std::max<int64_t>(256 * (int64_t)rounds / bh, 1), n_cap);
+    const int64_t n_cap = std::max<int64_t>(1, nqt / 3);
+    int64_t best_c = nqt, best_cost = INT64_MAX;
+    for (int64_t rounds = 1; rounds <= 64; ++rounds) {
+      const int64_t n0 = std::min(std::max<int64_t>(256 * rounds / bh, 1), n_cap);
       const int64_t c = (nqt + n0 - 1) / n0, n = (nqt + c - 1) / c;
-      const int64_t blocks = bh * n;
-      const double eff = (double)blocks / (256.0 * (double)((blocks + 255) / 256));
-      if (eff > best_eff + 1e-9) {
-        best_eff = eff;
-        best_n = (int)n;
+      const int64_t cost = ((bh * n + 255) / 256) * (c * p.G + 6);
+      if (cost < best_cost) {
+        best_cost = cost;
+        best_c = c;
       }
       if (n0 == n_cap) break;
     }
-    p.qs_chunk = (int)((nqt + best_n - 1) / best_n);
-    p.qs_nch = (int)((nqt + p.qs_chunk - 1) / p.qs_chunk);
+    p.qs_chunk = (int)best_c;
+    p.qs_nch = (int)((nqt + best_c - 1) / best_c);
   }
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one
@@ -350,7 +366,7 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   pl->stat_rows = (int64_t)p.Hq * p.total_q;
   size_t off = 0;
   pl->off_delta = off;
-  off = align256(off + sizeof(float) * (size_t)pl->stat_rows);
+  if (!p.qstream) off = align256(off + sizeof(float) * (size_t)pl->stat_rows);  // (bwd_qstream keeps delta in LDS)
   pl->off_acc = off;
   if (p.qstream) {
     // the fp32 dK / dV partials of the 32-key tiles neighbouring chunks
@@ -511,18 +527,19 @@ sdpa_status sdpa_bwd_schedule(const sdpa_bwd_plan_t* pl, int32_t len_q, int32_t 
   if (!pl) return fail(SDPA_ERR_INVALID_ARG, "plan is NULL");
   if (len_q < 0 || len_kv < 0) return fail(SDPA_ERR_INVALID_ARG, "len_q %d / len_kv %d must be >= 0", len_q, len_kv);
   // The streaming kernel evaluates its schedule in the shift form of
-  // StreamSched with the plan's window; the per-tile kernels use SeqSched.
-  // Reporting what each kernel itself computes lets host tests check the
-  // form that runs.
-  const int tkv = pl->prob.step_kv;
+  // StreamSched with the plan's window; the per-tile kernels use SeqSched,
+  // and so does the q-major streaming kernel, on 32-row q-steps and 32-key
+  // tiles.  Reporting what each kernel itself computes lets host tests check
+  // the form that runs.
+  const int tq = pl->prob.qstream ? 32 : kTile, tkv = pl->prob.qstream ? 32 : pl->prob.step_kv;
   swa::SeqSched g;
   g.init(len_q, len_kv, pl->desc.bottom_right, pl->desc.causal, clamp_band(pl->desc.window_left, len_q, len_kv),
-         clamp_band(pl->desc.window_right, len_q, len_kv), kTile, tkv);
+         clamp_band(pl->desc.window_right, len_q, len_kv), tq, tkv);
   swa::StreamSched gs;
   gs.init(len_q, len_kv, pl->desc.bottom_right, pl->prob.window);
   const bool stream = pl->prob.stream;
   const int nq = stream ? gs.n_q_tiles : g.n_q_tiles, nk = stream ? gs.n_kv_tiles : g.n_kv_tiles;
-  if (tile_q) *tile_q = kTile;
+  if (tile_q) *tile_q = tq;
   if (tile_kv) *tile_kv = tkv;
   if (n_q) *n_q = nq;
   if (n_kv) *n_kv = nk;

@@ -98,7 +98,7 @@ def test_forced_engines_full_oracle(w, engine):
 # diag a multiple of 32, no sink): GQA and MHA, both anchors, windows from 0
 # to 96, ragged lengths, a tail of keys no row sees (top-left, S_kv > S_q),
 # and enough 32-row steps that chunks meet (the plan's chunks are at least
-# 8 steps long)
+# 3 steps long: 9 steps make three chunks of exactly 3)
 QSTREAM_CASES = [
     _wl("qs_gqa8_br_w96_s700", BF16, 1, 8, 1, 128, 700, 700, bottom_right=True, window_left=96),
     _wl("qs_mha_tl_w96_s300", BF16, 1, 2, 2, 128, 300, 300, window_left=96),
@@ -108,6 +108,7 @@ QSTREAM_CASES = [
     _wl("qs_mha_br_w96_s2000", BF16, 1, 2, 2, 128, 2000, 2000, bottom_right=True, window_left=96),
     _wl("qs_gqa8_br_w96_s1200x1264_f16", F16, 2, 16, 2, 128, 1200, 1264, bottom_right=True, window_left=96),
     _wl("qs_gqa3_tl_w17_s900", BF16, 3, 6, 2, 128, 900, 900, window_left=17),
+    _wl("qs_gqa4_br_w96_s288x352", BF16, 1, 4, 1, 128, 288, 352, bottom_right=True, window_left=96),
 ]
 
 

@@ -394,6 +394,56 @@ def test_forced_engine_sets_the_schedule_and_workspace(lib, engine, det, tile_kv
     assert plan.workspace_bytes == _sections(4 * rows, acc, stash, 4 * B * H * ntq, 16, 4 * H * B * ntq)
 
 
+def _qstream_chunks(B, Hkv, G, S):
+    # the plan's chunking for the q-major streaming kernel, restated: r
+    # rounds of 256 blocks, chunks of ceil(nqt / floor(256 r / (B Hkv)))
+    # 32-row steps (at least 3), least r (C G + 6), fewer rounds on a tie
+    bh, nqt = B * Hkv, (S + 31) // 32
+    n_cap = max(1, nqt // 3)
+    best_c, best_cost = nqt, None
+    for r in range(1, 65):
+        n0 = min(max(256 * r // bh, 1), n_cap)
+        c = -(-nqt // n0)
+        n = -(-nqt // c)
+        cost = -(-bh * n // 256) * (c * G + 6)
+        if best_cost is None or cost < best_cost:
+            best_c, best_cost = c, cost
+        if n0 == n_cap:
+            break
+    return -(-nqt // best_c)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv", [(2, 8, 2, 1000, 1064), (1, 2, 2, 300, 300), (12, 48, 6, 16484, 16484),
+                                           (1, 8, 1, 16384, 16384)])
+def test_forced_engine_5_schedule_and_workspace(lib, B, Hq, Hkv, Sq, Skv):
+    # q-major streaming kernel: 32-row q-steps and 32-key tiles; workspace:
+    # no delta rows (formed in LDS), the fp32 dK / dV partials of the three
+    # kv-tiles at each chunk boundary (both sides), then the common sections
+    D = 128
+    plan = api.sdpa_bwd_plan(_desc(B=B, Hq=Hq, Hkv=Hkv, D=D, Sq=Sq, Skv=Skv, window_left=96, bottom_right=True,
+                                   engine=5, deterministic=1))
+    s = api.sdpa_bwd_schedule(plan, Sq, Skv)
+    assert (s["tile_q"], s["tile_kv"]) == (32, 32)
+    nch = _qstream_chunks(B, Hkv, Hq // Hkv, Sq)
+    ntq = -(-Sq // 64)
+    part = 4 * B * Hkv * nch * 6 * 32 * 2 * D
+    assert plan.workspace_bytes == _sections(0, part, 0, 4 * B * Hq * ntq, 16, 4 * Hq * B * ntq)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,W,det,qstream", [
+    (2, 16, 2, 4096, 96, 0, True),    # GQA 8, 512 q-steps, window 96: the q-major streaming kernel
+    (2, 16, 2, 4096, 96, 1, True),    # repeatable, so deterministic 1 too
+    (2, 16, 2, 4064, 96, 0, False),   # 508 q-steps: the per-tile kernels
+    (2, 16, 2, 4096, 32, 0, False),   # GQA 8 with a 32-key window: the per-tile kernels
+    (2, 16, 16, 1024, 32, 0, True),   # multi-head: any window
+    (2, 16, 2, 4096, 100, 0, False),  # window beyond 96: not eligible
+    (2, 16, 2, 4096, 96, 2, False),   # deterministic 2: the per-kv-tile relay
+])
+def test_default_engine_d128_follows_the_measured_table(lib, B, Hq, Hkv, S, W, det, qstream):
+    plan = api.sdpa_bwd_plan(_desc(B=B, Hq=Hq, Hkv=Hkv, D=128, Sq=S, Skv=S, window_left=W, deterministic=det))
+    assert (api.sdpa_bwd_schedule(plan, S, S)["tile_q"] == 32) == qstream
+
+
 @pytest.mark.parametrize("B,H,S,det,stream", [
     (2, 16, 32768, 1, True),    # 2^20 query rows: the streaming kernel (chunk relay)
     (2, 16, 32768, 0, True),    # unordered too: the chunk relay ties or beats the atomics

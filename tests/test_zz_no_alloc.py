@@ -18,6 +18,8 @@ BF16, F16 = torch.bfloat16, torch.float16
 SEQUENCE = [
     (Workload("na_stream_relay_b2_h8_s4096_w128", BF16, 2, 8, 8, 64, 4096, 4096, window_left=128,
               scale=0.125, engine=2), 1),
+    (Workload("na_qstream_gqa_br_w96_d128", BF16, 2, 8, 2, 128, 1000, 1064, bottom_right=True, window_left=96,
+              engine=5), 1),
     (Workload("na_stream_atomic_b2_h4_s2048_w128", BF16, 2, 4, 4, 64, 2048, 2048, window_left=128,
               scale=0.125, engine=1), 0),
     (Workload("na_tile_relay_gqa_br_w100_d128", BF16, 1, 8, 2, 128, 500, 700, bottom_right=True,
