@@ -17,18 +17,19 @@
 // Waves: wave w owns keys 16 (w % 2) .. + 15 of ring slot w / 2 (slot of
 // kv-tile j: j mod 4).  A step s (q-step i, head h), with its Q / dO / O
 // rows already in LDS buffer s mod 4:
-//   T  barrier; at a q-step's first head the slot entering the ring stores
-//      its K rows to LDS.
+//   T  this wave's loads of step s + 1's rows have landed; barrier; at a
+//      q-step's first head the slot entering the ring stores its K rows to
+//      LDS.
 //   1  every wave, for its 16 keys and the 32 rows: S = Q K^T, dP = dO V^T,
 //      P = exp2(S c - LSE), dS = P (dP - delta) (masked), dV^T += dO^T P,
 //      dK^T += Q^T dS, dS^T to LDS.
-//   A  this wave's loads for step s + 1 have landed; barrier.
+//   A  barrier: dS^T complete.
 //   2  after a q-step's last head the oldest slot's waves retire their
 //      kv-tile and load the entering one; every wave forms delta of step
-//      s + 1's rows, computes and stores 16 rows x 32 head-dim columns of
-//      dQ, and last starts the loads of step s + 3 (straight into LDS buffer
-//      (s + 3) mod 4), so that they are the only ones the wait before the
-//      next step's barrier A leaves in flight.
+//      s + 1's rows, computes 16 rows x 32 head-dim columns of dQ, starts
+//      the loads of step s + 3 (straight into LDS buffer (s + 3) mod 4) and
+//      last stores its dQ, so that those loads and stores are the only
+//      operations the wait before the next barrier T leaves in flight.
 // The kv-tiles a chunk shares with its neighbours leave as fp32 partial
 // sums; bwd_qstream_fix adds the two sides in a fixed order, so the whole
 // pass is bitwise repeatable.
@@ -57,12 +58,12 @@ constexpr int QROWS = QR * QD;       // elements of a step's Q (or dO, O) rows
 constexpr int DSP = QR + 8;          // dS^T row pitch (elements): 80 bytes
 constexpr int QPART = QK * 2 * QD;   // floats of one kv-tile's dK / dV partial
 constexpr int QPIECES = 3 * QROWS * 2 / 1024;  // 1 KB pieces of a step's Q, dO, O
-constexpr int kWaitVm3 = 0xF73;      // s_waitcnt vmcnt(3) (no LDS / export wait)
+constexpr int kWaitVm5 = 0xF75;      // s_waitcnt vmcnt(5) (no LDS / export wait)
 constexpr int kWaitVm0 = 0xF70;      // s_waitcnt vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;   // s_waitcnt lgkmcnt(0)
 
 static_assert(QPIECES % QWAVE == 0, "a step's rows stream in whole pieces per wave");
-static_assert(QPIECES / QWAVE == 3, "the wait before barrier A leaves one step's 3 pieces in flight");
+static_assert(QPIECES / QWAVE == 3, "the wait at a step's top leaves the last step's 3 pieces and 2 stores in flight");
 
 // A barrier for LDS only: this wave's LDS accesses are complete, then
 // s_barrier.  (__syncthreads also orders global memory, which here would
@@ -311,9 +312,8 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   // columns 32 dq4 .. + 31, over the ring's tiles that see the rows
   const int rb = w & 1, dq4 = w >> 1;
   const int tr_dq[2] = {troff<QD>(c, gq, 2 * dq4), troff<QD>(c, gq, 2 * dq4 + 1)};  // (dq4 varies by wave)
-  auto phase2_dq = [&](int i, int h) {
+  auto phase2_dq = [&](int i, f32x4 (&dQt)[2]) {
     const int q0 = i * QR;
-    f32x4 dQt[2];
     dQt[0] = dQt[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < QSLOT; ++m) {
@@ -329,16 +329,20 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
       for (int e = 0; e < 2; ++e)
         dQt[e] = mfma16(trpair(&kt[tr_dq[e]], &kt[16 * QD + tr_dq[e]]), as, dQt[e]);
     }
-    const int row = q0 + 16 * rb + c;
-    if (row < s.cap_q) {
-      T* dqr = static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, h, row) + 32 * dq4 + 4 * gq;
+  };
+  // The two stores of every lane are issued whatever the row (rows past the
+  // sequence's slots write into the never-used partial slot of chunk 0), so
+  // every step ends with the same loads and stores in flight.
+  auto store_dq = [&](int i, int h, const f32x4 (&dQt)[2]) {
+    const int row = i * QR + 16 * rb + c;
+    T* dqr = (row < s.cap_q ? static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, h, row)
+                            : reinterpret_cast<T*>(a.dq_acc)) + 32 * dq4 + 4 * gq;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        T x[4];
+    for (int e = 0; e < 2; ++e) {
+      T x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = Elem<T>::from_float(p.scale * dQt[e][r]);
-        *reinterpret_cast<u32x2*>(dqr + 16 * e) = __builtin_bit_cast(u32x2, x);
-      }
+      for (int r = 0; r < 4; ++r) x[r] = Elem<T>::from_float(p.scale * dQt[e][r]);
+      *reinterpret_cast<u32x2*>(dqr + 16 * e) = __builtin_bit_cast(u32x2, x);
     }
   };
 
@@ -399,10 +403,11 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     next_of(bi, bg);
     const bool more = ni < i1, more2 = ai < i1;
     const int so = (ci + dq - 3) & 3;  // the oldest slot: its kv-tile leaves after this q-step
-    // Everything this wave issued but the last 3 loads of the previous step
-    // (the rows of step s + 2) has completed: the rows of step s + 1, its
-    // own K / V rows, stores and LSE loads.
-    __builtin_amdgcn_s_waitcnt(kWaitVm3);
+    // Everything this wave issued but the last 5 operations of the previous
+    // step (the 3 loads of the rows of step s + 2, then its 2 dQ stores) has
+    // completed: the rows of step s + 1, its own K / V rows, the earlier
+    // stores and the LSE loads.
+    __builtin_amdgcn_s_waitcnt(kWaitVm5);
     lds_barrier();  // T: this step's statistics are in, phase 2 of the last step is done
     if (cg == 0 && ci > i0 && slot == ((ci + dq) & 3)) store_k_rows();  // the slot entering at ci
     phase1(ci, cqo, cld);
@@ -414,10 +419,12 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
       if (more) load_keys(ni + dq);
     }
     if (more) form_delta(ni, nqo, nob, nld);
-    phase2_dq(ci, hk * G + cg);
+    f32x4 dQt[2];
+    phase2_dq(ci, dQt);
     // (past the chunk's end: a copy of in-range rows into the free buffer, so
     // that every step ends with the same 3 loads in flight)
     stream_rows(bi, hk * G + bg, n3qo, n3ob);
+    store_dq(ci, hk * G + cg, dQt);
     ci = ni;
     cg = ng;
     return more;
