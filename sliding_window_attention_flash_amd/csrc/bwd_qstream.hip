@@ -250,7 +250,12 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   // Phase 1 for this wave's keys: the 32 rows of q-step i in (qo, ld)
   auto phase1 = [&](int i, const T* qo, const float* ld) {
     const int j = my_j;
-    if (j < 0 || j >= nkt) return;
+    if (j < 0 || j >= nkt) {  // a hole: its dS^T is zero (phase 2 reads every slot)
+      const u32x2 z = {0u, 0u};
+      *reinterpret_cast<u32x2*>(my_ds) = z;
+      *reinterpret_cast<u32x2*>(my_ds + 16) = z;
+      return;
+    }
     const T* sQ = qo;
     const T* sdO = qo + QROWS;
     const int kv0 = j * QK + 16 * wk;
@@ -312,22 +317,25 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   // columns 32 dq4 .. + 31, over the ring's tiles that see the rows
   const int rb = w & 1, dq4 = w >> 1;
   const int tr_dq[2] = {troff<QD>(c, gq, 2 * dq4), troff<QD>(c, gq, 2 * dq4 + 1)};  // (dq4 varies by wave)
-  auto phase2_dq = [&](int i, f32x4 (&dQt)[2]) {
-    const int q0 = i * QR;
+  auto phase2_dq = [&](f32x4 (&dQt)[2]) {
     dQt[0] = dQt[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < QSLOT; ++m) {
-      const int j = slot_tile(m, i);
-      if (j < 0 || j >= nkt) continue;
-      // keys 32 j .. + 31 against rows q0 + 16 rb .. + 15: t in [u - 31, u + 15]
-      const int u = q0 + 16 * rb + g.diag - j * QK;
-      if (u + 15 < 0 || u - 31 > W) continue;
+    // every slot (its dS^T is zero where its keys do not see these rows, and
+    // a hole's K rows are zeros); slot m + 1's operands are read while slot
+    // m's products run
+    V8 as[2], ak[2][2];
+    auto read = [&](int m, int x) {
       const T* dsb = sdSt + m * QK * DSP + 16 * rb + ds_rd;
-      const V8 as = trpair(dsb, dsb + 16 * DSP);
+      as[x] = trpair(dsb, dsb + 16 * DSP);
       const T* kt = sK + m * QK * QD;
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        dQt[e] = mfma16(trpair(&kt[tr_dq[e]], &kt[16 * QD + tr_dq[e]]), as, dQt[e]);
+      for (int e = 0; e < 2; ++e) ak[x][e] = trpair(&kt[tr_dq[e]], &kt[16 * QD + tr_dq[e]]);
+    };
+    read(0, 0);
+#pragma unroll
+    for (int m = 0; m < QSLOT; ++m) {
+      if (m + 1 < QSLOT) read(m + 1, (m + 1) & 1);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) dQt[e] = mfma16(ak[m & 1][e], as[m & 1], dQt[e]);
     }
   };
   // The two stores of every lane are issued whatever the row (rows past the
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     }
     if (more) form_delta(ni, nqo, nob, nld);
     f32x4 dQt[2];
-    phase2_dq(ci, dQt);
+    phase2_dq(dQt);
     // (past the chunk's end: a copy of in-range rows into the free buffer, so
     // that every step ends with the same 3 loads in flight)
     stream_rows(bi, hk * G + bg, n3qo, n3ob);
