@@ -142,7 +142,12 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   // (lane c of a 16-lane group points at key 4 gq + c / 4, rows 4 (c % 4) ..;
   // it receives keys 4 gq .. + 3 of row c)
   T* const my_ds = sdSt + (slot * QK + 16 * wk + c) * DSP + 4 * gq;
-  const int ds_rd = (4 * gq + (c >> 2)) * DSP + 4 * (c & 3);
+  int ds_rd = (4 * gq + (c >> 2)) * DSP + 4 * (c & 3);
+  int kst_off[QNS];  // this lane's K chunks in its slot's LDS tile
+#pragma unroll
+  for (int st = 0; st < QNS; ++st) kst_off[st] = toff<QD>(16 * wk + c, 4 * st + gq);
+  int fd_row = tid >> 4, fd_off = toff<QD>(tid >> 4, tid & 15);  // delta: row and chunk of this lane
+  int g4 = 4 * gq, lq = l;
 
   // ---- the ring: this wave's 16 keys of its slot's kv-tile -------------------
   V8 kB[QNS], vB[QNS];
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   auto store_k_rows = [&]() {  // this wave's K rows into its slot's LDS tile
     T* kt = sK + slot * QK * QD;
 #pragma unroll
-    for (int st = 0; st < QNS; ++st) *reinterpret_cast<V8*>(&kt[toff<QD>(16 * wk + c, 4 * st + gq)]) = kB[st];
+    for (int st = 0; st < QNS; ++st) *reinterpret_cast<V8*>(&kt[kst_off[st]]) = kB[st];
   };
   // dK = scale dS^T Q, dV = P^T dO of kv-tile my_j: straight out when every
   // q-step that sees it is in this chunk, else as one side's fp32 partial
@@ -227,14 +232,14 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     return a.lse[s.stat0 + h * s.stat_hs + min(i * QR + (l & 31), s.len_q - 1)];
   };
   auto store_lse = [&](int i, float v, float* ld) {
-    if (w == 0 && l < QR) ld[l] = i * QR + l < s.len_q ? v * kLog2e : INFINITY;  // padding rows: P = 0
+    if (w == 0 && lq < QR) ld[lq] = i * QR + lq < s.len_q ? v * kLog2e : INFINITY;  // padding rows: P = 0
   };
   // delta of the step's rows from its dO (in qo) and O (in ob): 16 lanes per
   // row, one 16-byte chunk each
   auto form_delta = [&](int i, const T* qo, const T* ob, float* ld) {
-    const int row = tid >> 4, ch = tid & 15;
-    const V8 x = *reinterpret_cast<const V8*>(&qo[QROWS + toff<QD>(row, ch)]);
-    const V8 y = *reinterpret_cast<const V8*>(&ob[toff<QD>(row, ch)]);
+    const int row = fd_row, ch = tid & 15;
+    const V8 x = *reinterpret_cast<const V8*>(&qo[QROWS + fd_off]);
+    const V8 y = *reinterpret_cast<const V8*>(&ob[fd_off]);
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc += Elem<T>::to_float(x[k]) * Elem<T>::to_float(y[k]);
@@ -247,10 +252,14 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   // sequence carry LSE = +inf.
   const unsigned trange = (unsigned)W;
 
-  // Phase 1 for this wave's keys: the 32 rows of q-step i in (qo, ld)
+  // Phase 1 for this wave's keys: the 32 rows of q-step i in (qo, ld).
+  // Both 16-row blocks are computed (the mask zeroes what no row sees), so
+  // the products form one straight run, with each operand read one product
+  // ahead; a hole only writes zeros into its dS^T (phase 2 reads every
+  // slot).
   auto phase1 = [&](int i, const T* qo, const float* ld) {
     const int j = my_j;
-    if (j < 0 || j >= nkt) {  // a hole: its dS^T is zero (phase 2 reads every slot)
+    if (j < 0 || j >= nkt) {
       const u32x2 z = {0u, 0u};
       *reinterpret_cast<u32x2*>(my_ds) = z;
       *reinterpret_cast<u32x2*>(my_ds + 16) = z;
@@ -258,65 +267,85 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     }
     const T* sQ = qo;
     const T* sdO = qo + QROWS;
-    const int kv0 = j * QK + 16 * wk;
-    const int key = kv0 + c;
+    const int key = j * QK + 16 * wk + c;
     const int tkey = key < s.len_kv ? g.diag - key : -(1 << 30);  // t = row + tkey
     const int q0 = i * QR;
-    const int u0 = q0 + g.diag - kv0;  // t at (row q0, key kv0)
-    f32x4 S[2], dP[2];
-    bool live[2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 S[2] = {zero4, zero4}, dP[2] = {zero4, zero4};
+    V8 aq[2][2], ao[2][2];  // [k-step parity][16-row block]: one k-step ahead
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {  // 16-row block mb spans t in [um - 15, um + 15]
-      const int um = u0 + 16 * mb;
-      live[mb] = um + 15 >= 0 && um - 15 <= W;
-      S[mb] = dP[mb] = zero4;
-      if (!live[mb]) continue;
+    for (int mb = 0; mb < 2; ++mb) {
+      aq[0][mb] = *reinterpret_cast<const V8*>(&sQ[16 * mb * QD + rd_off[0]]);
+      ao[0][mb] = *reinterpret_cast<const V8*>(&sdO[16 * mb * QD + rd_off[0]]);
+    }
 #pragma unroll
-      for (int st = 0; st < QNS; ++st) {
-        S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * QD + rd_off[st]]), kB[st], S[mb]);
-        dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * QD + rd_off[st]]), vB[st], dP[mb]);
+    for (int st = 0; st < QNS; ++st) {
+      if (st + 1 < QNS) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          aq[(st + 1) & 1][mb] = *reinterpret_cast<const V8*>(&sQ[16 * mb * QD + rd_off[st + 1]]);
+          ao[(st + 1) & 1][mb] = *reinterpret_cast<const V8*>(&sdO[16 * mb * QD + rd_off[st + 1]]);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        S[mb] = mfma16(aq[st & 1][mb], kB[st], S[mb]);
+        dP[mb] = mfma16(ao[st & 1][mb], vB[st], dP[mb]);
       }
     }
+    V8 to[2], tq[2];  // the transposed operands, one 16-column block ahead
+    to[0] = trpair(&sdO[tr_off[0]], &sdO[16 * QD + tr_off[0]]);
+    tq[0] = trpair(&sQ[tr_off[0]], &sQ[16 * QD + tr_off[0]]);
     V8 pP, pS;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      float pv[4] = {0.f, 0.f, 0.f, 0.f}, dsv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (live[mb]) {
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&ld[16 * mb + 4 * gq]);
-        const f32x4 del4 = *reinterpret_cast<const f32x4*>(&ld[QR + 16 * mb + 4 * gq]);
-        const int tb = q0 + 16 * mb + 4 * gq + tkey;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = S[mb][r] * p.scale_log2 - lse4[r];
-          asm("" : "+v"(x));
-          pv[r] = fast_exp2((unsigned)(tb + r) <= trange ? x : -INFINITY);
-          dsv[r] = pv[r] * (dP[mb][r] - del4[r]);
-        }
-      }
+      const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&ld[16 * mb + g4]);
+      const f32x4 del4 = *reinterpret_cast<const f32x4*>(&ld[QR + 16 * mb + g4]);
+      const int tb = q0 + 16 * mb + 4 * gq + tkey;
       T sk[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sk[r] = Elem<T>::from_float(dsv[r]);
-        pP[mb * 4 + r] = Elem<T>::from_float(pv[r]);
+        float x = S[mb][r] * p.scale_log2 - lse4[r];
+        asm("" : "+v"(x));
+        const float pv = fast_exp2((unsigned)(tb + r) <= trange ? x : -INFINITY);
+        const float dsv = pv * (dP[mb][r] - del4[r]);
+        sk[r] = Elem<T>::from_float(dsv);
+        pP[mb * 4 + r] = Elem<T>::from_float(pv);
         pS[mb * 4 + r] = sk[r];
       }
       // dS^T [key][row] for the dQ of phase 2 (zeros where unseen)
       *reinterpret_cast<u32x2*>(my_ds + 16 * mb) = __builtin_bit_cast(u32x2, sk);
     }
-    if (!live[0] && !live[1]) return;
     // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows
 #pragma unroll
     for (int db = 0; db < QNDB; ++db) {
-      dV[db] = mfma16(trpair(&sdO[tr_off[db]], &sdO[16 * QD + tr_off[db]]), pP, dV[db]);
-      dK[db] = mfma16(trpair(&sQ[tr_off[db]], &sQ[16 * QD + tr_off[db]]), pS, dK[db]);
+      if (db + 1 < QNDB) {
+        to[(db + 1) & 1] = trpair(&sdO[tr_off[db + 1]], &sdO[16 * QD + tr_off[db + 1]]);
+        tq[(db + 1) & 1] = trpair(&sQ[tr_off[db + 1]], &sQ[16 * QD + tr_off[db + 1]]);
+      }
+      dV[db] = mfma16(to[db & 1], pP, dV[db]);
+      dK[db] = mfma16(tq[db & 1], pS, dK[db]);
     }
   };
 
   // Phase 2: dQ^T of rows 16 rb .. + 15 of q-step i, head h, head-dim
   // columns 32 dq4 .. + 31, over the ring's tiles that see the rows
   const int rb = w & 1, dq4 = w >> 1;
-  const int tr_dq[2] = {troff<QD>(c, gq, 2 * dq4), troff<QD>(c, gq, 2 * dq4 + 1)};  // (dq4 varies by wave)
+  int tr_dq[2] = {troff<QD>(c, gq, 2 * dq4), troff<QD>(c, gq, 2 * dq4 + 1)};  // (dq4 varies by wave)
+  // The lane offsets above are made opaque at the top of every step: left
+  // loop-invariant, the compiler would keep a precomputed copy of each for
+  // every LDS buffer of the unrolled loop (dozens of registers) instead of
+  // folding the buffer into the instructions' offset field.
+  auto refresh_offsets = [&]() {
+#pragma unroll
+    for (int st = 0; st < QNS; ++st) {
+      asm volatile("" : "+v"(rd_off[st]));
+      asm volatile("" : "+v"(kst_off[st]));
+    }
+#pragma unroll
+    for (int db = 0; db < QNDB; ++db) asm volatile("" : "+v"(tr_off[db]));
+    asm volatile("" : "+v"(tr_dq[0]), "+v"(tr_dq[1]), "+v"(ds_rd), "+v"(fd_row), "+v"(fd_off), "+v"(g4), "+v"(lq));
+  };
   auto phase2_dq = [&](f32x4 (&dQt)[2]) {
     dQt[0] = dQt[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     // every slot (its dS^T is zero where its keys do not see these rows, and
@@ -415,6 +444,7 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     // step (the 3 loads of the rows of step s + 2, then its 2 dQ stores) has
     // completed: the rows of step s + 1, its own K / V rows, the earlier
     // stores and the LSE loads.
+    refresh_offsets();
     __builtin_amdgcn_s_waitcnt(kWaitVm5);
     lds_barrier();  // T: this step's statistics are in, phase 2 of the last step is done
     if (cg == 0 && ci > i0 && slot == ((ci + dq) & 3)) store_k_rows();  // the slot entering at ci
