@@ -414,8 +414,8 @@ def summarize_traffic(fetch_dir, write_dir, out, command, workload):
     print("\n".join(lines))
 
 
-SQ_KERNELS = ("bwd_stream_kernel", "bwd_main_kernel", "bwd_dq_kernel", "bwd_dot_kernel", "bwd_clear_kernel",
-              "bwd_dsink_kernel", "fwd_kernel")
+SQ_KERNELS = ("bwd_stream_kernel", "bwd_qstream_kernel", "bwd_qstream_fix_kernel", "bwd_main_kernel", "bwd_dq_kernel",
+              "bwd_dot_kernel", "bwd_clear_kernel", "bwd_dsink_kernel", "fwd_kernel")
 CLOCK_GHZ = 2.4   # MI355X peak engine clock
 N_SIMD = 256 * 4  # compute units x SIMDs
 
