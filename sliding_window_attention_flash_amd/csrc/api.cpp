@@ -183,20 +183,20 @@ sdpa_status resolve_engine(const sdpa_attn_desc* d, int* engine) {
   // ties or beats its fp32 atomics everywhere (within 1.5% at the largest
   // shape) and is repeatable, so it serves both deterministic 0 and 1.
   //
-  // Head_dim 128 (the study's d128 family: causal, windows 32 / 96, groups of
-  // 8 and multi-head, 1 .. 72 (sequence, kv head) pairs, 1K .. 16K rows):
-  // the q-major streaming kernel takes about 3 us per 32-row step whatever
-  // the window, so it wins by 4-76% once the grid holds at least 512
-  // q-steps (B Hkv S_q / 32) and either the heads are not grouped or the
-  // window is 64 keys or more; with groups of 8 and a 32-key window the
-  // per-tile kernels are within 6% or ahead, and below 512 q-steps ahead by
-  // up to 35%.  Both are bitwise repeatable (deterministic 0 and 1).
+  // Head_dim 128 (the study's d128 family: causal, windows 32 / 96, groups
+  // of 8 and multi-head, 1 .. 72 (sequence, kv head) pairs, 1K .. 16K rows):
+  // the q-major streaming kernel wins on every multi-head shape (by
+  // 10-80%) and wherever the window is 64 keys or more (by 15-55%), also on
+  // the smallest grids; with groups of 8 and a 32-key window it wins once
+  // the grid holds at least 1024 q-steps (B Hkv S_q / 32), and below that
+  // the per-tile kernels lead by up to 16%.  Both are bitwise repeatable
+  // (deterministic 0 and 1).
   const int64_t q_rows =
       (d->layout == SDPA_LAYOUT_THD ? d->total_q : (int64_t)d->batch * d->seq_q) * (int64_t)d->heads_q;
   const int64_t q_steps = (int64_t)d->batch * d->heads_kv * (((int64_t)d->seq_q + 31) / 32);
   if (d->deterministic == 2)
     *engine = ENGINE_TILE_RELAY;
-  else if (qstream_eligible(d) && q_steps >= 512 && (d->heads_q == d->heads_kv || d->window_left >= 64))
+  else if (qstream_eligible(d) && (d->heads_q == d->heads_kv || d->window_left >= 64 || q_steps >= 1024))
     *engine = ENGINE_QSTREAM;
   else if (stream_ok && q_rows >= (int64_t(1) << 16))
     *engine = ENGINE_STREAM_RELAY;

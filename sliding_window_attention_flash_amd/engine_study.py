@@ -62,10 +62,12 @@ def grid(family: str):
                                 bottom_right=True, window_left=128, scale=0.125))
         return out
     # head_dim 128: GQA groups of 8 and multi-head, small to full-chip grids
-    for (b, hq, hkv) in ((1, 8, 1), (2, 16, 2), (2, 16, 16), (12, 48, 6)):
-        for s in (1024, 4096, 16384):
+    for (b, hq, hkv) in ((1, 2, 2), (1, 8, 1), (2, 16, 2), (2, 16, 16), (12, 48, 6)):
+        for s in (1024, 4096, 8192, 16384):
             for win in (32, 96):
                 if b * hq * s > 12 * 48 * 16384 // 2 and win != 96:
+                    continue
+                if s == 8192 and (b, hq, hkv) != (2, 16, 2):
                     continue
                 out.append(Workload(f"b{b}_h{hq}x{hkv}_s{s}_w{win}_tl", torch.bfloat16, b, hq, hkv, 128, s, s,
                                     window_left=win))

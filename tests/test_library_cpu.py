@@ -431,11 +431,12 @@ def test_forced_engine_5_schedule_and_workspace(lib, B, Hq, Hkv, Sq, Skv):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,W,det,qstream", [
-    (2, 16, 2, 4096, 96, 0, True),    # GQA 8, 512 q-steps, window 96: the q-major streaming kernel
-    (2, 16, 2, 4096, 96, 1, True),    # repeatable, so deterministic 1 too
-    (2, 16, 2, 4064, 96, 0, False),   # 508 q-steps: the per-tile kernels
-    (2, 16, 2, 4096, 32, 0, False),   # GQA 8 with a 32-key window: the per-tile kernels
-    (2, 16, 16, 1024, 32, 0, True),   # multi-head: any window
+    (1, 8, 1, 1024, 96, 0, True),     # window of 64 keys or more: the q-major streaming kernel, any grid
+    (2, 16, 2, 4096, 64, 1, True),    # repeatable, so deterministic 1 too
+    (2, 16, 2, 4096, 32, 0, False),   # 32-key window, 512 q-steps: the per-tile kernels
+    (2, 16, 2, 8160, 32, 0, False),   # 1020 q-steps
+    (2, 16, 2, 8192, 32, 0, True),    # 1024 q-steps
+    (1, 2, 2, 1024, 32, 0, True),     # multi-head: any window, any grid
     (2, 16, 2, 4096, 100, 0, False),  # window beyond 96: not eligible
     (2, 16, 2, 4096, 96, 2, False),   # deterministic 2: the per-kv-tile relay
 ])
