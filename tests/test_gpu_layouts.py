@@ -1,8 +1,8 @@
 """GPU: tensors held sequence-major ([B, S, H, D] memory, passed as the
 [B, H, S, D] view most callers have) give the results of contiguous
 [B, H, S, D] tensors: the forward and the ordered dQ modes bit for bit, the
-unordered mode within the parity tolerance.  Covers both main kernels and
-row strides of H * D elements."""
+unordered mode within the parity tolerance.  Covers the three main kernels
+and row strides of H * D elements."""
 import pytest
 import torch
 
@@ -17,6 +17,10 @@ CASES = [
     # GQA, bottom-right, head_dim 128, sinks: the per-tile path
     Workload("seqmajor_gqa_br_w80_d128_sink", torch.float16, 2, 8, 2, 128, 300, 420, bottom_right=True,
              window_left=80, sink=True),
+    # GQA, bottom-right, head_dim 128, window 96: the q-major streaming
+    # kernel in the unordered and ordered modes (the plan's choice)
+    Workload("seqmajor_qstream_gqa_br_w96_d128", torch.bfloat16, 2, 8, 2, 128, 700, 700, bottom_right=True,
+             window_left=96),
 ]
 
 

@@ -109,6 +109,9 @@ QSTREAM_CASES = [
     _wl("qs_gqa8_br_w96_s1200x1264_f16", F16, 2, 16, 2, 128, 1200, 1264, bottom_right=True, window_left=96),
     _wl("qs_gqa3_tl_w17_s900", BF16, 3, 6, 2, 128, 900, 900, window_left=17),
     _wl("qs_gqa4_br_w96_s288x352", BF16, 1, 4, 1, 128, 288, 352, bottom_right=True, window_left=96),
+    # one partial q-step; two q-steps, the second of one row
+    _wl("qs_gqa2_br_w96_s20x52", BF16, 1, 4, 2, 128, 20, 52, bottom_right=True, window_left=96),
+    _wl("qs_mha_tl_w50_s33_f16", F16, 2, 3, 3, 128, 33, 33, window_left=50),
 ]
 
 
