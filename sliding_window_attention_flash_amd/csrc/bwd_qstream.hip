@@ -216,16 +216,30 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   // wave, straight into LDS; lane l fills bytes 16 l of a piece: row
   // 4 pr + l / 16, stored chunk l % 16, which holds logical chunk
   // (l % 16) ^ tsw(row).  Rows past the sequence repeat its last row.
+  // A wave's pieces always come from the same tensors: their sequence base
+  // and strides are picked once, by value (a pointer into the kernel
+  // arguments chosen at run time would cost a scalar load, and a wait on
+  // every outstanding LDS access, per piece and step).
+  constexpr int QPW = QPIECES / QWAVE;  // pieces per wave
+  const T* pc_base[QPW];
+  int64_t pc_hs[QPW], pc_rs[QPW];
+#pragma unroll
+  for (int k = 0; k < QPW; ++k) {
+    const int ten = (QPW * w + k) >> 3;
+    const T* base = static_cast<const T*>(ten == 0 ? a.q : (ten == 1 ? a.dO : a.o));
+    const int64_t s0 = ten == 0 ? p.sq[0] : (ten == 1 ? p.sdo[0] : p.so[0]);
+    pc_hs[k] = ten == 0 ? p.sq[1] : (ten == 1 ? p.sdo[1] : p.so[1]);
+    pc_rs[k] = ten == 0 ? p.sq[2] : (ten == 1 ? p.sdo[2] : p.so[2]);
+    pc_base[k] = base + (p.layout == LAYOUT_THD ? s.row0_q * pc_rs[k] : (int64_t)b * s0);
+  }
   auto stream_rows = [&](int i, int h, T* qo, T* ob) {
 #pragma unroll
-    for (int k = 0; k < QPIECES / QWAVE; ++k) {
-      const int pc = (QPIECES / QWAVE) * w + k, ten = pc >> 3, pr = pc & 7;
+    for (int k = 0; k < QPW; ++k) {
+      const int pc = QPW * w + k, ten = pc >> 3, pr = pc & 7;
       const int row = 4 * pr + (l >> 4), ch = (l & 15) ^ tsw<QD>(row);
       const int gr = min(i * QR + row, s.len_q - 1);
-      const int64_t* st = ten == 0 ? p.sq : (ten == 1 ? p.sdo : p.so);
-      const T* base = static_cast<const T*>(ten == 0 ? a.q : (ten == 1 ? a.dO : a.o));
       T* dst = ten == 2 ? ob : qo + ten * QROWS;
-      ld16_to_lds(base + elem_off(p, st, b, s.row0_q, h, gr) + 8 * ch, dst + pr * 512);
+      ld16_to_lds(row_at(pc_base[k] + h * pc_hs[k], gr, pc_rs[k]) + 8 * ch, dst + pr * 512);
     }
   };
   auto load_lse = [&](int i, int h) {  // wave 0, lane l < 32: row l
