@@ -453,22 +453,49 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
       constexpr bool FULL = decltype(full_tag)::value;
       f32x4 S[4], dP[4];
       const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (FULL) {
+        // every block: one straight run, each block's operands read while
+        // the previous block's products run
+        V8 aq[2][NS], ao[2][NS];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int um = u0 + 16 * mb;
-        if (!FULL && (um + 15 < 0 || um - 15 > (int)trange)) {
-          S[mb] = dP[mb] = zero4;
-          continue;
+        for (int st = 0; st < NS; ++st) {
+          aq[0][st] = *reinterpret_cast<const V8*>(&sQ[rd_off[st]]);
+          ao[0][st] = *reinterpret_cast<const V8*>(&sdO[rd_off[st]]);
         }
-        // the first product starts from a literal zero accumulator
-        S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[0]]), kB[0], zero4);
-        dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[0]]), vB[0], zero4);
 #pragma unroll
-        for (int st = 1; st < NS; ++st) {
-          S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[st]]), kB[st], S[mb]);
-          dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[st]]), vB[st], dP[mb]);
+        for (int mb = 0; mb < 4; ++mb) {
+          if (mb + 1 < 4) {
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+              aq[(mb + 1) & 1][st] = *reinterpret_cast<const V8*>(&sQ[16 * (mb + 1) * D + rd_off[st]]);
+              ao[(mb + 1) & 1][st] = *reinterpret_cast<const V8*>(&sdO[16 * (mb + 1) * D + rd_off[st]]);
+            }
+          }
+          S[mb] = mfma16(aq[mb & 1][0], kB[0], zero4);
+          dP[mb] = mfma16(ao[mb & 1][0], vB[0], zero4);
+#pragma unroll
+          for (int st = 1; st < NS; ++st) {
+            S[mb] = mfma16(aq[mb & 1][st], kB[st], S[mb]);
+            dP[mb] = mfma16(ao[mb & 1][st], vB[st], dP[mb]);
+          }
         }
-        if (FULL) __builtin_amdgcn_sched_barrier(0);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int um = u0 + 16 * mb;
+          if (um + 15 < 0 || um - 15 > (int)trange) {
+            S[mb] = dP[mb] = zero4;
+            continue;
+          }
+          // the first product starts from a literal zero accumulator
+          S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[0]]), kB[0], zero4);
+          dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[0]]), vB[0], zero4);
+#pragma unroll
+          for (int st = 1; st < NS; ++st) {
+            S[mb] = mfma16(*reinterpret_cast<const V8*>(&sQ[16 * mb * D + rd_off[st]]), kB[st], S[mb]);
+            dP[mb] = mfma16(*reinterpret_cast<const V8*>(&sdO[16 * mb * D + rd_off[st]]), vB[st], dP[mb]);
+          }
+        }
       }
       V8 pP[2], pS[2];
 #pragma unroll
@@ -507,6 +534,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
         if (RELAY) *reinterpret_cast<u32x2*>(&sdSt[ds_w[mb]]) = __builtin_bit_cast(u32x2, sk);
       }
       // dV^T += dO^T P, dK^T += Q^T dS over 32-row halves that see any key
+      if constexpr (FULL) {
+        // both halves, the transposed operands read one product ahead
+        auto tro = [&](int x) { return trpair(&sdO[32 * (x / NDB) * D + tr_off[x % NDB]], &sdO[(32 * (x / NDB) + 16) * D + tr_off[x % NDB]]); };
+        auto trq = [&](int x) { return trpair(&sQ[32 * (x / NDB) * D + tr_off[x % NDB]], &sQ[(32 * (x / NDB) + 16) * D + tr_off[x % NDB]]); };
+        V8 to[2], tq[2];
+        to[0] = tro(0);
+        tq[0] = trq(0);
+#pragma unroll
+        for (int x = 0; x < 2 * NDB; ++x) {
+          if (x + 1 < 2 * NDB) {
+            to[(x + 1) & 1] = tro(x + 1);
+            tq[(x + 1) & 1] = trq(x + 1);
+          }
+          dV[x % NDB] = mfma16(to[x & 1], pP[x / NDB], dV[x % NDB]);
+          dK[x % NDB] = mfma16(tq[x & 1], pS[x / NDB], dK[x % NDB]);
+        }
+        return;
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int um = u0 + 32 * s2;  // rows +0..31: t - tlo in [um - 15, um + 31]
