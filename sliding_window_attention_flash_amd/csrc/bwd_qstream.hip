@@ -124,6 +124,17 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   if (i0 >= i1) return;
   const int dq = g.diag / QK;  // the plan checked diag % 32 == 0
   const int W = p.window;      // 0 <= W <= 96
+  // Row 0 of this (sequence, kv head) in K, V, dK, dV, and of this
+  // sequence in dQ, with the row (and dQ's head) strides: formed once, so
+  // that the loop keeps a few scalars instead of every tensor's strides.
+  const T* const k_row0 = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, 0);
+  const T* const v_row0 = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, 0);
+  T* const dk_row0 = static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, hk, 0);
+  T* const dv_row0 = static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, hk, 0);
+  T* const dq_row0 = static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, 0, 0);
+  const int64_t k_rs = p.sk[2], v_rs = p.sv[2], dk_rs = p.sdk[2], dv_rs = p.sdv[2], dq_rs = p.sdq[2],
+                dq_hs = p.sdq[1];
+  const float* const lse0p = a.lse + s.stat0;
   // kv-tile in ring slot sl while q-step i runs: the one of i + dq - 3 ..
   // i + dq congruent to sl mod 4 (outside [0, nkt): a hole)
   auto slot_tile = [&](int sl, int i) { return i + dq - 3 + ((sl - (i + dq - 3)) & 3); };
@@ -158,8 +169,8 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     const int key = j * QK + 16 * wk + c;
     const bool ok = j >= 0 && j < nkt && key < s.len_kv;
     const int kr = clampi(key, 0, max(s.len_kv - 1, 0));
-    const T* krow = static_cast<const T*>(a.k) + elem_off(p, p.sk, b, s.row0_kv, hk, kr) + 8 * gq;
-    const T* vrow = static_cast<const T*>(a.v) + elem_off(p, p.sv, b, s.row0_kv, hk, kr) + 8 * gq;
+    const T* krow = row_at(k_row0, kr, k_rs) + 8 * gq;
+    const T* vrow = row_at(v_row0, kr, v_rs) + 8 * gq;
 #pragma unroll
     for (int st = 0; st < QNS; ++st) {
       kB[st] = ok ? ld8(krow + 32 * st) : zero8;
@@ -182,8 +193,8 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     const int lo = g.q_lo(j), hi = lo + g.n_iters(j);
     if (lo >= i0 && hi <= i1) {
       if (key < s.cap_kv) {
-        T* dkp = static_cast<T*>(a.dk) + elem_off(p, p.sdk, b, s.row0_kv, hk, key) + 4 * gq;
-        T* dvp = static_cast<T*>(a.dv) + elem_off(p, p.sdv, b, s.row0_kv, hk, key) + 4 * gq;
+        T* dkp = row_at(dk_row0, key, dk_rs) + 4 * gq;
+        T* dvp = row_at(dv_row0, key, dv_rs) + 4 * gq;
 #pragma unroll
         for (int db = 0; db < QNDB; ++db) {
           T kx[4], vx[4];
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     }
   };
   auto load_lse = [&](int i, int h) {  // wave 0, lane l < 32: row l
-    return a.lse[s.stat0 + h * s.stat_hs + min(i * QR + (l & 31), s.len_q - 1)];
+    return lse0p[h * s.stat_hs + min(i * QR + (l & 31), s.len_q - 1)];
   };
   auto store_lse = [&](int i, float v, float* ld) {
     if (w == 0 && lq < QR) ld[lq] = i * QR + lq < s.len_q ? v * kLog2e : INFINITY;  // padding rows: P = 0
@@ -386,7 +397,7 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   // every step ends with the same loads and stores in flight.
   auto store_dq = [&](int i, int h, const f32x4 (&dQt)[2]) {
     const int row = i * QR + 16 * rb + c;
-    T* dqr = (row < s.cap_q ? static_cast<T*>(a.dq) + elem_off(p, p.sdq, b, s.row0_q, h, row)
+    T* dqr = (row < s.cap_q ? row_at(dq_row0 + h * dq_hs, row, dq_rs)
                             : reinterpret_cast<T*>(a.dq_acc)) + 32 * dq4 + 4 * gq;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {

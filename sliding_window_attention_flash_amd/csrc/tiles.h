@@ -30,6 +30,10 @@ template <typename T>
 __device__ __forceinline__ const T* row_at(const T* base, int row, int64_t stride) {
   return base + (uint64_t)(uint32_t)row * (uint32_t)stride;
 }
+template <typename T>
+__device__ __forceinline__ T* row_at(T* base, int row, int64_t stride) {
+  return base + (uint64_t)(uint32_t)row * (uint32_t)stride;
+}
 
 // Blocks are dealt to the 8 XCDs round-robin; renumber them so that each XCD
 // runs one contiguous range of logical tiles (neighbouring tiles of one head
