@@ -269,6 +269,13 @@ swa::Problem make_problem(const sdpa_attn_desc* d, int engine) {
   // per-q-tile dSink partials stay with bwd_dot.
   p.dq_delta = p.split_dq && p.dq_tiles > 1 && !d->has_sink;
   p.stream_delta = p.stream && !d->has_sink;
+  // bwd_clear: q-tiles per block such that its grid has about 512 blocks
+  // (with fp32 atomics its blocks zero 16 KB slots, and a grid of a few
+  // dozen blocks left most CUs idle: 8.5 us at c2's 4096 rows)
+  {
+    const int64_t tiles = (int64_t)p.n_q_tiles * d->heads_q * d->batch;
+    p.clear_tiles = (int)std::min<int64_t>(64, std::max<int64_t>(1, tiles / 512));
+  }
   p.qstream = engine == ENGINE_QSTREAM;
   if (p.qstream) {
     // One 8-wave block per CU walks a chunk of consecutive 32-row q-steps of

@@ -175,12 +175,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
 // bwd_clear: where the streaming kernel forms delta itself (no sink), the
 // clearing bwd_dot would do for it: the control words, the q-tile counters,
 // the dQ rows of q-tiles no chunk visits and, with fp32 atomics, the
-// partial-sum slots of q-tiles several chunks visit.  A block takes 64
-// q-tiles: each thread of the first 64 clears one counter and decides
+// partial-sum slots of q-tiles several chunks visit.  A block takes up to
+// 64 q-tiles (the plan's clear_tiles, chosen so that the grid fills the
+// chip): each thread of the first ones clears one counter and decides
 // whether its tile needs more; the whole block then clears those tiles in
 // turn (head_dim 64, the streaming kernel's).
 
-constexpr int kClearTiles = 64;
+constexpr int kClearTiles = 64;  // most q-tiles per block
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_clear_kernel(BwdArgs a) {
@@ -189,12 +190,12 @@ __global__ __launch_bounds__(kThreads) void bwd_clear_kernel(BwdArgs a) {
   __shared__ int s_tile[kClearTiles];
   __shared__ int s_n;
   const Problem& p = a.p;
-  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z, t0 = blockIdx.x * kClearTiles;
+  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z, nt = p.clear_tiles, t0 = blockIdx.x * nt;
   if (blockIdx.x == 0 && h == 0 && b == 0 && tid < 2) a.ctl[tid] = 0;
   if (tid == 0) s_n = 0;
   __syncthreads();
   const Seq s = load_seq(p, b);
-  if (tid < kClearTiles && t0 + tid < p.n_q_tiles) {
+  if (tid < nt && t0 + tid < p.n_q_tiles) {
     const int tile = t0 + tid;
     a.sem[((int64_t)b * p.Hq + h) * p.n_q_tiles + tile] = 0;
     if (tile * kTile < s.cap_q) {
@@ -988,7 +989,7 @@ static hipError_t dot_t(const BwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd_clear(const BwdArgs& a, hipStream_t st) {
   if (a.p.n_q_tiles == 0) return hipSuccess;
-  dim3 grid((a.p.n_q_tiles + kClearTiles - 1) / kClearTiles, a.p.Hq, a.p.B);
+  dim3 grid((a.p.n_q_tiles + a.p.clear_tiles - 1) / a.p.clear_tiles, a.p.Hq, a.p.B);
   if (a.dtype == 0)
     hipLaunchKernelGGL((bwd_clear_kernel<__bf16>), grid, dim3(kThreads), 0, st, a);
   else

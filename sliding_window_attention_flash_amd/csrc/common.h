@@ -49,6 +49,7 @@ struct Problem {
   int stream;
   int stream_relay;  // streaming kernel: boundary q-tiles by the chunk relay (else fp32 atomics)
   int stream_delta;  // streaming kernel forms delta as it stages q-tiles (no bwd_dot; no sink)
+  int clear_tiles;   // q-tiles per block of bwd_clear (1 .. 64)
   int step_kv;
   int chunk;
   int n_chunks;
