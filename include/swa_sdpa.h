@@ -117,7 +117,8 @@ typedef struct sdpa_attn_desc {
                            0..128, head_dim 64; 5 needs head_dim 128,
                            causal, window_right 0, window_left 0..96, BHSD
                            without seq_lens, seq_kv - seq_q a multiple of 32
-                           if bottom-right, no sink (SDPA_ERR_UNSUPPORTED
+                           if bottom-right, at most 64 query heads per kv
+                           head with a sink (SDPA_ERR_UNSUPPORTED
                            otherwise); 1 needs deterministic 0, and
                            deterministic 2 admits only 4
                            (SDPA_ERR_INVALID_ARG otherwise).  The forward

@@ -141,14 +141,16 @@ enum { ENGINE_STREAM_ATOMIC = 1, ENGINE_STREAM_RELAY = 2, ENGINE_TILE_QMAJOR = 3
 
 // The q-major streaming kernel (bwd_qstream): head_dim 128, causal with no
 // right band, left window 0..96, dense sequences without padding lengths
-// whose diagonal offset is a multiple of 32, no sink.
+// whose diagonal offset is a multiple of 32; with a sink, groups of at most
+// 64 query heads.
 bool qstream_eligible(const sdpa_attn_desc* d) {
   bool small_rows = true;
   for (const int64_t rs : {d->stride_q[2], d->stride_k[2], d->stride_v[2], d->stride_o[2], d->stride_do[2],
                            d->stride_dq[2], d->stride_dk[2], d->stride_dv[2]})
     small_rows &= rs > 0 && rs <= INT32_MAX;
   const int64_t diag = d->bottom_right ? (int64_t)d->seq_kv - d->seq_q : 0;
-  return d->layout == SDPA_LAYOUT_BHSD && !d->has_seq_lens && !d->has_sink && d->causal && d->window_right == 0 &&
+  return d->layout == SDPA_LAYOUT_BHSD && !d->has_seq_lens && d->causal && d->window_right == 0 &&
+         (!d->has_sink || d->heads_q / d->heads_kv <= 64) &&
          d->window_left >= 0 && d->window_left <= 96 && d->head_dim == 128 && diag >= 0 && diag % 32 == 0 &&
          d->seq_q > 0 && small_rows;
 }
@@ -163,7 +165,7 @@ sdpa_status resolve_engine(const sdpa_attn_desc* d, int* engine) {
       return fail(SDPA_ERR_UNSUPPORTED,
                   "engine 5 (q-major streaming kernel) needs head_dim 128, causal, window_right 0, window_left "
                   "0..96, dense sequences without seq_lens, seq_kv - seq_q a multiple of 32 (bottom-right), "
-                  "no sink and row strides below 2^31");
+                  "at most 64 query heads per kv head with a sink, and row strides below 2^31");
     if ((d->engine == ENGINE_STREAM_ATOMIC || d->engine == ENGINE_STREAM_RELAY) && !stream_ok)
       return fail(SDPA_ERR_UNSUPPORTED,
                   "engine %d (streaming kernel) needs heads_q == heads_kv, causal, window_right 0, window_left "
@@ -302,6 +304,7 @@ swa::Problem make_problem(const sdpa_attn_desc* d, int engine) {
     p.qs_chunk = (int)best_c;
     p.qs_nch = (int)((nqt + best_c - 1) / best_c);
   }
+  p.sink_tiles = p.qstream ? (d->seq_q + 31) / 32 : p.n_q_tiles;
   if (p.stream) {
     // One block per CU: chunks of kv-steps sized so the grid is about one
     // block per MI355X CU, never shorter than 2 steps (so a q-tile has at
@@ -399,7 +402,7 @@ sdpa_status sdpa_bwd_plan(const sdpa_attn_desc* desc, sdpa_bwd_plan_t** plan, si
   pl->off_ctl = off;
   off = align256(off + sizeof(int) * 4);
   pl->off_sink = off;
-  off = align256(off + sizeof(float) * (size_t)p.Hq * p.B * p.n_q_tiles);
+  off = align256(off + sizeof(float) * (size_t)p.Hq * p.B * p.sink_tiles);
   pl->ws_bytes = off;
   pl->spin_limit = 1 << 20;  // ~55 ms of s_sleep per wait; legitimate waits take microseconds
   pl->relay_bias = 0;

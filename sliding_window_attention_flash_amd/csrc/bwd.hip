@@ -961,11 +961,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dsink: dSink[h] = -sum of the per-q-tile partials, in a fixed order.
+// bwd_dsink: dSink[h] = -sum of the per-q-tile (per-q-step with the q-major
+// streaming kernel) partials, in a fixed order.
 
 __global__ __launch_bounds__(64) void bwd_dsink_kernel(BwdArgs a) {
   const int h = blockIdx.x, l = threadIdx.x;
-  const int n = a.p.B * a.p.n_q_tiles;
+  const int n = a.p.B * a.p.sink_tiles;
   const float* part = a.sink_part + (int64_t)h * n;
   float acc = 0.f;
   for (int e = l; e < n; e += 64) acc += part[e];

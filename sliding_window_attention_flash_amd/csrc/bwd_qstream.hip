@@ -4,7 +4,7 @@
 // The rows of a 32-row q-step see at most 32 + W keys, four 32-key tiles for
 // W <= 96: kv-tiles i + d - 3 .. i + d for q-step i, with d = diag / 32 (the
 // plan takes this kernel only when diag is a multiple of 32, causal with no
-// right band, W <= 96, dense sequences, no sink).  One block of 8 waves (one
+// right band, W <= 96, dense sequences).  One block of 8 waves (one
 // per CU) walks a chunk of consecutive q-steps of one (sequence, kv head);
 // for each q-step it takes the G query heads of the group in turn, one step
 // each.  The four kv-tiles of the window stay in a ring: K and V rows in
@@ -256,6 +256,20 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   auto load_lse = [&](int i, int h) {  // wave 0, lane l < 32: row l
     return lse0p[h * s.stat_hs + min(i * QR + (l & 31), s.len_q - 1)];
   };
+  // With a sink: wave 0 adds the step's 32 terms exp(sink_h - LSE) delta
+  // (zero past the sequence: LSE +inf there, delta 0) in a fixed order and
+  // writes the step's dSink partial
+  // (lane g of every wave holds the group's g-th sink logit in log2 units;
+  // the plan takes this kernel with a sink only for groups of up to 64 heads)
+  const float sink_l = p.has_sink && l < G ? a.sink[hk * G + l] * kLog2e : 0.f;
+  auto sink_partial = [&](int i, int g, const float* ld) {
+    const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sink_l), g));
+    const int h = hk * G + g;
+    float t = lq < QR ? fast_exp2(s2 - ld[lq]) * ld[QR + lq] : 0.f;
+#pragma unroll
+    for (int off = QR / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+    if (lq == 0) a.sink_part[((int64_t)h * p.B + b) * p.sink_tiles + i] = t;
+  };
   auto store_lse = [&](int i, float v, float* ld) {
     if (w == 0 && lq < QR) ld[lq] = i * QR + lq < s.len_q ? v * kLog2e : INFINITY;  // padding rows: P = 0
   };
@@ -473,6 +487,7 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm5);
     lds_barrier();  // T: this step's statistics are in, phase 2 of the last step is done
     if (cg == 0 && ci > i0 && slot == ((ci + dq) & 3)) store_k_rows();  // the slot entering at ci
+    if (p.has_sink && w == 0) sink_partial(ci, cg, cld);
     phase1(ci, cqo, cld);
     lds_barrier();  // A: dS^T complete; everyone's rows of step s + 1 are in (since T)
     if (more) store_lse(ni, nlse, nld);

@@ -50,6 +50,7 @@ struct Problem {
   int stream_relay;  // streaming kernel: boundary q-tiles by the chunk relay (else fp32 atomics)
   int stream_delta;  // streaming kernel forms delta as it stages q-tiles (no bwd_dot; no sink)
   int clear_tiles;   // q-tiles per block of bwd_clear (1 .. 64)
+  int sink_tiles;    // dSink partials per (query head, sequence): 64-row q-tiles, or 32-row q-steps (bwd_qstream)
   int step_kv;
   int chunk;
   int n_chunks;

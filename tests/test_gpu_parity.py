@@ -95,7 +95,7 @@ def test_forced_engines_full_oracle(w, engine):
 
 
 # engine 5, the q-major streaming kernel (head_dim 128, causal, W <= 96, dense,
-# diag a multiple of 32, no sink): GQA and MHA, both anchors, windows from 0
+# diag a multiple of 32): GQA and MHA, both anchors, windows from 0
 # to 96, ragged lengths, a tail of keys no row sees (top-left, S_kv > S_q),
 # and enough 32-row steps that chunks meet (the plan's chunks are at least
 # 3 steps long: 9 steps make three chunks of exactly 3)
@@ -112,6 +112,9 @@ QSTREAM_CASES = [
     # one partial q-step; two q-steps, the second of one row
     _wl("qs_gqa2_br_w96_s20x52", BF16, 1, 4, 2, 128, 20, 52, bottom_right=True, window_left=96),
     _wl("qs_mha_tl_w50_s33_f16", F16, 2, 3, 3, 128, 33, 33, window_left=50),
+    # sink logits: dSink from per-q-step partials
+    _wl("qs_gqa4_br_w96_s700x764_sink", BF16, 2, 8, 2, 128, 700, 764, bottom_right=True, window_left=96, sink=True),
+    _wl("qs_mha_tl_w40_s300_sink_f16", F16, 1, 3, 3, 128, 300, 300, window_left=40, sink=True),
 ]
 
 

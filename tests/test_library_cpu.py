@@ -367,6 +367,7 @@ def test_noalloc_rejects_a_workspace_beyond_its_scratch(lib):
     (dict(engine=5, D=128, window_right=3), _lib.SDPA_ERR_UNSUPPORTED, "q-major streaming kernel"),
     (dict(engine=5, D=128, bottom_right=True, Skv=316), _lib.SDPA_ERR_UNSUPPORTED, "q-major streaming kernel"),
     (dict(engine=5, D=128, deterministic=2), _lib.SDPA_ERR_INVALID_ARG, "per-kv-tile relay"),
+    (dict(engine=5, D=128, Hq=130, Hkv=1, has_sink=1), _lib.SDPA_ERR_UNSUPPORTED, "q-major streaming kernel"),
     (dict(engine=1, Hkv=2), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
     (dict(engine=2, Hkv=4, window_left=200), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
     (dict(engine=2, Hkv=4, D=128), _lib.SDPA_ERR_UNSUPPORTED, "streaming kernel"),
@@ -425,9 +426,10 @@ def test_forced_engine_5_schedule_and_workspace(lib, B, Hq, Hkv, Sq, Skv):
     s = api.sdpa_bwd_schedule(plan, Sq, Skv)
     assert (s["tile_q"], s["tile_kv"]) == (32, 32)
     nch = _qstream_chunks(B, Hkv, Hq // Hkv, Sq)
-    ntq = -(-Sq // 64)
+    ntq, nqs = -(-Sq // 64), -(-Sq // 32)
     part = 4 * B * Hkv * nch * 6 * 32 * 2 * D
-    assert plan.workspace_bytes == _sections(0, part, 0, 4 * B * Hq * ntq, 16, 4 * Hq * B * ntq)
+    # (the dSink partials, one per 32-row q-step and query head)
+    assert plan.workspace_bytes == _sections(0, part, 0, 4 * B * Hq * ntq, 16, 4 * Hq * B * nqs)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,W,det,qstream", [
