@@ -190,15 +190,17 @@ sdpa_status resolve_engine(const sdpa_attn_desc* d, int* engine) {
   // the q-major streaming kernel wins on every multi-head shape (by
   // 10-80%) and wherever the window is 64 keys or more (by 15-55%), also on
   // the smallest grids; with groups of 8 and a 32-key window it wins once
-  // the grid holds at least 1024 q-steps (B Hkv S_q / 32), and below that
-  // the per-tile kernels lead by up to 16%.  Both are bitwise repeatable
+  // the grid holds at least 1024 q-steps (B Hkv S_q / 32), or 512 with a
+  // sink (where the per-tile path also runs bwd_dot), and below that the
+  // per-tile kernels lead by up to 16%.  Both are bitwise repeatable
   // (deterministic 0 and 1).
   const int64_t q_rows =
       (d->layout == SDPA_LAYOUT_THD ? d->total_q : (int64_t)d->batch * d->seq_q) * (int64_t)d->heads_q;
   const int64_t q_steps = (int64_t)d->batch * d->heads_kv * (((int64_t)d->seq_q + 31) / 32);
   if (d->deterministic == 2)
     *engine = ENGINE_TILE_RELAY;
-  else if (qstream_eligible(d) && (d->heads_q == d->heads_kv || d->window_left >= 64 || q_steps >= 1024))
+  else if (qstream_eligible(d) &&
+           (d->heads_q == d->heads_kv || d->window_left >= 64 || q_steps >= (d->has_sink ? 512 : 1024)))
     *engine = ENGINE_QSTREAM;
   else if (stream_ok && q_rows >= (int64_t(1) << 16))
     *engine = ENGINE_STREAM_RELAY;

@@ -75,6 +75,12 @@ def grid(family: str):
                         bottom_right=True, window_left=96))
     out.append(Workload("b4_h32x4_q2048_kv4096_w96_br_f16", torch.float16, 4, 32, 4, 128, 2048, 4096,
                         bottom_right=True, window_left=96))
+    # with sink logits
+    for (b, hq, hkv, s) in ((1, 8, 1, 4096), (2, 16, 2, 1024), (2, 16, 2, 4096)):
+        out.append(Workload(f"b{b}_h{hq}x{hkv}_s{s}_w32_tl_sink", torch.bfloat16, b, hq, hkv, 128, s, s,
+                            window_left=32, sink=True))
+    out.append(Workload("b12_h48x6_s4096_w96_br_sink", torch.bfloat16, 12, 48, 6, 128, 4096, 4096,
+                        bottom_right=True, window_left=96, sink=True))
     return out
 
 
@@ -82,14 +88,14 @@ def study(workloads, engines, rounds: int = 3, iters: int = 10, warmup: int = 5)
     rows = []
     for w in workloads:
         inp = make_inputs(w, device="cuda", seed=0)
-        o, lse = api.Forward(inp["q"], inp["k"], inp["v"], **_mask_kw(w)).run()
+        o, lse = api.Forward(inp["q"], inp["k"], inp["v"], sink=inp["sink"], **_mask_kw(w)).run()
         times = {(e, d): [] for e in (0,) + engines for d in (0, 1)}
         for _ in range(rounds):
             for (e, d) in times:
                 if (e, d) == (1, 1):  # atomics are not repeatable
                     continue
                 bw = api.Backward(inp["q"], inp["k"], inp["v"], o, inp["dO"], lse, engine=e, deterministic=d,
-                                  **_mask_kw(w))
+                                  sink=inp["sink"], **_mask_kw(w))
                 times[(e, d)].append(_time(bw.run, iters, warmup))
         med = {k: statistics.median(v) for k, v in times.items() if v}
         rows.append((w, med))

@@ -447,6 +447,14 @@ def test_default_engine_d128_follows_the_measured_table(lib, B, Hq, Hkv, S, W, d
     assert (api.sdpa_bwd_schedule(plan, S, S)["tile_q"] == 32) == qstream
 
 
+@pytest.mark.parametrize("S,qstream", [(4096, True), (4064, False)])
+def test_default_engine_d128_with_sink_from_512_q_steps(lib, S, qstream):
+    # groups of 8, a 32-key window and sink logits: the q-major streaming
+    # kernel from 512 q-steps (the per-tile path also runs bwd_dot then)
+    plan = api.sdpa_bwd_plan(_desc(B=2, Hq=16, Hkv=2, D=128, Sq=S, Skv=S, window_left=32, has_sink=1))
+    assert (api.sdpa_bwd_schedule(plan, S, S)["tile_q"] == 32) == qstream
+
+
 @pytest.mark.parametrize("B,H,S,det,stream", [
     (2, 16, 32768, 1, True),    # 2^20 query rows: the streaming kernel (chunk relay)
     (2, 16, 32768, 0, True),    # unordered too: the chunk relay ties or beats the atomics
