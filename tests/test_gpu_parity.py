@@ -127,6 +127,39 @@ def test_qstream_engine_full_oracle(w, det):
     compare_full(w, inp, out, check_fwd=False)
 
 
+def _qstream_random_cases(n=24, seed=2026):
+    """Seeded shapes across engine 5's domain: groups of 1 to 8 heads, both
+    anchors (bottom-right offsets that are multiples of 32), windows 0 to 96,
+    1 to 900 query rows (single partial q-steps, chunks of exactly 3,
+    several chunks), both 16-bit types, with and without a sink."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for k in range(n):
+        g = rng.choice([1, 2, 3, 4, 8])
+        hkv = rng.choice([1, 2, 3])
+        b = rng.choice([1, 2])
+        sq = rng.choice([1, 17, 32, 95, 96, 97, 288, 300, 513, 900])
+        br = rng.random() < 0.5
+        skv = sq + 32 * rng.randint(0, 4) if br else sq + rng.choice([0, 0, 5, 64])
+        wl = rng.choice([0, 1, 31, 32, 33, 63, 64, 65, 95, 96])
+        dt = rng.choice([BF16, F16])
+        sink = rng.random() < 0.3
+        out.append(_wl(f"qsr{k}_g{g}x{hkv}_b{b}_q{sq}_kv{skv}_{'br' if br else 'tl'}_w{wl}{'_sink' if sink else ''}",
+                       dt, b, g * hkv, hkv, 128, sq, skv, bottom_right=br, window_left=wl, sink=sink))
+    return out
+
+
+QSTREAM_RANDOM = _qstream_random_cases()
+
+
+@pytest.mark.parametrize("w", QSTREAM_RANDOM, ids=[w.name for w in QSTREAM_RANDOM])
+def test_qstream_engine_seeded_shapes_full_oracle(w):
+    say(f"case {w.name} engine=5")
+    inp, out, _ = run_gpu(w, seed=5, deterministic=1, engine=5)
+    compare_full(w, inp, out, check_fwd=False)
+
+
 def test_qstream_engine_bitwise_repeatable():
     # every sum in a fixed order: dQ inside one step, dK / dV in registers over
     # the chunk's steps, the two sides of a shared kv-tile added in turn
