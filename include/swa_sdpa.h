@@ -121,8 +121,12 @@ typedef struct sdpa_attn_desc {
                            head with a sink (SDPA_ERR_UNSUPPORTED
                            otherwise); 1 needs deterministic 0, and
                            deterministic 2 admits only 4
-                           (SDPA_ERR_INVALID_ARG otherwise).  The forward
-                           ignores it.                                        */
+                           (SDPA_ERR_INVALID_ARG otherwise).  The forward:
+                           0 takes the q-major forward where it applies,
+                           5 forces it (engine 5's shapes, with heads_q /
+                           heads_kv a multiple of 8, at most 512, and
+                           seq_kv > 0; SDPA_ERR_UNSUPPORTED otherwise),
+                           1..4 run the per-tile forward.                     */
   /* Element strides (batch, head, row) of each tensor; the head_dim axis is
    * contiguous.  THD ignores the batch entry (rows are tokens).  Rows and
    * base pointers must be 16-byte aligned; row strides below 2^32 elements
@@ -232,8 +236,11 @@ sdpa_status sdpa_bwd_run_noalloc(const sdpa_bwd_plan_t* plan, const sdpa_bwd_ten
  * sdpa_fwd_plan / sdpa_fwd_run -- the window-trimmed forward
  * ([PR866] Problem: the forward already trims its kv range by the window):
  * each q-tile walks only the kv-tiles [kv_first, kv_last] its rows can see
- * and writes O (dtype) and LSE (fp32).  Workspace is 0 bytes today; pass
- * the planned size anyway.
+ * and writes O (dtype) and LSE (fp32).  For head_dim 128, short windows and
+ * query-head groups of a multiple of 8 (see `engine`), a q-major kernel
+ * walks 32-row q-steps of a (sequence, kv head) with the window's kv-tiles
+ * resident and every head of the group reading them.  Workspace is 0 bytes
+ * today; pass the planned size anyway.
  */
 sdpa_status sdpa_fwd_plan(const sdpa_attn_desc* desc, sdpa_fwd_plan_t** plan,
                           size_t* workspace_bytes);

@@ -208,14 +208,14 @@ class Forward:
     here unless given)."""
 
     def __init__(self, q, k, v, *, causal=True, bottom_right=False, window_left=-1, window_right=0,
-                 q_run_tiles=0, scale=None, sink=None, cu_seqlens_q=None, cu_seqlens_kv=None,
+                 q_run_tiles=0, engine=0, scale=None, sink=None, cu_seqlens_q=None, cu_seqlens_kv=None,
                  seq_lens_q=None, seq_lens_kv=None, max_seqlen_q=None, max_seqlen_kv=None, o=None,
                  lse=None):
         g = geometry(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_kv)
         self.o = torch.empty_like(q) if o is None else o
         self.lse = torch.empty(lse_shape(g), dtype=torch.float32, device=q.device) if lse is None else lse
         desc = make_desc(g, q.dtype, causal=causal, bottom_right=bottom_right, window_left=window_left,
-                         window_right=window_right, q_run_tiles=q_run_tiles, scale=scale,
+                         window_right=window_right, q_run_tiles=q_run_tiles, engine=engine, scale=scale,
                          has_sink=sink is not None, has_seq_lens=seq_lens_q is not None,
                          q=q, k=k, v=v, o=self.o)
         self.plan = sdpa_fwd_plan(desc)

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libswa_sdpa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "bwd.hip", "bwd_stream.hip", "bwd_qstream.hip", "fwd.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "bwd.hip", "bwd_stream.hip", "bwd_qstream.hip", "fwd.hip", "fwd_qstream.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

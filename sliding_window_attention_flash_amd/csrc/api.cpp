@@ -155,6 +155,41 @@ bool qstream_eligible(const sdpa_attn_desc* d) {
          d->seq_q > 0 && small_rows;
 }
 
+// The q-major forward (fwd_qstream): the same shapes, checked on the tensors
+// the forward reads and writes, with query-head groups of a multiple of 8
+// (each of the block's 8 waves owns whole heads) and a non-empty kv sequence.
+bool fwd_qstream_eligible(const sdpa_attn_desc* d) {
+  bool small_rows = true;
+  for (const int64_t rs : {d->stride_q[2], d->stride_k[2], d->stride_v[2], d->stride_o[2]})
+    small_rows &= rs > 0 && rs <= INT32_MAX;
+  const int64_t diag = d->bottom_right ? (int64_t)d->seq_kv - d->seq_q : 0;
+  const int G = d->heads_q / d->heads_kv;
+  return d->layout == SDPA_LAYOUT_BHSD && !d->has_seq_lens && d->causal && d->window_right == 0 &&
+         d->window_left >= 0 && d->window_left <= 96 && d->head_dim == 128 && diag >= 0 && diag % 32 == 0 &&
+         d->seq_q > 0 && d->seq_kv > 0 && G % 8 == 0 && G / 8 <= 64 && small_rows;
+}
+
+// Chunks of a q-major kernel's grid: one 8-wave block per CU walks `c`
+// consecutive 32-row q-steps of one (sequence, kv head), `per_step` steps of
+// work each; with r rounds of 256 CUs the chunks are ceil(nqt / floor(256 r /
+// bh)) q-steps long (at least min_len), and r minimizes the estimated makespan
+// r (c per_step + startup) in steps (fewer rounds on a tie).
+int64_t qstream_chunk(int64_t bh, int64_t nqt, int64_t per_step, int64_t startup, int64_t min_len) {
+  const int64_t n_cap = std::max<int64_t>(1, nqt / min_len);
+  int64_t best_c = nqt, best_cost = INT64_MAX;
+  for (int64_t rounds = 1; rounds <= 64; ++rounds) {
+    const int64_t n0 = std::min(std::max<int64_t>(256 * rounds / bh, 1), n_cap);
+    const int64_t c = (nqt + n0 - 1) / n0, n = (nqt + c - 1) / c;
+    const int64_t cost = ((bh * n + 255) / 256) * (c * per_step + startup);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best_c = c;
+    }
+    if (n0 == n_cap) break;
+  }
+  return best_c;
+}
+
 // The backward's kernels and dQ mechanism: a forced engine (validated
 // against the shape and the deterministic promise) or the plan's default.
 sdpa_status resolve_engine(const sdpa_attn_desc* d, int* engine) {
@@ -291,18 +326,7 @@ swa::Problem make_problem(const sdpa_attn_desc* d, int engine) {
     // least 3 q-steps (so a 32-key tile, seen by at most 4 q-steps, is
     // shared by at most two chunks); fewer rounds on a tie.
     const int64_t bh = (int64_t)d->batch * d->heads_kv, nqt = ((int64_t)d->seq_q + 31) / 32;
-    const int64_t n_cap = std::max<int64_t>(1, nqt / 3);
-    int64_t best_c = nqt, best_cost = INT64_MAX;
-    for (int64_t rounds = 1; rounds <= 64; ++rounds) {
-      const int64_t n0 = std::min(std::max<int64_t>(256 * rounds / bh, 1), n_cap);
-      const int64_t c = (nqt + n0 - 1) / n0, n = (nqt + c - 1) / c;
-      const int64_t cost = ((bh * n + 255) / 256) * (c * p.G + 6);
-      if (cost < best_cost) {
-        best_cost = cost;
-        best_c = c;
-      }
-      if (n0 == n_cap) break;
-    }
+    const int64_t best_c = qstream_chunk(bh, nqt, p.G, 6, 3);
     p.qs_chunk = (int)best_c;
     p.qs_nch = (int)((nqt + best_c - 1) / best_c);
   }
@@ -601,10 +625,29 @@ sdpa_status sdpa_fwd_plan(const sdpa_attn_desc* desc, sdpa_fwd_plan_t** plan, si
   *plan = nullptr;
   sdpa_status st = check_desc(desc, false);
   if (st) return st;
+  // The forward's kernel: the q-major forward where it applies (engine 0 or
+  // 5; 5 fails elsewhere), else the per-tile forward (any other engine).
+  if (desc->engine < 0 || desc->engine > 5) return fail(SDPA_ERR_INVALID_ARG, "engine %d is not 0..5", desc->engine);
+  const bool qs_ok = fwd_qstream_eligible(desc);
+  if (desc->engine == ENGINE_QSTREAM && !qs_ok)
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "engine 5 (q-major forward) needs head_dim 128, causal, window_right 0, window_left 0..96, "
+                "dense sequences without seq_lens, seq_kv - seq_q a multiple of 32 (bottom-right), seq_kv > 0, "
+                "heads_q / heads_kv a multiple of 8 (at most 512) and row strides below 2^31");
   auto* pl = new (std::nothrow) struct sdpa_fwd_plan();
   if (!pl) return fail(SDPA_ERR_INVALID_ARG, "out of host memory");
   pl->desc = *desc;
   pl->prob = make_problem(desc, ENGINE_TILE_QMAJOR);  // (the backward's engine does not apply)
+  if (qs_ok && (desc->engine == 0 || desc->engine == ENGINE_QSTREAM)) {
+    // One 8-wave block per CU walks a chunk of q-steps of one (sequence, kv
+    // head), G / 8 (q-step, head) steps per q-step; a chunk's start-up (its
+    // ring's first tiles and rows) costs about two steps.
+    const int64_t bh = (int64_t)desc->batch * desc->heads_kv, nqt = ((int64_t)desc->seq_q + 31) / 32;
+    const int64_t c = qstream_chunk(bh, nqt, pl->prob.G / 8, 2, 1);
+    pl->prob.qstream = 1;
+    pl->prob.qs_chunk = (int)c;
+    pl->prob.qs_nch = (int)((nqt + c - 1) / c);
+  }
   *plan = pl;
   *workspace_bytes = 0;
   g_err[0] = 0;

@@ -264,8 +264,12 @@ static void fwd_td(const FwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((fwd_kernel<T, D, false>), dim3(n), dim3(kThreads), 0, st, a);
 }
 
+// the q-major forward for short windows at head_dim 128 (fwd_qstream.hip)
+hipError_t launch_fwd_qstream(const FwdArgs& a, hipStream_t st);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   if (a.p.n_q_tiles == 0) return hipSuccess;
+  if (a.p.qstream) return launch_fwd_qstream(a, st);
   if (a.dtype == 0) {
     if (a.p.D == 64) fwd_td<__bf16, 64>(a, st);
     else fwd_td<__bf16, 128>(a, st);
