@@ -19,16 +19,16 @@
 // group; for each q-step and head it computes
 //   S^T = K Q^T over the NS tiles   A: K rows from the ring, B: the Q rows,
 //                                   loaded straight into registers while the
-//                                   previous (q-step, head) computed;
+//                                   previous (q-step, head) step computed;
 //   the softmax of each row at once (every key the row sees is in the ring:
 //   max, exp2, sum; the sink joins the max and the denominator);
 //   O^T = V^T P^T                   A: transposed reads of the ring's V
 //                                   tiles, B: P^T from the S^T accumulators;
-// and stores O (8-byte stores of 4 consecutive head-dim values per lane) and
-// the row LSE.  Rows past the sequence repeat its last row, so every lane
-// issues the same stores (identical values to the same address) and the
-// memory operations in flight at a step's top are always the same: the
-// previous step's 17 stores.
+// and stores O (through a per-wave LDS tile, so that each store writes four
+// whole rows) and the row LSE.  Rows past the sequence repeat its last row,
+// so every lane issues the same stores (identical values to the same
+// address) and the memory operations in flight at a step's top are always
+// the same: the previous step's 9 stores.
 //
 // All products are v_mfma_f32_16x16x32 (bf16 / f16 in, fp32 accumulate),
 // with the lane layouts and swizzled 128-wide LDS rows of the other kernels.
@@ -50,9 +50,10 @@ constexpr int FRING = 8;        // ring slots (NS + 1 <= 5 in use)
 constexpr int FWAVE = 8;
 constexpr int FTHR = 64 * FWAVE;
 constexpr int FTILE = FK * FD;  // elements of a K (or V) tile
-// s_waitcnt vmcnt(17): everything but the last 17 vector-memory operations
-// (the previous step's 16 O stores and its LSE store) has completed
-constexpr int kWaitVm17 = 0x4F71;
+// s_waitcnt vmcnt(9): everything but the last 9 vector-memory operations
+// (the previous step's 8 O stores and its LSE store) has completed
+constexpr int kWaitVm9 = 0xF79;
+constexpr int FOST = 16 * FD;   // elements of a wave's O staging tile (16 rows)
 static_assert(FTHR * 8 == FTILE, "each thread stages one 16-byte chunk of a K and a V tile");
 
 // A barrier for LDS only: this wave's LDS accesses are complete, then
@@ -62,6 +63,37 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Max / sum over the 4 lanes c, c + 16, c + 32, c + 48 of a wave, in every
+// one of them: v_permlane16_swap exchanges 16-lane rows 2k + 1 of its first
+// operand and 2k of its second, v_permlane32_swap the upper half of the
+// first and the lower half of the second; given two copies of x, each pair
+// of results holds both operands of a butterfly step (in the same order in
+// every lane).  The second copy is made opaque: the compiler otherwise takes
+// the two results of a swap of equal operands to be equal, and drops the
+// step.
+__device__ __forceinline__ void swap_pair(unsigned (&r)[2], float x, bool halves) {
+  unsigned y = __builtin_bit_cast(unsigned, x);
+  asm volatile("" : "+v"(y));
+  const auto a = halves ? __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), y, false, false)
+                        : __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), y, false, false);
+  r[0] = a[0];
+  r[1] = a[1];
+}
+__device__ __forceinline__ float col4_max(float x) {
+  unsigned r[2];
+  swap_pair(r, x, false);
+  x = fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  swap_pair(r, x, true);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+__device__ __forceinline__ float col4_sum(float x) {
+  unsigned r[2];
+  swap_pair(r, x, false);
+  x = __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+  swap_pair(r, x, true);
+  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+
 }  // namespace
 
 template <typename T, int NS>
@@ -69,6 +101,7 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
   typedef typename Elem<T>::vec8 V8;
   __shared__ __align__(16) T sK[FRING * FTILE];
   __shared__ __align__(16) T sV[FRING * FTILE];
+  __shared__ __align__(16) T sO[FWAVE * FOST];  // per wave: 16 rows of O on their way out
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
@@ -109,12 +142,13 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
 
   // ---- Q rows, O rows, LSE ------------------------------------------------------
   const T* const q_b = static_cast<const T*>(a.q) + elem_off(p, p.sq, b, s.row0_q, 0, 0) + 8 * gq;
-  T* const o_b = static_cast<T*>(a.o) + elem_off(p, p.so, b, s.row0_q, 0, 0) + 4 * gq;
+  T* const o_b = static_cast<T*>(a.o) + elem_off(p, p.so, b, s.row0_q, 0, 0);
   const int64_t q_hs = p.sq[1], q_rs = p.sq[2], o_hs = p.so[1], o_rs = p.so[2];
   float* const lse_b = a.lse + s.stat0;
-  // B operand of S^T: lane (c, g) holds Q[row 16 rb + c][32 kst + 8 g .. + 7]
-  V8 qB[2][FNS];
-  auto load_q = [&](int i, int h) {
+  // B operand of S^T: lane (c, g) holds Q[row 16 rb + c][32 kst + 8 g .. + 7];
+  // two buffers, the next step's rows loading while this one computes
+  V8 qX[2][FNS], qY[2][FNS];
+  auto load_q = [&](int i, int h, V8 (&qB)[2][FNS]) {
     const T* qh = q_b + h * q_hs;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -141,11 +175,13 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
   }
   stage(i0 + dq);
   int ci = i0, hh = 0;  // the current step: q-step ci, head w + 8 hh of the group
-  load_q(ci, hk * G + w);
+  load_q(ci, hk * G + w, qX);
   __builtin_amdgcn_s_waitcnt(0);
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  while (true) {
+  // One step (q-step ci, head w + 8 hh) with its rows in qB, the next step's
+  // rows loading into qN; false after the chunk's last step.
+  auto step = [&](const V8 (&qB)[2][FNS], V8 (&qN)[2][FNS]) -> bool {
     // (the lane offsets are made opaque each step: left loop-invariant, the
     // compiler keeps a precomputed copy of each for every ring slot)
 #pragma unroll
@@ -153,7 +189,7 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < FNDB; ++db) asm volatile("" : "+v"(tr_off[db]));
     // the Q rows of this step and the staged tile have landed
-    __builtin_amdgcn_s_waitcnt(kWaitVm17);
+    __builtin_amdgcn_s_waitcnt(kWaitVm9);
     if (hh == 0) {
       // the tile entering at q-step ci; its slot last held tile ci + dq - 8,
       // which no wave has read since q-step ci - 5
@@ -168,6 +204,7 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
       ++ni;
     }
     const bool more = ni < i1;
+    if (more) load_q(ni, hk * G + w + FWAVE * nh, qN);
     const int jb = ci + dq - NS + 1;  // the ring's oldest tile for this q-step
 
     // S^T [key][row] for the NS tiles: [tile][16-key half][16-row block]
@@ -188,7 +225,6 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
         }
       }
     }
-    if (more) load_q(ni, hk * G + w + FWAVE * nh);
 
     // Mask: row r sees key k when 0 <= r + diag - k <= W and k < len_kv,
     // i.e. lo <= r + diag - k <= W with lo = max(0, r + diag - len_kv + 1).
@@ -231,10 +267,7 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
     V8 bP[2][NS];  // B operand of O^T: P^T of 32 keys (tile t) x 16 rows
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float m = mx[rb];
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      m = fmaxf(m * p.scale_log2, snk);  // the scale is > 0
+      float m = fmaxf(col4_max(mx[rb]) * p.scale_log2, snk);  // the scale is > 0
       mref[rb] = m == -INFINITY ? 0.f : m;  // a row that sees nothing keeps zeros
       float rs = 0.f;
 #pragma unroll
@@ -247,9 +280,7 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
             rs += pv;
             bP[rb][t][4 * kh + e] = Elem<T>::from_float(pv);
           }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      lsum[rb] = rs + fast_exp2(snk - mref[rb]);  // exp2(-inf) = 0 without a sink
+      lsum[rb] = col4_sum(rs) + fast_exp2(snk - mref[rb]);  // exp2(-inf) = 0 without a sink
     }
 
     // O^T [head dim][row] = V^T P^T over the NS tiles
@@ -267,6 +298,10 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
 
     // O = O^T / denominator (a row with neither a visible key nor a sink
     // gets O = 0 and LSE = -inf), then LSE
+    // Each 16-row block goes through the wave's LDS tile (16-byte chunk k of
+    // row r stored at chunk k ^ r: the 8-byte writes of 32 lanes and the
+    // row reads of 16 fall on distinct banks), so that every store writes
+    // four whole rows.
     T* const oh = o_b + h * o_hs;
     float lse_v[2];
 #pragma unroll
@@ -274,13 +309,20 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
       const bool live = lsum[rb] > 0.f;
       const float inv = live ? 1.f / lsum[rb] : 0.f;
       lse_v[rb] = live ? (mref[rb] + __log2f(lsum[rb])) * kLn2 : -INFINITY;
-      T* orow = row_at(oh, min(ci * FR + 16 * rb + c, s.len_q - 1), o_rs);
 #pragma unroll
       for (int db = 0; db < FNDB; ++db) {
         T ox[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) ox[e] = Elem<T>::from_float(O[db][rb][e] * inv);
-        *reinterpret_cast<u32x2*>(orow + 16 * db) = __builtin_bit_cast(u32x2, ox);
+        // row c, head-dim 16 db + 4 g: chunk 2 db + g / 2, half g % 2
+        *reinterpret_cast<u32x2*>(&sO[w * FOST + c * FD + (((2 * db + (gq >> 1)) ^ c) << 3) + 4 * (gq & 1)]) =
+            __builtin_bit_cast(u32x2, ox);
+      }
+#pragma unroll
+      for (int ps = 0; ps < 4; ++ps) {
+        const int r = 4 * ps + (l >> 4), k = l & 15;
+        const V8 x = *reinterpret_cast<const V8*>(&sO[w * FOST + r * FD + ((k ^ r) << 3)]);
+        *reinterpret_cast<V8*>(row_at(oh, min(ci * FR + 16 * rb + r, s.len_q - 1), o_rs) + 8 * k) = x;
       }
     }
     {
@@ -290,7 +332,9 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
     }
     ci = ni;
     hh = nh;
-    if (!more) break;
+    return more;
+  };
+  while (step(qX, qY) && step(qY, qX)) {
   }
 }
 

@@ -380,6 +380,32 @@ def test_plan_rejects_engines_that_do_not_apply(lib, kw, status, needle):
     assert e.value.status == status and needle in str(e.value)
 
 
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(engine=6, D=128, Hq=8, Hkv=1), _lib.SDPA_ERR_INVALID_ARG, "engine 6"),
+    (dict(engine=-1), _lib.SDPA_ERR_INVALID_ARG, "engine -1"),
+    (dict(engine=5, D=128, Hq=4, Hkv=2), _lib.SDPA_ERR_UNSUPPORTED, "q-major forward"),  # groups of 2
+    (dict(engine=5, D=64, Hq=8, Hkv=1), _lib.SDPA_ERR_UNSUPPORTED, "q-major forward"),
+    (dict(engine=5, D=128, Hq=8, Hkv=1, window_left=100), _lib.SDPA_ERR_UNSUPPORTED, "q-major forward"),
+    (dict(engine=5, D=128, Hq=8, Hkv=1, window_right=3), _lib.SDPA_ERR_UNSUPPORTED, "q-major forward"),
+    (dict(engine=5, D=128, Hq=8, Hkv=1, bottom_right=True, Skv=316), _lib.SDPA_ERR_UNSUPPORTED, "q-major forward"),
+])
+def test_forward_plan_rejects_engines_that_do_not_apply(lib, kw, status, needle):
+    with pytest.raises(_lib.SdpaError) as e:
+        api.sdpa_fwd_plan(_desc(**kw))
+    assert e.value.status == status and needle in str(e.value)
+
+
+@pytest.mark.parametrize("kw", [dict(engine=5, D=128, Hq=8, Hkv=1), dict(engine=5, D=128, Hq=16, Hkv=1, window_left=0),
+                                dict(engine=5, D=128, Hq=8, Hkv=1, bottom_right=True, Skv=332, window_left=96),
+                                dict(engine=3, D=128, Hq=8, Hkv=1), dict(engine=0, D=128, Hq=4, Hkv=2),
+                                dict(engine=2, D=64, Hq=4, Hkv=4)])
+def test_forward_plan_accepts_engines_that_apply(lib, kw):
+    # the q-major forward where forced on its shapes; any other engine (or
+    # the default, on shapes it does not take) plans the per-tile forward
+    plan = api.sdpa_fwd_plan(_desc(**kw))
+    assert plan.workspace_bytes == 0
+
+
 @pytest.mark.parametrize("engine,det,tile_kv", [(1, 0, 128), (2, 0, 128), (2, 1, 128), (3, 0, 64), (3, 1, 64),
                                                 (4, 0, 64), (4, 2, 64)])
 def test_forced_engine_sets_the_schedule_and_workspace(lib, engine, det, tile_kv):
