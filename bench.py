@@ -393,7 +393,7 @@ def summarize_traffic(fetch_dir, write_dir, out, command, workload):
         except RuntimeError:
             continue
         fb, wb = kf * 1024 / ff, kw * 1024 / fw
-        total += fb + wb if k != "fwd_kernel" else 0.0
+        total += fb + wb if not k.startswith("fwd") else 0.0  # (the forward is not part of the step)
         lines.append(f"{k:20s} {nf:8d} {fb / 1e6:10.2f} {wb / 1e6:10.2f} {(fb + wb) / 1e6:10.2f}")
         if k == MAIN_KERNEL:
             algo = main_kernel_bytes(w)
@@ -415,7 +415,7 @@ def summarize_traffic(fetch_dir, write_dir, out, command, workload):
 
 
 SQ_KERNELS = ("bwd_stream_kernel", "bwd_qstream_kernel", "bwd_qstream_fix_kernel", "bwd_main_kernel", "bwd_dq_kernel",
-              "bwd_dot_kernel", "bwd_clear_kernel", "bwd_dsink_kernel", "fwd_kernel")
+              "bwd_dot_kernel", "bwd_clear_kernel", "bwd_dsink_kernel", "fwd_qstream_kernel", "fwd_kernel")
 CLOCK_GHZ = 2.4   # MI355X peak engine clock
 N_SIMD = 256 * 4  # compute units x SIMDs
 
