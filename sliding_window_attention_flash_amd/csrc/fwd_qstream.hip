@@ -322,7 +322,9 @@ __global__ __launch_bounds__(FTHR, 1) void fwd_qstream_kernel(FwdArgs a) {
       for (int ps = 0; ps < 4; ++ps) {
         const int r = 4 * ps + (l >> 4), k = l & 15;
         const V8 x = *reinterpret_cast<const V8*>(&sO[w * FOST + r * FD + ((k ^ r) << 3)]);
-        *reinterpret_cast<V8*>(row_at(oh, min(ci * FR + 16 * rb + r, s.len_q - 1), o_rs) + 8 * k) = x;
+        // (non-temporal: O is not read again here; 2% faster at c4)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x),
+                                    reinterpret_cast<u32x4*>(row_at(oh, min(ci * FR + 16 * rb + r, s.len_q - 1), o_rs) + 8 * k));
       }
     }
     {
