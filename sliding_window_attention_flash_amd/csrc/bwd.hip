@@ -684,7 +684,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_main_kernel(BwdArgs a) {
 // leaves each lane with 4 consecutive head-dim values of one row: one 8-byte
 // store per 16 columns.  A wave skips the 16-key blocks its rows cannot see.
 
-// With DELTA (runs of q-tiles, no sink) the pass also forms each row's
+// With DELTA (runs of q-tiles, or head_dim 128; no sink; a single-tile
+// block takes the run path with a run of one) the pass also forms each row's
 // delta = <dO, O> from the dO rows it holds and an extra read of O, and
 // stores it for bwd_main, which then runs after it: the separate bwd_dot
 // pass, which reads dO and O once more, is not launched.
