@@ -119,8 +119,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdArgs a) {
     if (row < s.len_q)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += Elem<T>::to_float(ov[ps][e]) * Elem<T>::to_float(gv[ps][e]);
-#pragma unroll
-    for (int off = CH / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    acc = CH == 8 ? lanes8_sum(acc) : lanes16_sum(acc);  // the lanes of the row
     if (c == 0) {
       float t = 0.f;
       if (row < s.cap_q) {
@@ -807,8 +806,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
     for (int st = 0; st < NS; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += Elem<T>::to_float(ov[st][e]) * Elem<T>::to_float(xv[st][e]);
-    acc += __shfl_xor(acc, 16);
-    acc += __shfl_xor(acc, 32);
+    acc = col4_sum(acc);
     const int row = i * kTile + 16 * w + c;
     const float dl = row < s.len_q ? acc : 0.f;
     if (gq == 0 && row < s.cap_q) a.delta[s.stat0 + h * s.stat_hs + row] = dl;

@@ -301,9 +301,11 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += Elem<T>::to_float(dov[e]) * Elem<T>::to_float(xv[e]);
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
+    // the 8 lanes of the row by DPP (no LDS traffic): swaps within quads,
+    // then each half-row's mirror, which pairs the two quads
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0xB1, 0xF, 0xF, false));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x4E, 0xF, 0xF, false));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x141, 0xF, 0xF, false));
     if ((tid & 7) == 0) sLD[1][mb + (row >> 4)][row & 15] = tile * kTile + row < s.len_q ? acc : 0.f;
   };
   auto load_o_rows = [&](int i) {

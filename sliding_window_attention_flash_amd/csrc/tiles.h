@@ -77,4 +77,45 @@ __device__ __forceinline__ typename Elem<T>::vec8 trpair(const T* p0, const T* p
   return __builtin_bit_cast(typename Elem<T>::vec8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
+// Max / sum over the 4 lanes c, c + 16, c + 32, c + 48 of a wave, in every
+// one of them: v_permlane16_swap exchanges 16-lane rows 2k + 1 of its first
+// operand and 2k of its second, v_permlane32_swap the upper half of the
+// first and the lower half of the second; given two copies of x, each pair
+// of results holds both operands of a butterfly step (in the same order in
+// every lane).  The second copy is made opaque: the compiler otherwise takes
+// the two results of a swap of equal operands to be equal, and drops the
+// step.
+__device__ __forceinline__ void swap_pair(unsigned (&r)[2], float x, bool halves) {
+  unsigned y = __builtin_bit_cast(unsigned, x);
+  asm volatile("" : "+v"(y));
+  const auto a = halves ? __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), y, false, false)
+                        : __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), y, false, false);
+  r[0] = a[0];
+  r[1] = a[1];
+}
+__device__ __forceinline__ float col4_max(float x) {
+  unsigned r[2];
+  swap_pair(r, x, false);
+  x = fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  swap_pair(r, x, true);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+__device__ __forceinline__ float col4_sum(float x) {
+  unsigned r[2];
+  swap_pair(r, x, false);
+  x = __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+  swap_pair(r, x, true);
+  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+
+// Sums over 8 (16) consecutive lanes, in every one of them, by DPP (no LDS
+// traffic): swaps within quads, then the mirror of each half-row, which pairs
+// the two quads (and of the row, which pairs the two halves).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lanes8_sum(float x) { return dpp_add<0x141>(dpp_add<0x4E>(dpp_add<0xB1>(x))); }
+__device__ __forceinline__ float lanes16_sum(float x) { return dpp_add<0x140>(lanes8_sum(x)); }
+
 }  // namespace swa
