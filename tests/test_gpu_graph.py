@@ -29,7 +29,14 @@ CASES = [
               sink=True), 2),
     (Workload("graph_gqa_br_w70_sink", BF16, 2, 8, 2, 64, 190, 230, bottom_right=True, window_left=70,
               sink=True), 0),
+    # head_dim 128, groups of 8, W = 96: the q-major streaming kernel (its
+    # chunk-boundary fix pass included), after the q-major forward
+    (Workload("graph_qstream_g8_br_w96_sink", BF16, 1, 16, 2, 128, 700, 764, bottom_right=True, window_left=96,
+              sink=True, engine=5), 1),
 ]
+
+# the per-tile forward, and the q-major forward (head_dim 128, groups of 8)
+FWD_CASES = [CASES[2][0], CASES[4][0]]
 
 
 def _capture(fn):
@@ -72,8 +79,8 @@ def test_backward_graph_replays_match_eager(w, det):
             assert bw.relay_expiries() == 0
 
 
-def test_forward_graph_replays_match_eager():
-    w = CASES[2][0]
+@pytest.mark.parametrize("w", FWD_CASES, ids=[w.name for w in FWD_CASES])
+def test_forward_graph_replays_match_eager(w):
     say(f"case {w.name}: forward, eager, capture, 3 replays")
     inp = make_inputs(w, device="cuda", seed=32)
     fw = api.Forward(inp["q"], inp["k"], inp["v"], sink=inp["sink"], causal=w.causal,
