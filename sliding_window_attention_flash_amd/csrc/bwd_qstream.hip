@@ -27,9 +27,11 @@
 //   2  after a q-step's last head the oldest slot's waves retire their
 //      kv-tile and load the entering one; every wave forms delta of step
 //      s + 1's rows, computes 16 rows x 32 head-dim columns of dQ, starts
-//      the loads of step s + 3 (straight into LDS buffer (s + 3) mod 4) and
-//      last stores its dQ, so that those loads and stores are the only
-//      operations the wait before the next barrier T leaves in flight.
+//      the loads of step s + 3 (straight into LDS buffer (s + 3) mod 4),
+//      puts its dQ block into the step's LDS tile and last stores 4 whole
+//      rows of the previous step's tile, so that those loads and that store
+//      are the only operations the wait before the next barrier T leaves in
+//      flight.
 // The kv-tiles a chunk shares with its neighbours leave as fp32 partial
 // sums; bwd_qstream_fix adds the two sides in a fixed order, so the whole
 // pass is bitwise repeatable.
@@ -58,12 +60,13 @@ constexpr int QROWS = QR * QD;       // elements of a step's Q (or dO, O) rows
 constexpr int DSP = QR + 8;          // dS^T row pitch (elements): 80 bytes
 constexpr int QPART = QK * 2 * QD;   // floats of one kv-tile's dK / dV partial
 constexpr int QPIECES = 3 * QROWS * 2 / 1024;  // 1 KB pieces of a step's Q, dO, O
-constexpr int kWaitVm5 = 0xF75;      // s_waitcnt vmcnt(5) (no LDS / export wait)
+constexpr int kWaitVm4 = 0xF74;      // s_waitcnt vmcnt(4) (no LDS / export wait)
 constexpr int kWaitVm0 = 0xF70;      // s_waitcnt vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;   // s_waitcnt lgkmcnt(0)
 
 static_assert(QPIECES % QWAVE == 0, "a step's rows stream in whole pieces per wave");
-static_assert(QPIECES / QWAVE == 3, "the wait at a step's top leaves the last step's 3 pieces and 2 stores in flight");
+static_assert(QPIECES / QWAVE == 3, "the wait at a step's top leaves the last step's 3 pieces and 1 store in flight");
+static_assert(QR * QCH == QTHR, "each thread stores one 16-byte chunk of a step's dQ (4 whole rows per wave)");
 
 // A barrier for LDS only: this wave's LDS accesses are complete, then
 // s_barrier.  (__syncthreads also orders global memory, which here would
@@ -107,6 +110,10 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   __shared__ __align__(16) float sLD3[2 * QR];
   __shared__ __align__(16) T sK[QSLOT * QK * QD];
   __shared__ __align__(16) T sdSt[QSLOT * QK * DSP];
+  // dQ of a step on its way out (two, used in turn): the 8 waves' blocks
+  // meet here so that each wave stores 4 whole rows
+  __shared__ __align__(16) T sDQ0[QROWS];
+  __shared__ __align__(16) T sDQ1[QROWS];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, l = tid & 63, c = l & 15, gq = l >> 4;
@@ -406,20 +413,32 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
       for (int e = 0; e < 2; ++e) dQt[e] = mfma16(ak[m & 1][e], as[m & 1], dQt[e]);
     }
   };
-  // The two stores of every lane are issued whatever the row (rows past the
-  // sequence's slots write into the never-used partial slot of chunk 0), so
-  // every step ends with the same loads and stores in flight.
-  auto store_dq = [&](int i, int h, const f32x4 (&dQt)[2]) {
-    const int row = i * QR + 16 * rb + c;
-    T* dqr = (row < s.cap_q ? row_at(dq_row0 + h * dq_hs, row, dq_rs)
-                            : reinterpret_cast<T*>(a.dq_acc)) + 32 * dq4 + 4 * gq;
+  // dQ leaves through a step's LDS tile: each wave writes its 16 rows x 32
+  // head-dim columns (16-byte chunk k of row r stored at chunk k ^ (r mod 16),
+  // so that the 8-byte writes of 16 lanes fall on distinct chunks and the row
+  // reads of 16 on a whole row), and after the next barrier reads rows
+  // 4 w .. 4 w + 3 back and stores them whole.  The store of every lane is
+  // issued whatever the row (rows past the sequence's slots, and the step
+  // before the chunk's first, write into the never-used partial slot of
+  // chunk 0), so every step ends with the same loads and stores in flight.
+  auto dq_tile_write = [&](T* tile, const f32x4 (&dQt)[2]) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       T x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = Elem<T>::from_float(p.scale * dQt[e][r]);
-      *reinterpret_cast<u32x2*>(dqr + 16 * e) = __builtin_bit_cast(u32x2, x);
+      const int k = 4 * dq4 + 2 * e + (gq >> 1);
+      *reinterpret_cast<u32x2*>(&tile[(16 * rb + c) * QD + ((k ^ c) << 3) + 4 * (gq & 1)]) = __builtin_bit_cast(u32x2, x);
     }
+  };
+  auto dq_tile_read = [&](const T* tile) {
+    const int r = 4 * w + (l >> 4), k = l & 15;
+    return *reinterpret_cast<const V8*>(&tile[r * QD + ((k ^ (r & 15)) << 3)]);
+  };
+  auto dq_tile_store = [&](int i, int h, bool valid, const V8& x) {
+    const int row = i * QR + 4 * w + (l >> 4), k = l & 15;
+    T* dst = (valid && row < s.cap_q ? row_at(dq_row0 + h * dq_hs, row, dq_rs) : reinterpret_cast<T*>(a.dq_acc)) + 8 * k;
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x), reinterpret_cast<u32x4*>(dst));
   };
 
   // ---- kv-tiles no chunk's ring holds: zeros ----------------------------------
@@ -464,13 +483,16 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
   __syncthreads();
   store_lse(i0, lse0, sLD0);
   form_delta(i0, sQO0, sO0, sLD0);
+  int pi = i0, ph = 0;  // the previous step's q-step and head, whose dQ tile is pending
+  bool pending = false;
+  const T* last_tile = sDQ0;
 
   // One step: rows of (q-step ci, head hk G + cg) in buffer c; the next
   // step's rows are in buffer n (landed by barrier A), and the rows of the
   // step after the one after that start streaming into buffer n3 at the
   // end.  False after the chunk's last step.
   auto step = [&](const T* cqo, const float* cld, const T* nqo, const T* nob, float* nld, T* n3qo,
-                  T* n3ob) -> bool {
+                  T* n3ob, T* dqw, const T* dqp) -> bool {
     int ni = ci, ng = cg;
     next_of(ni, ng);
     int ai = ni, ag = ng;  // step s + 2 (its LSE), then s + 3 (its rows)
@@ -479,12 +501,12 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     next_of(bi, bg);
     const bool more = ni < i1, more2 = ai < i1;
     const int so = (ci + dq - 3) & 3;  // the oldest slot: its kv-tile leaves after this q-step
-    // Everything this wave issued but the last 5 operations of the previous
-    // step (the 3 loads of the rows of step s + 2, then its 2 dQ stores) has
+    // Everything this wave issued but the last 4 operations of the previous
+    // step (the 3 loads of the rows of step s + 2, then its dQ store) has
     // completed: the rows of step s + 1, its own K / V rows, the earlier
     // stores and the LSE loads.
     refresh_offsets();
-    __builtin_amdgcn_s_waitcnt(kWaitVm5);
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
     lds_barrier();  // T: this step's statistics are in, phase 2 of the last step is done
     if (cg == 0 && ci > i0 && slot == ((ci + dq) & 3)) store_k_rows();  // the slot entering at ci
     if (p.has_sink && w == 0) sink_partial(ci, cg, cld);
@@ -502,14 +524,27 @@ __global__ __launch_bounds__(QTHR, 1) void bwd_qstream_kernel(BwdArgs a) {
     // (past the chunk's end: a copy of in-range rows into the free buffer, so
     // that every step ends with the same 3 loads in flight)
     stream_rows(bi, hk * G + bg, n3qo, n3ob);
-    store_dq(ci, hk * G + cg, dQt);
+    // the previous step's dQ rows (its tile is complete since barrier T),
+    // then this step's tile, then the store
+    const V8 prev = dq_tile_read(dqp);
+    dq_tile_write(dqw, dQt);
+    dq_tile_store(pi, ph, pending, prev);
+    pi = ci;
+    ph = hk * G + cg;
+    pending = true;
+    last_tile = dqw;
     ci = ni;
     cg = ng;
     return more;
   };
-  while (step(sQO0, sLD0, sQO1, sO1, sLD1, sQO3, sO3) && step(sQO1, sLD1, sQO2, sO2, sLD2, sQO0, sO0) &&
-         step(sQO2, sLD2, sQO3, sO3, sLD3, sQO1, sO1) && step(sQO3, sLD3, sQO0, sO0, sLD0, sQO2, sO2)) {
+  while (step(sQO0, sLD0, sQO1, sO1, sLD1, sQO3, sO3, sDQ0, sDQ1) &&
+         step(sQO1, sLD1, sQO2, sO2, sLD2, sQO0, sO0, sDQ1, sDQ0) &&
+         step(sQO2, sLD2, sQO3, sO3, sLD3, sQO1, sO1, sDQ0, sDQ1) &&
+         step(sQO3, sLD3, sQO0, sO0, sLD0, sQO2, sO2, sDQ1, sDQ0)) {
   }
+  // the last step's dQ tile
+  lds_barrier();
+  dq_tile_store(pi, ph, true, dq_tile_read(last_tile));
   // the three newer slots of the last q-step still hold kv-tiles
   if (slot != ((i1 - 1 + dq - 3) & 3)) retire();
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no LDS write outlives the block
