@@ -86,6 +86,43 @@ def test_qmajor_forward_full_oracle(w):
         _compare(w, o, lse, ref_o, ref_lse)
 
 
+def _forward_random_cases(n=16, seed=4049):
+    """Seeded shapes across the q-major forward's domain: groups of 8, 16
+    and 24 heads, 1 to 3 kv heads, both anchors (bottom-right offsets that
+    are multiples of 32; top-left with more or fewer keys than queries),
+    windows 0 to 96, 1 to 1000 query rows, both 16-bit types, with and
+    without a sink."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for k in range(n):
+        g = rng.choice([8, 8, 16, 24])
+        hkv = rng.choice([1, 2, 3])
+        b = rng.choice([1, 2])
+        sq = rng.choice([1, 31, 32, 33, 95, 160, 257, 511, 1000])
+        br = rng.random() < 0.5
+        skv = sq + 32 * rng.randint(0, 3) if br else max(1, sq + rng.choice([0, 0, 7, 64, -20]))
+        wl = rng.choice([0, 1, 17, 31, 32, 33, 64, 65, 95, 96])
+        dt = rng.choice([BF16, F16])
+        sink = rng.random() < 0.3
+        out.append(_wl(f"fqr{k}_g{g}x{hkv}_b{b}_q{sq}_kv{skv}_{'br' if br else 'tl'}_w{wl}{'_sink' if sink else ''}",
+                       dt, b, g * hkv, hkv, sq, skv, bottom_right=br, window_left=wl, sink=sink))
+    return out
+
+
+FWD_RANDOM = _forward_random_cases()
+
+
+@pytest.mark.parametrize("w", FWD_RANDOM, ids=[w.name for w in FWD_RANDOM])
+def test_qmajor_forward_seeded_shapes_full_oracle(w):
+    inp = make_inputs(w, device="cuda", seed=7)
+    inp_cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    ref_o, ref_lse = oracle_forward(oracle_problem(w), inp_cpu["q"], inp_cpu["k"], inp_cpu["v"], inp_cpu["sink"])
+    say(f"case {w.name} forward engine=5")
+    o, lse = _run_forward(w, inp, 5)
+    _compare(w, o, lse, ref_o, ref_lse)
+
+
 def test_qmajor_forward_bitwise_repeatable():
     # each (q-step, head) is summed inside one wave in a fixed order
     w = FWD_QS_CASES[0]
