@@ -303,13 +303,16 @@ swa::Problem make_problem(const sdpa_attn_desc* d, int engine) {
     if (d->q_run_tiles > 0) p.dq_tiles = p.fwd_tiles = d->q_run_tiles;
   }
   // Where the dQ pass walks runs of q-tiles (short windows, whose passes
-  // stream Q / dO / O at full size), or at head_dim 128 (where its run
-  // and single-tile kernels both hold two blocks per CU), it also forms
+  // stream Q / dO / O at full size), at head_dim 128 (where its run and
+  // single-tile kernels both hold two blocks per CU), or where its grid fits
+  // one round at two blocks per CU (at most 512 blocks), it also forms
   // delta from the dO rows it holds, replacing the bwd_dot pass and its
-  // second read of dO (the f16 head_dim-128 GQA workload at S = 128:
-  // 71.4 -> 67.4 us per step on MI355X); the per-q-tile dSink partials stay
-  // with bwd_dot.
-  p.dq_delta = p.split_dq && (p.dq_tiles > 1 || d->head_dim == 128) && !d->has_sink;
+  // second read of dO and one launch (on MI355X: the f16 head_dim-128 GQA
+  // workload at S = 128, 71.4 -> 67.4 us per step; the 256-row two-head
+  // workload, 19.9 -> 16.9 us); the per-q-tile dSink partials stay with
+  // bwd_dot.
+  const int64_t dq_blocks = (int64_t)p.n_q_tiles * d->heads_q * d->batch;
+  p.dq_delta = p.split_dq && (p.dq_tiles > 1 || d->head_dim == 128 || dq_blocks <= 512) && !d->has_sink;
   p.stream_delta = p.stream && !d->has_sink;
   // bwd_clear: q-tiles per block such that its grid has about 512 blocks
   // (with fp32 atomics its blocks zero 16 KB slots, and a grid of a few
