@@ -21,6 +21,9 @@ CASES = [
     # kernel in the unordered and ordered modes (the plan's choice)
     Workload("seqmajor_qstream_gqa_br_w96_d128", torch.bfloat16, 2, 8, 2, 128, 700, 700, bottom_right=True,
              window_left=96),
+    # groups of 8: the q-major forward too, on sequence-major strides
+    Workload("seqmajor_qstream_g8_br_w96_d128", torch.bfloat16, 1, 16, 2, 128, 700, 764, bottom_right=True,
+             window_left=96),
 ]
 
 
