@@ -882,6 +882,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
       f32x4 St[4], dPt[4];
       bool live[4];
       const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 ndel4 = {-del, -del, -del, -del};  // dP^T accumulates from -delta: it leaves as dP - delta
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int um = u0 - 16 * nb;  // the block spans t - tlo in [um - 15, um + 15]
@@ -892,7 +893,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
         }
         // the first product starts from a literal zero accumulator
         St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[0]]), qB[0], zero4);
-        dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[0]]), oB[0], zero4);
+        dPt[nb] = mfma16(*reinterpret_cast<const V8*>(&cV[16 * nb * D + rd_off[0]]), oB[0], ndel4);
 #pragma unroll
         for (int st = 1; st < NS; ++st) {
           St[nb] = mfma16(*reinterpret_cast<const V8*>(&cK[16 * nb * D + rd_off[st]]), qB[st], St[nb]);
@@ -907,14 +908,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !RUN) ? 4 : 2) void bwd_dq_ke
         float dsv[4] = {0.f, 0.f, 0.f, 0.f};
         if (FULL) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dsv[r] = fast_exp2(St[nb][r] * p.scale_log2 - lse2) * (dPt[nb][r] - del);
+          for (int r = 0; r < 4; ++r) dsv[r] = fast_exp2(St[nb][r] * p.scale_log2 - lse2) * dPt[nb][r];
         } else if (live[nb]) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float x = St[nb][r] * p.scale_log2 - lse2;
             asm("" : "+v"(x));
             const bool vis = (unsigned)(tq - 16 * nb - r) <= trange && 16 * nb + 4 * gq + r < kvn;
-            dsv[r] = fast_exp2(vis ? x : -INFINITY) * (dPt[nb][r] - del);
+            dsv[r] = fast_exp2(vis ? x : -INFINITY) * dPt[nb][r];
           }
         }
 #pragma unroll

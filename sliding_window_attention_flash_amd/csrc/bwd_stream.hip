@@ -28,7 +28,8 @@
 // [key - diag, key + W - diag] of its keys, at most 10 blocks for W <= 128,
 // the same count for every wave -- two blocks at a time:
 //   S, dP  = Q K^T, dO V^T        A: Q / dO rows (LDS), B: K / V rows (regs)
-//   P, dS  = exp2(S c - LSE), P (dP - delta)          (fp32, masked)
+//   P, dS  = exp2(S c - LSE), P (dP - delta)          (fp32, masked; dP
+//          accumulates from -delta, which the ring stores negated)
 //   dV^T  += dO^T P,  dK^T += Q^T dS                  A: transposed LDS reads
 // and writes dS^T into its own LDS band: 16 keys x 12 block positions, where
 // position 1 + n holds the wave's n-th block and positions 0 and 11 (and
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0xB1, 0xF, 0xF, false));
     acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x4E, 0xF, 0xF, false));
     acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x141, 0xF, 0xF, false));
-    if ((tid & 7) == 0) sLD[1][mb + (row >> 4)][row & 15] = tile * kTile + row < s.len_q ? acc : 0.f;
+    if ((tid & 7) == 0) sLD[1][mb + (row >> 4)][row & 15] = tile * kTile + row < s.len_q ? -acc : 0.f;
   };
   auto load_o_rows = [&](int i) {
     const int row = tid >> 3, ch = tid & 7, qi = min(i * kTile + row, s.len_q - 1);
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const bool okr = r.tile * kTile + tid < s.len_q;
       // exp2(x - inf) = 0: padding rows carry no weight
       sLD[0][mb + (tid >> 4)][tid & 15] = okr ? r.lse * kLog2e : INFINITY;
-      if (!DELTA) sLD[1][mb + (tid >> 4)][tid & 15] = okr ? r.delta : 0.f;
+      if (!DELTA) sLD[1][mb + (tid >> 4)][tid & 15] = okr ? -r.delta : 0.f;
     }
     if (DELTA && with_o) put_delta(r.tile, r.o, r.x);
   };
@@ -522,9 +523,13 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     auto ld_addr = [&](int m) { return ring_ld + (uint32_t)m * (16 * sizeof(float)); };
     // S = Q K^T and dP = dO V^T of both blocks
     auto stage_sdp = [&](int pr) {
-      const uint32_t a0 = blk_addr(ring_pos(2 * pr)), a1 = blk_addr(ring_pos(2 * pr + 1));
+      const int m0 = ring_pos(2 * pr), m1 = ring_pos(2 * pr + 1);
+      const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
       PairSD r;
-      r.S0 = r.D0 = r.S1 = r.D1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      r.S0 = r.S1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      // dP starts from -delta of its rows, so that it leaves as dP - delta
+      r.D0 = lds_ld<f32x4>(pin(ld_addr(m0) + ld_off_b) + LD_DL);
+      r.D1 = lds_ld<f32x4>(pin(ld_addr(m1) + ld_off_b) + LD_DL);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const uint32_t x0 = pin(a0 + rd_off_b[ks]), x1 = pin(a1 + rd_off_b[ks]);
@@ -541,10 +546,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const bool has0 = b0 >= 0, has1 = b0 + 1 >= 0 && b0 + 1 <= bhi;
       const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
       const uint32_t l0 = pin(ld_addr(m0) + ld_off_b), l1 = pin(ld_addr(m1) + ld_off_b);
-      const f32x4 lse0 = lds_ld<f32x4>(l0), del0 = lds_ld<f32x4>(l0 + LD_DL);
-      const f32x4 lse1 = lds_ld<f32x4>(l1), del1 = lds_ld<f32x4>(l1 + LD_DL);
+      const f32x4 lse0 = lds_ld<f32x4>(l0), lse1 = lds_ld<f32x4>(l1);
       const float lsev[8] = {lse0[0], lse0[1], lse0[2], lse0[3], lse1[0], lse1[1], lse1[2], lse1[3]};
-      const float delv[8] = {del0[0], del0[1], del0[2], del0[3], del1[0], del1[1], del1[2], del1[3]};
       const float sv[8] = {r.S0[0], r.S0[1], r.S0[2], r.S0[3], r.S1[0], r.S1[1], r.S1[2], r.S1[3]};
       const float dv[8] = {r.D0[0], r.D0[1], r.D0[2], r.D0[3], r.D1[0], r.D1[1], r.D1[2], r.D1[3]};
       const int tb0 = has0 ? 16 * b0 + 4 * gq + tkey : -(1 << 29);
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         float x = sv[e] * p.scale_log2 - lsev[e];
         asm("" : "+v"(x));
         pv[e] = fast_exp2((unsigned)t <= (unsigned)W ? x : -INFINITY);
-        dsv[e] = pv[e] * (dv[e] - delv[e]);
+        dsv[e] = pv[e] * dv[e];  // (dv: dP - delta)
       }
       const u32x2 p0 = pack4<T>(pv[0], pv[1], pv[2], pv[3]), p1 = pack4<T>(pv[4], pv[5], pv[6], pv[7]);
       const u32x2 s0 = pack4<T>(dsv[0], dsv[1], dsv[2], dsv[3]);
