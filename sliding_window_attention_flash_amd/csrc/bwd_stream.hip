@@ -526,6 +526,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const int m0 = ring_pos(2 * pr), m1 = ring_pos(2 * pr + 1);
       const uint32_t a0 = blk_addr(m0), a1 = blk_addr(m1);
       PairSD r;
+      // Wave priority 1 over each run of products: of a SIMD's two waves,
+      // the one with MFMAs ready issues first while the other's softmax
+      // fills the gaps (c3 main kernel -1.5%)
+      __builtin_amdgcn_s_setprio(1);
       r.S0 = r.S1 = f32x4{0.f, 0.f, 0.f, 0.f};
       // dP starts from -delta of its rows, so that it leaves as dP - delta
       r.D0 = lds_ld<f32x4>(pin(ld_addr(m0) + ld_off_b) + LD_DL);
@@ -538,6 +542,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         r.S1 = mfma16(lds_ld<V8>(x1), kB[ks], r.S1);
         r.D1 = mfma16(lds_ld<V8>(x1 + QO_DO), vB[ks], r.D1);
       }
+      __builtin_amdgcn_s_setprio(0);
       return r;
     };
     // P, dS, the band write and dV^T += dO^T P, dK^T += Q^T dS
@@ -569,6 +574,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
       const u32x2 s1 = pack4<T>(dsv[4], dsv[5], dsv[6], dsv[7]);
       const V8 pP = __builtin_bit_cast(V8, u32x4{p0[0], p0[1], p1[0], p1[1]});
       const V8 pS = __builtin_bit_cast(V8, u32x4{s0[0], s0[1], s1[0], s1[1]});
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const uint32_t y0 = pin(a0 + tr_off_b[db]), y1 = pin(a1 + tr_off_b[db]);
@@ -577,6 +583,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
         dVa[db] = mfma16(__builtin_bit_cast(V8, u32x4{o_lo[0], o_lo[1], o_hi[0], o_hi[1]}), pP, dVa[db]);
         dKa[db] = mfma16(__builtin_bit_cast(V8, u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}), pS, dKa[db]);
       }
+      __builtin_amdgcn_s_setprio(0);
       // dS^T of blocks b0, b1 at band positions 2 pr + 1, 2 pr + 2 (after the
       // pair's ring reads, which the stores would otherwise hold back)
       *reinterpret_cast<u32x2*>(myband + band_wr + 16 * (2 * pr + 1)) = s0;
@@ -644,6 +651,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
     {
       const int nb = g.dq_nb(j), c0 = g.dq_c0(j, wr);
       const uint32_t bbase = pin(band0 + band_rd * sizeof(T) + 32 * c0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         store_dkdv(ks);
@@ -665,6 +673,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_stream_kernel(BwdArgs a) {
           dQa[k][1] = mfma16(kt1, st, dQa[k][1]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
 
     // q-tiles whose last visitor in this chunk was this step (all of them
